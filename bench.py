@@ -1,0 +1,408 @@
+"""Benchmark of the quantized GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+
+Prints ONE JSON line for the chosen workload (default: the W8A16 decode
+workload, M in {1, 4, 16}, K = 4096, N = 11008).  A step is one pass of the
+whole hot path over one batch of synthetic input; for a decode workload that
+is one GEMM call per listed M, for a square workload one GEMM.  Prepack and
+quantization of the operands are offline and untimed; inputs are resident in
+HBM before the timed region starts.
+
+Timing: the K timed steps are captured once into a HIP graph (untimed) and
+replayed once between two device synchronizations; `value` divides the work of
+K steps by that wall time.  HIP events recorded on the same stream around the
+replay give the average kernel duration used for the roofline figure.  Weight
+buffers rotate over copies totalling >= 600 MB (more than twice the 256 MB
+Infinity Cache), so each call streams its weight from HBM.
+
+The CPU baseline times the oracle (fp64 dequantize + NumPy matmul) on the host
+over a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "weight GB/s (%HBM peak) at M≤16; TFLOPS (%MFMA peak) at M=N=K=8192"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+ROTATE_BYTES = 600e6
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "decode": "bit_quantized_gemm_qgemm_amd/csrc/decode_gemm.hip",
+    "tile": "bit_quantized_gemm_qgemm_amd/csrc/tile_gemm.hip",
+}
+
+WORKLOADS = {
+    # name: (format, Ms, N, K)
+    "w4a16_small": ("w4a16", (16,), 1024, 1024),
+    "w8a16_decode": ("w8a16", (1, 4, 16), 11008, 4096),
+    "w4a16_decode": ("w4a16", (1, 8, 16), 28672, 8192),
+    "mxfp4_square": ("mxfp4", (8192,), 8192, 8192),
+    "fp8_square": ("fp8", (8192,), 8192, 8192),
+    "fp8_decode": ("fp8", (16,), 8192, 8192),
+}
+DEFAULT_WORKLOAD = "w8a16_decode"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(kind):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[kind]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# workload set-up (device side)
+# ---------------------------------------------------------------------------
+
+class Setup:
+    """Device buffers and per-call launchers of one workload."""
+
+    def __init__(self, name):
+        import torch
+        import qgemm_workloads as wl
+        import bit_quantized_gemm_qgemm_amd as qg
+
+        self.name = name
+        fmt, ms, n, k = WORKLOADS[name]
+        self.fmt, self.ms, self.n, self.k = fmt, ms, n, k
+        self.kind = "decode" if (fmt in ("w4a16", "w8a16") or max(ms) <= 16) else "tile"
+        dev = torch.device("cuda:0")
+        mmax = max(ms)
+        self.calls = []        # per call: (launch(copy) -> None, alg_bytes, weight_bytes, flops)
+        if fmt in ("w4a16", "w8a16"):
+            gen = wl.w4a16 if fmt == "w4a16" else wl.w8a16
+            x, w, s = gen(mmax, k, n)
+            w_d = torch.from_numpy(w).to(dev)
+            packed = qg.qgemm_prepack(fmt, w_d, k, n)
+            del w_d
+            s_d = torch.from_numpy(s).to(dev)
+            x_d = torch.from_numpy(x).to(dev)
+            w_bytes = (k * n // 2 if fmt == "w4a16" else k * n) + 2 * n
+            self.copies = self._rotate(packed, w_bytes)
+            fn = qg.qgemm_w4a16 if fmt == "w4a16" else qg.qgemm_w8a16
+            self.dtype = "f16"
+            for m in ms:
+                xm = x_d[:m].contiguous()
+                out = torch.empty((m, n), dtype=torch.float16, device=dev)
+                alg = w_bytes + 2 * m * k + 2 * m * n
+                self.calls.append((lambda c, xm=xm, out=out: fn(xm, self.copies[c], s_d, n, out=out),
+                                   alg, w_bytes, 2 * m * n * k))
+        elif fmt == "mxfp4":
+            a, w = wl.mxfp4_operands(mmax, n, k)
+            ac, ae = qg.qgemm_quantize_mxfp4(torch.from_numpy(a).to(dev))
+            wc, we = qg.qgemm_quantize_mxfp4(torch.from_numpy(w).to(dev))
+            del a, w
+            packed = qg.qgemm_prepack("mxfp4", wc, k, n, w_scales=we)
+            del wc, we
+            w_bytes = n * k // 2 + n * k // 32
+            a_bytes = mmax * k // 2 + mmax * k // 32
+            self.copies = self._rotate(packed, w_bytes + a_bytes)
+            self.a_copies = [ac] + [ac.clone() for _ in range(len(self.copies) - 1)]
+            ae_d = ae
+            self.dtype = "fp4"
+            out = torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
+            alg = w_bytes + a_bytes + 2 * mmax * n
+            self.calls.append((lambda c: qg.qgemm_mxfp4(self.a_copies[c], ae_d, self.copies[c], n,
+                                                        out=out),
+                               alg, w_bytes, 2 * mmax * n * k))
+        elif fmt == "fp8":
+            a, b = wl.fp8_operands(mmax, n, k)
+            qa, sa = qg.qgemm_quantize_fp8(torch.from_numpy(a).to(dev))
+            qb, sb = qg.qgemm_quantize_fp8(torch.from_numpy(b).to(dev))
+            del a, b
+            packed = qg.qgemm_prepack("fp8", qb, k, n)
+            del qb
+            w_bytes = n * k
+            a_bytes = mmax * k
+            self.copies = self._rotate(packed, w_bytes + a_bytes)
+            self.a_copies = [qa] + [qa.clone() for _ in range(len(self.copies) - 1)]
+            self.dtype = "fp8"
+            out = torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
+            alg = w_bytes + a_bytes + 2 * mmax * n
+            self.calls.append((lambda c: qg.qgemm_fp8(self.a_copies[c], self.copies[c], sa, sb, n,
+                                                      out=out),
+                               alg, w_bytes, 2 * mmax * n * k))
+        torch.cuda.synchronize()
+
+    @staticmethod
+    def _rotate(packed, bytes_per_copy):
+        r = max(1, math.ceil(ROTATE_BYTES / max(bytes_per_copy, 1)))
+        return [packed] + [packed.clone() for _ in range(r - 1)]
+
+    def enqueue_step(self, step):
+        """Enqueue one step; call j of step i uses weight copy (len(calls)*i + j) % R."""
+        per = len(self.calls)
+        r = len(self.copies)
+        for j, (launch, _, _, _) in enumerate(self.calls):
+            launch((per * step + j) % r)
+
+    def per_step(self):
+        alg = sum(c[1] for c in self.calls)
+        wgt = sum(c[2] for c in self.calls)
+        flops = sum(c[3] for c in self.calls)
+        return alg, wgt, flops
+
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+
+def time_steps(setup, steps, warmup, use_graph=True):
+    import torch
+
+    for i in range(warmup):
+        setup.enqueue_step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                setup.enqueue_step(i)
+        torch.cuda.synchronize()
+        graph.replay()              # one untimed replay: first-launch costs
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(steps):
+            setup.enqueue_step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t1 - t0, ev0.elapsed_time(ev1) / 1e3
+
+
+def per_call_times(setup, reps=60):
+    """Average device time of each call on its own (graph of `reps` calls)."""
+    import torch
+
+    out = []
+    r = len(setup.copies)
+    for launch, alg, wgt, flops in setup.calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                launch(i % r)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / 1e3 / reps)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the host
+# ---------------------------------------------------------------------------
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(name, budget_s=10.0):
+    import oracle
+    import qgemm_workloads as wl
+
+    fmt, ms, n, k = WORKLOADS[name]
+    mmax = max(ms)
+    if fmt in ("w4a16", "w8a16"):
+        gen = wl.w4a16 if fmt == "w4a16" else wl.w8a16
+        gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16
+        # bounded sample: the full K and a column slice sized for ~1 s per step
+        cols = n if k * n <= 50_000_000 else max(16, int(50_000_000 // k))
+        x, w, s = gen(mmax, k, n)
+        w, s = np.ascontiguousarray(w[:, :cols]), s[:cols]
+        w_bytes_per_step = sum(((k * cols // 2) if fmt == "w4a16" else k * cols) + 2 * cols
+                               for _ in ms)
+        unit, done, t0 = "GB/s", 0, time.perf_counter()
+        while True:
+            for m in ms:
+                gemm(x[:m], w, s)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+        value = w_bytes_per_step * done / dt / 1e9
+        sample = (f"oracle {fmt} steps (M={list(ms)}), K={k}, {cols} of {n} columns, "
+                  f"{done} steps in {dt:.1f} s")
+    else:
+        # bounded sample: 256 rows of A against all of W (MXFP4) / B (FP8)
+        rows = 256
+        unit = "TFLOP/s"
+        if fmt == "mxfp4":
+            a, w = wl.mxfp4_operands(rows, n, k)
+            ac, ae = oracle.mxfp4_quantize(a)
+            wc, we = oracle.mxfp4_quantize(w)
+            run = lambda: oracle.gemm_mxfp4(ac, ae, wc, we)  # noqa: E731
+        else:
+            a, b = wl.fp8_operands(rows, n, k)
+            qa, sa = oracle.fp8_quantize(a)
+            qb, sb = oracle.fp8_quantize(b)
+            run = lambda: oracle.gemm_fp8(qa, qb, sa, sb)  # noqa: E731
+        done, t0 = 0, time.perf_counter()
+        while True:
+            run()
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+        value = 2.0 * rows * n * k * done / dt / 1e12
+        sample = (f"oracle {fmt} GEMM of {rows} x {k} by {k} x {n} (dequantize + fp64 matmul), "
+                  f"{done} runs in {dt:.1f} s")
+    return {"value": value, "unit": unit, "cores": blas_threads(), "kind": "oracle",
+            "sample": sample}
+
+
+# ---------------------------------------------------------------------------
+
+def traffic_for(kind, kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    missing or taken on a different version of the kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+        ent = data.get(kernel)
+        if ent and ent.get("source_sha") == source_hash(kind):
+            return ent["bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def run(name, steps, warmup, with_cpu, use_graph):
+    import torch
+
+    setup = Setup(name)
+    alg, wgt, flops = setup.per_step()
+    wall, dev_s = time_steps(setup, steps, warmup, use_graph=use_graph)
+    launches = steps * len(setup.calls)
+    avg_launch = dev_s / launches
+    per_call = per_call_times(setup)
+    decode = setup.kind == "decode"
+    if decode:
+        value = wgt * steps / wall / 1e9
+        unit = "GB/s"
+        achieved = (alg / len(setup.calls)) / avg_launch / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        value = flops * steps / wall / 1e12
+        unit = "TFLOPS"
+        achieved = (flops / len(setup.calls)) / avg_launch / 1e12
+        peak = MFMA_PEAK_TFLOPS[setup.dtype]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    kernel = kernel_name(setup)
+    roof["traffic"] = traffic_for(setup.kind, kernel)
+    roof["kernel"] = kernel
+    detail = []
+    for (launch, a_b, w_b, fl), t, m in zip(setup.calls, per_call, setup.ms):
+        d = {"M": m, "us": round(t * 1e6, 3), "weight_GBps": round(w_b / t / 1e9, 1),
+             "alg_GBps": round(a_b / t / 1e9, 1), "TFLOPS": round(fl / t / 1e12, 2)}
+        d["pct_hbm"] = round(100 * a_b / t / 1e9 / HBM_PEAK_GBS, 1)
+        if not decode:
+            d["pct_mfma"] = round(100 * fl / t / 1e12 / MFMA_PEAK_TFLOPS[setup.dtype], 1)
+        detail.append(d)
+    cfg = {"workload": name, "format": setup.fmt, "M": list(setup.ms), "N": setup.n,
+           "K": setup.k, "weight_copies": len(setup.copies),
+           "timing": "hip-graph replay" if use_graph else "eager launches"}
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": setup.dtype,
+        "data": "synthetic (seeded NumPy draws in the workloads' shapes and distributions)",
+        "config": cfg,
+        "roofline": roof,
+        "detail": detail,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if with_cpu:
+        line["cpu_baseline"] = cpu_baseline(name)
+    del setup
+    torch.cuda.empty_cache()
+    return line
+
+
+def kernel_name(setup):
+    if setup.kind == "decode":
+        fmt_id = {"w4a16": 1, "w8a16": 2, "fp8": 4}[setup.fmt]
+        # mirrors the small-M dispatch: column groups per workgroup and waves
+        cg = -(-setup.n // 16)
+        kt = -(-setup.k // 128)
+        g = 4 if cg >= 4 * 256 + 256 else (2 if cg >= 2 * 256 + 128 else 1)
+        nw = 8 if kt >= 8 else 4
+        return f"decode_gemm_kernel<{fmt_id},{g},{nw}>"
+    return f"tile_gemm_kernel<{'fp4' if setup.fmt == 'mxfp4' else 'fp8'}>"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--all", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of a graph")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the kernels run on one GPU's share; see DESIGN.md for how they would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    names = sorted(WORKLOADS) if args.all else [args.workload]
+    for name in names:
+        square = WORKLOADS[name][1][0] > 16
+        steps = args.steps if args.steps is not None else (20 if square else 200)
+        warmup = args.warmup if args.warmup is not None else (3 if square else 20)
+        log(f"bench: {name} steps={steps} warmup={warmup}")
+        line = run(name, steps, warmup, with_cpu=not args.no_cpu, use_graph=not args.eager)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

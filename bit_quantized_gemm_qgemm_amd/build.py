@@ -1,0 +1,77 @@
+"""Build libqgemm.so in-tree with hipcc for gfx950.
+
+    python -m bit_quantized_gemm_qgemm_amd.build [-v]
+
+Every call compiles from source (no up-to-date check), so the library always
+matches the sources it sits next to.
+"""
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+ROOT = os.path.dirname(PKG_DIR)
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libqgemm.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+SOURCES = ["decode_gemm.hip", "tile_gemm.hip", "quantize.hip", "prepack.hip", "api.cpp"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+    # packed fp32 VALU ops stay off: the compiler would otherwise form them
+    # from plain float code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE,
+    "-I", CSRC,
+]
+
+
+def _hipcc():
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found; a ROCm toolchain is required to build libqgemm")
+    return exe
+
+
+def _compile(src, verbose):
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".cpp") else []
+    cmd = [_hipcc(), *HIPCC_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
+    return obj
+
+
+def build(verbose=False):
+    """Compile every HIP source for gfx950 and link libqgemm.so in the package."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

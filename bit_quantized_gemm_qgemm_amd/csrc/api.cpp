@@ -1,0 +1,198 @@
+// libqgemm C ABI: argument checks, dispatch by format and M, launch on the
+// caller's stream.  Every check that needs no device runs first, so a bad
+// call returns its status without touching the HIP runtime.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "../../include/qgemm.h"
+#include "qgemm_common.h"
+
+namespace {
+
+using qgemm::PackGeom;
+using qgemm::pack_geom;
+
+constexpr int64_t kMaxIndex = (int64_t)1 << 31;   // kernels index with 32-bit ints
+constexpr int kDecodeMaxM = 16;                   // small-M (bandwidth) path bound
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_format(int fmt) { return fmt >= QGEMM_W4A16 && fmt <= QGEMM_FP8; }
+
+// K constraints per format (see qgemm.h).
+bool k_ok(int fmt, int64_t K) {
+  switch (fmt) {
+    case QGEMM_W4A16: return K % 2 == 0;
+    case QGEMM_W8A16: return true;
+    case QGEMM_MXFP4: return K % 32 == 0;
+    case QGEMM_FP8: return K % 16 == 0;
+    default: return false;
+  }
+}
+
+// Sizes must be non-negative and every array the kernels index must stay
+// addressable with 32-bit element offsets.
+int check_sizes(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return QGEMM_ERR_SHAPE;
+  if (!k_ok(fmt, K)) return QGEMM_ERR_SHAPE;
+  if (M >= kMaxIndex || N >= kMaxIndex || K >= kMaxIndex) return QGEMM_ERR_SHAPE;
+  if (M * K * 2 >= kMaxIndex * 2 || M * N >= kMaxIndex || K * N >= kMaxIndex * 2)
+    return QGEMM_ERR_SHAPE;
+  return QGEMM_OK;
+}
+
+// Device architecture check, cached per device ordinal.
+int check_device() {
+  static std::mutex mu;
+  static int cached[64];
+  static bool init = false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QGEMM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!init) {
+    for (int& c : cached) c = 1;  // 1 = unknown
+    init = true;
+  }
+  if (dev < 0 || dev >= 64) return QGEMM_ERR_DEVICE;
+  if (cached[dev] == 1) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QGEMM_ERR_DEVICE;
+    cached[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? QGEMM_OK : QGEMM_ERR_ARCH;
+  }
+  return cached[dev];
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? QGEMM_OK : QGEMM_ERR_LAUNCH; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// A pointer may be NULL only when its array holds no elements.
+bool present(const void* p, int64_t elems) { return p != nullptr || elems == 0; }
+
+int weight_only(int fmt, const void* x, const void* w_packed, const void* scales, void* y,
+                int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_sizes(fmt, M, N, K);
+  if (st != QGEMM_OK) return st;
+  if (!present(x, M * K) || !present(w_packed, K * N) || !present(scales, N) ||
+      !present(y, M * N))
+    return QGEMM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(scales, 16) || !aligned(y, 16))
+    return QGEMM_ERR_ALIGN;
+  if (M == 0 || N == 0) return QGEMM_OK;
+  if ((st = check_device()) != QGEMM_OK) return st;
+  // every M runs the register-dequant path in 16-row slabs
+  return launched(qgemm::launch_decode_gemm(fmt, x, w_packed, scales, nullptr, nullptr, y, M, N,
+                                            K, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qgemm_status_string(int status) {
+  switch (status) {
+    case QGEMM_OK: return "ok";
+    case QGEMM_ERR_NULL: return "a required pointer is NULL";
+    case QGEMM_ERR_SHAPE: return "invalid shape (negative, K not a multiple the format needs, or too large)";
+    case QGEMM_ERR_ALIGN: return "pointer not aligned (16 bytes for arrays, 4 for scalar scales)";
+    case QGEMM_ERR_ARCH: return "current device is not gfx950";
+    case QGEMM_ERR_LAUNCH: return "kernel launch failed";
+    case QGEMM_ERR_FORMAT: return "unknown format id";
+    case QGEMM_ERR_DEVICE: return "no HIP device available";
+    default: return "unknown status";
+  }
+}
+
+int qgemm_abi_version(void) { return 100; }
+
+int64_t qgemm_prepack_bytes(int fmt, int64_t K, int64_t N) {
+  if (!valid_format(fmt)) return QGEMM_ERR_FORMAT;
+  const int st = check_sizes(fmt, 0, N, K);
+  if (st != QGEMM_OK) return st;
+  return pack_geom(fmt, K, N).total;
+}
+
+int qgemm_prepack(int fmt, const void* w, const void* w_scales, void* w_packed, int64_t K,
+                  int64_t N, void* stream) {
+  if (!valid_format(fmt)) return QGEMM_ERR_FORMAT;
+  if (!w_packed) return QGEMM_ERR_NULL;
+  int st = check_sizes(fmt, 0, N, K);
+  if (st != QGEMM_OK) return st;
+  const bool empty = (K == 0 || N == 0);
+  if (!empty && !w) return QGEMM_ERR_NULL;
+  if (fmt == QGEMM_MXFP4 && !empty && !w_scales) return QGEMM_ERR_NULL;
+  if (!aligned(w_packed, 16)) return QGEMM_ERR_ALIGN;
+  if (pack_geom(fmt, K, N).total == 0) return QGEMM_OK;
+  if ((st = check_device()) != QGEMM_OK) return st;
+  return launched(qgemm::launch_prepack(fmt, w, w_scales, w_packed, K, N, as_stream(stream)));
+}
+
+int qgemm_quantize_mxfp4(const float* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* e8m0,
+                         void* stream) {
+  if (rows < 0 || K < 0 || K % 32 != 0) return QGEMM_ERR_SHAPE;
+  if (!present(x, rows * K) || !present(codes, rows * K) || !present(e8m0, rows * K))
+    return QGEMM_ERR_NULL;
+  if (rows >= kMaxIndex || K >= kMaxIndex || rows * K >= kMaxIndex * 4) return QGEMM_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return QGEMM_ERR_ALIGN;
+  if (rows == 0 || K == 0) return QGEMM_OK;
+  int st = check_device();
+  if (st != QGEMM_OK) return st;
+  return launched(qgemm::launch_quantize_mxfp4(x, rows, K, codes, e8m0, as_stream(stream)));
+}
+
+int qgemm_quantize_fp8(const float* x, int64_t count, uint8_t* codes, float* scale,
+                       void* stream) {
+  if (!scale) return QGEMM_ERR_NULL;
+  if (count < 0) return QGEMM_ERR_SHAPE;
+  if (count > 0 && (!x || !codes)) return QGEMM_ERR_NULL;
+  if (!aligned(scale, 4)) return QGEMM_ERR_ALIGN;
+  int st = check_device();
+  if (st != QGEMM_OK) return st;
+  return launched(qgemm::launch_quantize_fp8(x, count, codes, scale, as_stream(stream)));
+}
+
+int qgemm_w4a16(const void* x, const void* w_packed, const void* scales, void* y, int64_t M,
+                int64_t N, int64_t K, void* stream) {
+  return weight_only(QGEMM_W4A16, x, w_packed, scales, y, M, N, K, stream);
+}
+
+int qgemm_w8a16(const void* x, const void* w_packed, const void* scales, void* y, int64_t M,
+                int64_t N, int64_t K, void* stream) {
+  return weight_only(QGEMM_W8A16, x, w_packed, scales, y, M, N, K, stream);
+}
+
+int qgemm_mxfp4(const void* a_codes, const void* a_e8m0, const void* w_packed, void* c,
+                int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_sizes(QGEMM_MXFP4, M, N, K);
+  if (st != QGEMM_OK) return st;
+  if (!present(a_codes, M * K) || !present(a_e8m0, M * K) || !present(w_packed, K * N) ||
+      !present(c, M * N))
+    return QGEMM_ERR_NULL;
+  if (!aligned(a_codes, 16) || !aligned(w_packed, 16) || !aligned(c, 16)) return QGEMM_ERR_ALIGN;
+  if (M == 0 || N == 0) return QGEMM_OK;
+  if ((st = check_device()) != QGEMM_OK) return st;
+  return launched(qgemm::launch_tile_gemm(QGEMM_MXFP4, a_codes, a_e8m0, w_packed, nullptr,
+                                          nullptr, c, M, N, K, as_stream(stream)));
+}
+
+int qgemm_fp8(const void* a, const void* b_packed, const float* scale_a, const float* scale_b,
+              void* c, int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_sizes(QGEMM_FP8, M, N, K);
+  if (st != QGEMM_OK) return st;
+  if (!present(a, M * K) || !present(b_packed, K * N) || !present(c, M * N) || !scale_a ||
+      !scale_b)
+    return QGEMM_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b_packed, 16) || !aligned(c, 16)) return QGEMM_ERR_ALIGN;
+  if (!aligned(scale_a, 4) || !aligned(scale_b, 4)) return QGEMM_ERR_ALIGN;
+  if (M == 0 || N == 0) return QGEMM_OK;
+  if ((st = check_device()) != QGEMM_OK) return st;
+  if (M <= kDecodeMaxM)
+    return launched(qgemm::launch_decode_gemm(QGEMM_FP8, a, b_packed, nullptr, scale_a, scale_b,
+                                              c, M, N, K, as_stream(stream)));
+  return launched(qgemm::launch_tile_gemm(QGEMM_FP8, a, nullptr, b_packed, scale_a, scale_b, c, M,
+                                          N, K, as_stream(stream)));
+}
+
+}  // extern "C"

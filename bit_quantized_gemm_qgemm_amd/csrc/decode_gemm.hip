@@ -1,0 +1,333 @@
+// Small-M GEMM with in-register dequantization (W4A16, W8A16, FP8).
+//
+// The bandwidth-bound shape of the W4A16 page (section 1: every decode step
+// streams the whole weight) and of the W8A16 page (Steps 1-2: load the low-bit
+// tile, convert and scale on chip, feed the dot product; never write W_fp16
+// back).  On gfx950 the multiply runs on the matrix cores
+// (v_mfma_f32_16x16x32_f16 for the fp16 formats, the scaled f8f6f4 16x16x128
+// instruction with unit scales for e4m3fn), with the M <= 16 rows of X in the
+// A operand and a 16-column fragment tile of W in the B operand.
+//
+// Work split: a workgroup owns G column groups (16 columns each) and one
+// 16-row slab of X; its NW waves split the K tiles round-robin, so at any time
+// the waves of a workgroup read neighbouring tiles.  Each wave keeps its fp32
+// partial sums in registers; the workgroup reduces them through LDS in a fixed
+// order (deterministic, no atomics, no workspace) and the epilogue applies the
+// per-column scale (or the per-tensor FP8 scales) once to the fp32 sum before
+// rounding to the output type.
+//
+// Dequantization without conversions: an fp16 with exponent field 25 and
+// mantissa field m has value 1024 + m, so OR-ing a code into the mantissa of
+// 0x6400 and subtracting a constant gives the exact small integer.  Two
+// nibbles (or bytes) become two fp16 lanes of one register per operation.
+#include "qgemm_common.h"
+
+namespace qgemm {
+namespace {
+
+template <int FMT> struct DecodeTraits;
+// W4A16: 16 B of W per lane per tile, 64 B of fp16 X per lane per tile.
+template <> struct DecodeTraits<1> {
+  static constexpr int WV = 1, XV = 4, TB = kTileBytesW4;
+};
+// W8A16: 32 B of W (two 1 KB halves), 64 B of fp16 X.
+template <> struct DecodeTraits<2> {
+  static constexpr int WV = 2, XV = 4, TB = kTileBytes;
+};
+// FP8: 32 B of W, 32 B of e4m3 A.
+template <> struct DecodeTraits<4> {
+  static constexpr int WV = 2, XV = 2, TB = kTileBytes;
+};
+
+// A 32-bit constant materialised in a VGPR, so that AND-OR can take it as a
+// register operand next to a scalar one (gfx9 VOP3 reads at most one scalar).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+struct W4Masks {
+  uint32_t lo, hi;  // 0x000f000f, 0x00f000f0 held in VGPRs
+};
+
+// Eight INT4 codes (nibble order k0,k2,k4,k6,k1,k3,k5,k7) -> code - 8 as fp16.
+__device__ __forceinline__ half8_t dequant_w4(uint32_t q, W4Masks mk) {
+  const uint32_t magic = 0x64006400u;       // fp16 1024 in both halves
+  const uint32_t t0 = (q & mk.lo) | magic;  // 1024 + c       (k0, k1)
+  const uint32_t t1 = (q & mk.hi) | magic;  // 1024 + 16 c    (k2, k3)
+  const uint32_t q2 = q >> 8;
+  const uint32_t t2 = (q2 & mk.lo) | magic;  //               (k4, k5)
+  const uint32_t t3 = (q2 & mk.hi) | magic;  //               (k6, k7)
+  const half2_t sub = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t off = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const half2_t h0 = __builtin_bit_cast(half2_t, t0) - sub;
+  const half2_t h1 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, t1), sixteenth, off);
+  const half2_t h2 = __builtin_bit_cast(half2_t, t2) - sub;
+  const half2_t h3 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, t3), sixteenth, off);
+  return half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+
+// Two biased INT8 bytes (w + 128) of a word, selected by `sel`, -> w as fp16.
+__device__ __forceinline__ half2_t dequant_w8_pair(uint32_t d, uint32_t sel) {
+  // byte permute of {0x64646464 : d}: selector 0..3 picks bytes of d, 4 picks 0x64
+  const uint32_t t = __builtin_amdgcn_perm(0x64646464u, d, sel);
+  const half2_t sub = {(_Float16)1152.0f, (_Float16)1152.0f};  // 1024 + 128
+  return __builtin_bit_cast(half2_t, t) - sub;
+}
+
+__device__ __forceinline__ half8_t dequant_w8(uint32_t lo, uint32_t hi) {
+  const half2_t a = dequant_w8_pair(lo, 0x04010400u);  // bytes 0, 1
+  const half2_t b = dequant_w8_pair(lo, 0x04030402u);  // bytes 2, 3
+  const half2_t c = dequant_w8_pair(hi, 0x04010400u);
+  const half2_t d = dequant_w8_pair(hi, 0x04030402u);
+  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+template <int FMT, int G>
+struct Chunk {
+  uintx4 x[DecodeTraits<FMT>::XV];
+  uintx4 w[G][DecodeTraits<FMT>::WV];
+};
+
+// Per-lane and per-workgroup addressing of one launch.  Scalar (wave-uniform)
+// parts stay in SGPRs; each lane adds a 32-bit offset.
+struct DecodeAddr {
+  const uint8_t* x;       // activations
+  uint32_t xlane;         // byte offset of this lane's row and K segment
+  const uint8_t* w;       // first weight tile of this workgroup
+  int64_t cg_stride;      // bytes between column groups
+  int cg_last;            // last valid group index relative to this workgroup
+  uint32_t wlane;         // 16 * lane
+  int K;
+  int kseg;               // this lane's K offset inside a tile (0, 32, 64, 96)
+};
+
+// Load lane data of K tile `kt`: the lane's 32-element K segment of X (or A)
+// and of each of the G weight tiles.  X pieces past K read as zero.  Rows past
+// M load row M-1 instead (their outputs are never stored); groups past the
+// last column load the last group (likewise discarded).
+template <int FMT, int G, bool X_ELEMENTWISE>
+__device__ __forceinline__ void load_chunk(Chunk<FMT, G>& ch, const DecodeAddr& ad, int kt) {
+  constexpr int XV = DecodeTraits<FMT>::XV;
+  constexpr int TB = DecodeTraits<FMT>::TB;
+  constexpr int XB = (FMT == 4) ? 1 : 2;          // bytes per activation element
+  constexpr int PIECE = 16 / XB;                  // elements per 16-byte piece
+  const uint8_t* xk = ad.x + (int64_t)kt * kTileK8 * XB;   // uniform
+  const bool full = (kt + 1) * kTileK8 <= ad.K;            // uniform
+  if constexpr (!X_ELEMENTWISE) {
+    if (full) {
+#pragma unroll
+      for (int p = 0; p < XV; ++p)
+        ch.x[p] = *reinterpret_cast<const uintx4*>(xk + ad.xlane + 16 * p);
+    } else {
+#pragma unroll
+      for (int p = 0; p < XV; ++p) {
+        const int k = kt * kTileK8 + ad.kseg + PIECE * p;
+        ch.x[p] = (k < ad.K) ? *reinterpret_cast<const uintx4*>(xk + ad.xlane + 16 * p)
+                             : uintx4{0, 0, 0, 0};
+      }
+    }
+  } else {
+    // K % 8 != 0 (fp16 only): rows are not 16-byte aligned; go element-wise
+    const uint16_t* xr = reinterpret_cast<const uint16_t*>(xk + ad.xlane);
+#pragma unroll
+    for (int p = 0; p < XV; ++p) {
+      uint32_t d[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = kt * kTileK8 + ad.kseg + 8 * p + 2 * j;
+        const uint32_t lo = (k < ad.K) ? xr[8 * p + 2 * j] : 0u;
+        const uint32_t hi = (k + 1 < ad.K) ? xr[8 * p + 2 * j + 1] : 0u;
+        d[j] = lo | (hi << 16);
+      }
+      ch.x[p] = uintx4{d[0], d[1], d[2], d[3]};
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int gg = g < ad.cg_last ? g : ad.cg_last;                      // uniform
+    const uint8_t* t = ad.w + gg * ad.cg_stride + (int64_t)kt * TB;     // uniform
+    ch.w[g][0] = __builtin_nontemporal_load(reinterpret_cast<const uintx4*>(t + ad.wlane));
+    if constexpr (DecodeTraits<FMT>::WV == 2)
+      ch.w[g][1] =
+          __builtin_nontemporal_load(reinterpret_cast<const uintx4*>(t + 1024 + ad.wlane));
+  }
+}
+
+template <int FMT, int G>
+__device__ __forceinline__ void compute_chunk(const Chunk<FMT, G>& ch, floatx4 (&acc)[G],
+                                              W4Masks mk) {
+  if constexpr (FMT == 4) {
+    const intx8 a = {(int)ch.x[0][0], (int)ch.x[0][1], (int)ch.x[0][2], (int)ch.x[0][3],
+                     (int)ch.x[1][0], (int)ch.x[1][1], (int)ch.x[1][2], (int)ch.x[1][3]};
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const intx8 b = {(int)ch.w[g][0][0], (int)ch.w[g][0][1], (int)ch.w[g][0][2],
+                       (int)ch.w[g][0][3], (int)ch.w[g][1][0], (int)ch.w[g][1][1],
+                       (int)ch.w[g][1][2], (int)ch.w[g][1][3]};
+      acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          a, b, acc[g], kFmtFP8, kFmtFP8, 0, kE8M0One, 0, kE8M0One);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const half8_t a = __builtin_bit_cast(half8_t, ch.x[s]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        half8_t b;
+        if constexpr (FMT == 1) {
+          b = dequant_w4(ch.w[g][0][s], mk);
+        } else {
+          const uintx4& h = ch.w[g][s >> 1];
+          b = dequant_w8(h[2 * (s & 1)], h[2 * (s & 1) + 1]);
+        }
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[g], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int FMT, int G, int NW, bool X_ELEMENTWISE>
+__global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
+    const uint8_t* __restrict__ x, const uint8_t* __restrict__ wp,
+    const _Float16* __restrict__ scales, const float* __restrict__ scale_a,
+    const float* __restrict__ scale_b, uint16_t* __restrict__ y, int M, int N, int K, int KT,
+    int CG) {
+  static_assert(NW >= 2, "the K split needs at least two waves");
+  constexpr int TB = DecodeTraits<FMT>::TB;
+  constexpr int XB = (FMT == 4) ? 1 : 2;
+  __shared__ floatx4 red[NW][G][kWave];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cg0 = blockIdx.x * G;
+  const int m0 = blockIdx.y * 16;
+  const int row = min(m0 + (lane & 15), M - 1);
+
+  DecodeAddr ad;
+  ad.kseg = 32 * (lane >> 4);
+  ad.x = x;
+  ad.xlane = (uint32_t)(((int64_t)row * K + ad.kseg) * XB);
+  ad.cg_stride = (int64_t)KT * TB;
+  ad.w = wp + (int64_t)cg0 * ad.cg_stride;
+  ad.cg_last = CG - 1 - cg0;
+  ad.wlane = 16u * lane;
+  ad.K = K;
+
+  W4Masks mk{};
+  if constexpr (FMT == 1) mk = W4Masks{vgpr_const(0x000f000fu), vgpr_const(0x00f000f0u)};
+
+  floatx4 acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // K tiles wave, wave + NW, ...; two register buffers, one tile of look-ahead
+  Chunk<FMT, G> b0, b1;
+  int kt = wave;
+  if (kt < KT) load_chunk<FMT, G, X_ELEMENTWISE>(b0, ad, kt);
+  while (kt < KT) {
+    if (kt + NW < KT) load_chunk<FMT, G, X_ELEMENTWISE>(b1, ad, kt + NW);
+    compute_chunk<FMT, G>(b0, acc, mk);
+    kt += NW;
+    if (kt >= KT) break;
+    if (kt + NW < KT) load_chunk<FMT, G, X_ELEMENTWISE>(b0, ad, kt + NW);
+    compute_chunk<FMT, G>(b1, acc, mk);
+    kt += NW;
+  }
+
+  // ---- reduce the NW partial tiles in a fixed order
+#pragma unroll
+  for (int g = 0; g < G; ++g) red[wave][g][lane] = acc[g];
+  __syncthreads();
+  const float fp8_scale = (FMT == 4) ? (*scale_a) * (*scale_b) : 1.0f;
+  const float* redf = reinterpret_cast<const float*>(&red[0][0][0]);
+  constexpr int OUT = 16 * 16 * G;
+  // consecutive threads take consecutive columns of one row (coalesced store);
+  // the 16x16 accumulator of a wave holds row 4*(lane>>4)+i, column lane&15
+  for (int o = threadIdx.x; o < OUT; o += NW * kWave) {
+    const int m = o / (16 * G);
+    const int nl = o - m * (16 * G);
+    const int g = nl >> 4;
+    const int c = nl & 15;
+    const int src_lane = 16 * (m >> 2) + c;
+    const int i = m & 3;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += redf[((w * G + g) * kWave + src_lane) * 4 + i];
+    const int gm = m0 + m;
+    const int gn = (cg0 + g) * 16 + c;
+    if (gm < M && gn < N) {
+      if constexpr (FMT == 4) {
+        y[(int64_t)gm * N + gn] = f32_to_bf16_rne(sum * fp8_scale);
+      } else {
+        y[(int64_t)gm * N + gn] = f32_to_f16_bits((float)scales[gn] * sum);
+      }
+    }
+  }
+}
+
+struct DecodeConfig {
+  int g;
+  int nw;
+};
+
+// Column groups per workgroup: as many as keep >= ~2 workgroups per CU busy,
+// so each X fragment loaded into registers is reused across more columns.
+DecodeConfig pick_decode_config(int64_t CG, int64_t KT) {
+  DecodeConfig c{1, 8};
+  if (CG >= 4 * 256 + 256) c.g = 4;        // e.g. N = 28672: 448 workgroups
+  else if (CG >= 2 * 256 + 128) c.g = 2;   // e.g. N = 11008: 344 workgroups
+  else c.g = 1;
+  c.nw = KT >= 8 ? 8 : 4;
+  return c;
+}
+
+template <int FMT, int G, int NW>
+hipError_t launch_cfg(const void* x, const void* w, const void* s, const float* sa,
+                      const float* sb, void* y, int64_t M, int64_t N, int64_t K, int64_t KT,
+                      int64_t CG, hipStream_t stream) {
+  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16));
+  dim3 block(NW * kWave);
+  const bool elementwise = (FMT != 4) && (K % 8 != 0);
+  if (elementwise) {
+    hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, true>), grid, block, 0, stream,
+                       (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)s, sa, sb,
+                       (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG);
+  } else {
+    hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, false>), grid, block, 0, stream,
+                       (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)s, sa, sb,
+                       (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG);
+  }
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const void* x, const void* w, const void* s, const float* sa,
+                      const float* sb, void* y, int64_t M, int64_t N, int64_t K,
+                      hipStream_t stream) {
+  const PackGeom pg = pack_geom(FMT, K, N);
+  const DecodeConfig c = pick_decode_config(pg.cg, pg.kt);
+#define QG_CASE(GG, WW)                                                                   \
+  if (c.g == GG && c.nw == WW)                                                            \
+    return launch_cfg<FMT, GG, WW>(x, w, s, sa, sb, y, M, N, K, pg.kt, pg.cg, stream);
+  QG_CASE(1, 4) QG_CASE(1, 8) QG_CASE(2, 4) QG_CASE(2, 8) QG_CASE(4, 4) QG_CASE(4, 8)
+#undef QG_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_gemm(int fmt, const void* x, const void* w_packed, const void* scales,
+                              const float* scale_a, const float* scale_b, void* y, int64_t M,
+                              int64_t N, int64_t K, hipStream_t stream) {
+  switch (fmt) {
+    case 1: return launch_fmt<1>(x, w_packed, scales, scale_a, scale_b, y, M, N, K, stream);
+    case 2: return launch_fmt<2>(x, w_packed, scales, scale_a, scale_b, y, M, N, K, stream);
+    case 4: return launch_fmt<4>(x, w_packed, scales, scale_a, scale_b, y, M, N, K, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qgemm

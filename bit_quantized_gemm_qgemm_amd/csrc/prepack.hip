@@ -1,0 +1,178 @@
+// Weight prepack: canonical layouts of the pages -> fragment tiles.
+//
+// Offline, once per weight; one thread per output 32-bit word, so every
+// output byte (padding included) is written exactly once.  The tile geometry
+// is described in qgemm_common.h.
+#include "qgemm_common.h"
+
+namespace qgemm {
+namespace {
+
+// W4A16 canonical input: uint8 [K/2, N], byte (j, n) holds k = 2j (low nibble)
+// and k = 2j + 1 (high nibble) -- W4A16 page, section 2.
+__device__ __forceinline__ uint32_t w4_code(const uint8_t* __restrict__ in, int64_t k,
+                                            int64_t n, int64_t K, int64_t N) {
+  if (k >= K || n >= N) return 8u;  // zero point: dequantizes to 0
+  const uint32_t b = in[(k >> 1) * N + n];
+  return (b >> (4 * (k & 1))) & 0xfu;
+}
+
+__global__ void prepack_w4_kernel(const uint8_t* __restrict__ in, uint32_t* __restrict__ out,
+                                  int64_t K, int64_t N, int64_t KT, int64_t words) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= words) return;
+  const int64_t tile = d >> 8;       // 256 words per 1 KB tile
+  const int within = (int)(d & 255);
+  const int lane = within >> 2;
+  const int j = within & 3;
+  const int64_t cg = tile / KT;
+  const int64_t kt = tile - cg * KT;
+  const int64_t n = cg * kTileN + (lane & 15);
+  const int64_t kbase = kt * kTileK8 + 32 * (lane >> 4) + 8 * j;
+  // nibble p holds k offset (0, 2, 4, 6, 1, 3, 5, 7)[p]
+  uint32_t word = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int koff = (p < 4) ? 2 * p : 2 * (p - 4) + 1;
+    word |= w4_code(in, kbase + koff, n, K, N) << (4 * p);
+  }
+  out[d] = word;
+}
+
+// W8A16 (int8 [K, N], stored biased by +128) and FP8 (e4m3fn [K, N], as is).
+template <bool BIAS>
+__global__ void prepack_k8_kernel(const uint8_t* __restrict__ in, uint32_t* __restrict__ out,
+                                  int64_t K, int64_t N, int64_t KT, int64_t words) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= words) return;
+  const int64_t tile = d >> 9;       // 512 words per 2 KB tile
+  const int off = (int)(d & 511) * 4;
+  const int h = off >> 10;
+  const int lane = (off & 1023) >> 4;
+  const int b0 = off & 15;
+  const int64_t cg = tile / KT;
+  const int64_t kt = tile - cg * KT;
+  const int64_t n = cg * kTileN + (lane & 15);
+  const int64_t k0 = kt * kTileK8 + 32 * (lane >> 4) + 16 * h + b0;
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t k = k0 + i;
+    uint32_t b = 0;
+    if (k < K && n < N) b = in[k * N + n];
+    if (BIAS) b = (b + 128u) & 0xffu;  // w + 128; padding becomes 0x80 (= 0)
+    word |= b << (8 * i);
+  }
+  out[d] = word;
+}
+
+// MXFP4 codes: canonical uint8 [N, K/2] (element 2j low nibble of byte j).
+// A tile byte holds elements k, k+1 with k even, exactly as the canonical
+// byte (n, k/2) does, so this is a byte gather.
+__global__ void prepack_mxfp4_codes_kernel(const uint8_t* __restrict__ in,
+                                           uint32_t* __restrict__ out, int64_t K, int64_t N,
+                                           int64_t KT, int64_t words) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= words) return;
+  const int64_t tile = d >> 9;
+  const int off = (int)(d & 511) * 4;
+  const int h = off >> 10;
+  const int lane = (off & 1023) >> 4;
+  const int b0 = off & 15;
+  const int64_t cg = tile / KT;
+  const int64_t kt = tile - cg * KT;
+  const int64_t n = cg * kTileN + (lane & 15);
+  const int64_t kbyte0 = (kt * kTileK4 + 128 * h + 32 * (lane >> 4)) / 2 + b0;
+  const int64_t row_bytes = K / 2;
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t kb = kbyte0 + i;
+    const uint32_t b = (kb < row_bytes && n < N) ? in[n * row_bytes + kb] : 0u;
+    word |= b << (8 * i);
+  }
+  out[d] = word;
+}
+
+// MXFP4 scales: canonical uint8 [N, K/32]; tile byte 2l + h is block
+// 8kt + 4h + (l >> 4) of column cg*16 + (l & 15).  Padding: 127 (= 1.0).
+__global__ void prepack_mxfp4_scales_kernel(const uint8_t* __restrict__ in,
+                                            uint32_t* __restrict__ out, int64_t K, int64_t N,
+                                            int64_t KT, int64_t words) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= words) return;
+  const int64_t tile = d >> 5;       // 32 words per 128 B tile
+  const int off = (int)(d & 31) * 4;
+  const int64_t cg = tile / KT;
+  const int64_t kt = tile - cg * KT;
+  const int64_t blocks = K / 32;
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int byte = off + i;
+    const int lane = byte >> 1;
+    const int h = byte & 1;
+    const int64_t n = cg * kTileN + (lane & 15);
+    const int64_t blk = 8 * kt + 4 * h + (lane >> 4);
+    const uint32_t e = (blk < blocks && n < N) ? in[n * blocks + blk] : (uint32_t)kE8M0One;
+    word |= e << (8 * i);
+  }
+  out[d] = word;
+}
+
+__global__ void zero_words_kernel(uint32_t* __restrict__ out, int64_t words) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (d < words) out[d] = 0u;
+}
+
+inline unsigned grid_for(int64_t words, int block) { return (unsigned)cdiv(words, block); }
+
+}  // namespace
+
+hipError_t launch_prepack(int fmt, const void* w, const void* w_scales, void* packed, int64_t K,
+                          int64_t N, hipStream_t stream) {
+  const PackGeom g = pack_geom(fmt, K, N);
+  const int block = 256;
+  const int64_t words = g.codes / 4;
+  if (words == 0) return hipSuccess;
+  const uint8_t* in = static_cast<const uint8_t*>(w);
+  uint32_t* out = static_cast<uint32_t*>(packed);
+  switch (fmt) {
+    case 1:
+      hipLaunchKernelGGL(prepack_w4_kernel, dim3(grid_for(words, block)), dim3(block), 0,
+                         stream, in, out, K, N, g.kt, words);
+      break;
+    case 2:
+      hipLaunchKernelGGL(prepack_k8_kernel<true>, dim3(grid_for(words, block)), dim3(block), 0,
+                         stream, in, out, K, N, g.kt, words);
+      break;
+    case 4:
+      hipLaunchKernelGGL(prepack_k8_kernel<false>, dim3(grid_for(words, block)), dim3(block), 0,
+                         stream, in, out, K, N, g.kt, words);
+      break;
+    case 3: {
+      hipLaunchKernelGGL(prepack_mxfp4_codes_kernel, dim3(grid_for(words, block)), dim3(block),
+                         0, stream, in, out, K, N, g.kt, words);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      // zero the alignment gap between the segments, then the scale tiles
+      const int64_t gap_words = (g.scales - g.codes) / 4;
+      if (gap_words > 0) {
+        hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, out + words,
+                           gap_words);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      const int64_t swords = (g.total - g.scales) / 4;
+      hipLaunchKernelGGL(prepack_mxfp4_scales_kernel, dim3(grid_for(swords, block)),
+                         dim3(block), 0, stream, static_cast<const uint8_t*>(w_scales),
+                         out + g.scales / 4, K, N, g.kt, swords);
+      break;
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qgemm

@@ -1,0 +1,132 @@
+// Internal definitions shared by the libqgemm HIP sources (gfx950 only).
+//
+// Packed weight layouts (produced by qgemm_prepack, private to the library)
+// -------------------------------------------------------------------------
+// All weight formats are stored as "fragment tiles": a tile covers 16 output
+// columns and a fixed span of K, and is laid out in exactly the order in which
+// the 64 lanes of a wavefront feed it to a 16x16 matrix-core instruction, so a
+// wave fetches a tile with fully coalesced 16-byte-per-lane loads and needs no
+// shuffling afterwards.  Tiles are ordered column-group-major:
+//   tile(cg, kt) at byte offset (cg * KT + kt) * TILE_BYTES.
+// Lane l of a wave owns column cg*16 + (l & 15) and the 32-element K segment
+// kt*TK + 32*(l >> 4) + [0, 32) of the tile's first (or only) half.
+//
+//   W4A16: TK = 128, 1024 B/tile.  Lane l's 16 bytes = four 32-bit words; word
+//          j holds k = base + 8j + [0, 8) as eight nibbles in the order
+//          (k0, k2, k4, k6, k1, k3, k5, k7) from the least significant nibble
+//          up, which lets one AND-OR with an fp16 exponent pattern turn two
+//          nibbles into two fp16 values at once.  Padding code: 8 (value 0).
+//   W8A16: TK = 128, 2048 B/tile, two 1 KB halves; half h holds lane l's
+//          bytes for k = base + 16h + [0, 16) at offset 1024h + 16l.  Bytes
+//          are stored biased (w + 128) so that a byte permute with an fp16
+//          exponent pattern yields 1024 + w + 128 exactly.  Padding: 0x80.
+//   FP8:   TK = 128, 2048 B/tile, same geometry as W8A16, e4m3fn bytes
+//          unbiased.  Padding: 0.
+//   MXFP4: TK = 256, 2048 B/tile of codes; half h (h = 0, 1) holds, at offset
+//          1024h + 16l, the 32 E2M1 codes k = kt*256 + 128h + 32(l>>4) +
+//          [0, 32) (even element in the low nibble).  A separate scale
+//          segment follows the code segment (256-byte aligned): 128 B per
+//          tile, byte 2l + h = E8M0 of block 8kt + 4h + (l >> 4) of lane l's
+//          column.  Padding: code 0, scale 127 (= 1.0).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qgemm {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef unsigned int uintx2 __attribute__((ext_vector_type(2)));
+typedef unsigned int uintx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kTileN = 16;                 // columns per fragment tile
+constexpr int kTileK8 = 128;               // K per tile for W4, W8, FP8
+constexpr int kTileK4 = 256;               // K per tile for MXFP4
+constexpr int kTileBytesW4 = 1024;
+constexpr int kTileBytes = 2048;           // W8, FP8, MXFP4 code tiles
+constexpr int kScaleTileBytes = 128;       // MXFP4 scale bytes per tile
+constexpr int kE8M0One = 127;              // E8M0 encoding of 1.0
+
+// Matrix-core operand formats of the scaled f8f6f4 instructions.
+constexpr int kFmtFP8 = 0;                 // e4m3 (OCP e4m3fn on gfx950)
+constexpr int kFmtFP4 = 4;                 // e2m1
+
+__host__ __device__ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Geometry of a packed weight (host and device).
+struct PackGeom {
+  int64_t cg;      // column groups of 16
+  int64_t kt;      // K tiles
+  int64_t tile;    // bytes per code tile
+  int64_t codes;   // bytes of the code segment
+  int64_t scales;  // offset of the scale segment (MXFP4) or 0
+  int64_t total;   // total bytes
+};
+
+inline PackGeom pack_geom(int fmt, int64_t K, int64_t N) {
+  PackGeom g{};
+  g.cg = cdiv(N, kTileN);
+  if (fmt == 1) {            // W4A16
+    g.kt = cdiv(K, kTileK8);
+    g.tile = kTileBytesW4;
+  } else if (fmt == 3) {     // MXFP4
+    g.kt = cdiv(K, kTileK4);
+    g.tile = kTileBytes;
+  } else {                   // W8A16, FP8
+    g.kt = cdiv(K, kTileK8);
+    g.tile = kTileBytes;
+  }
+  g.codes = g.cg * g.kt * g.tile;
+  if (fmt == 3) {
+    g.scales = cdiv(g.codes, 256) * 256;
+    g.total = g.scales + g.cg * g.kt * kScaleTileBytes;
+  } else {
+    g.scales = 0;
+    g.total = g.codes;
+  }
+  return g;
+}
+
+// ---- launchers (defined in the .hip files; all enqueue on `stream`) -------
+// Each returns hipSuccess or the launch error.
+
+hipError_t launch_prepack(int fmt, const void* w, const void* w_scales, void* packed,
+                          int64_t K, int64_t N, hipStream_t stream);
+
+hipError_t launch_quantize_mxfp4(const float* x, int64_t rows, int64_t K, uint8_t* codes,
+                                 uint8_t* e8m0, hipStream_t stream);
+hipError_t launch_quantize_fp8(const float* x, int64_t count, uint8_t* codes, float* scale,
+                               hipStream_t stream);
+
+// Small-M path (M rows handled in 16-row slabs) for W4A16 / W8A16 / FP8.
+hipError_t launch_decode_gemm(int fmt, const void* x, const void* w_packed, const void* scales,
+                              const float* scale_a, const float* scale_b, void* y,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// LDS-tiled matrix-core path for MXFP4 / FP8 (any M).
+hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const void* w_packed,
+                            const float* scale_a, const float* scale_b, void* c,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// ---- device helpers --------------------------------------------------------
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite here; a NaN
+// stays a NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // v_cvt_f16_f32, round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+}  // namespace qgemm

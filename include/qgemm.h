@@ -1,0 +1,174 @@
+/*
+ * qgemm.h -- C ABI of libqgemm: GEMMs whose low-bit operands are dequantized
+ * inside the kernel, for AMD Instinct MI355X (gfx950).
+ *
+ * Four variants:
+ *   W4A16  Y[M,N] = X[M,K] * ((code - 8) * s[n])   two INT4 codes per byte
+ *   W8A16  Y[M,N] = X[M,K] * (w * s[n])            INT8 weights
+ *   MXFP4  C[M,N] = A[M,K] * W[N,K]^T              E2M1 codes, one E8M0
+ *                                                  exponent per 32 K-elements
+ *   FP8    C[M,N] = (A[M,K] * B[K,N]) * sa * sb    e4m3fn, per-tensor scales
+ *
+ * Sources (short names):
+ *   W4A16 page -- "Triton W4A16 blocked GEMM and Blackwell NVFP4"
+ *                 (dreamvfia.cn), section 2: INT4 packing and dequant.
+ *   W8A16 page -- "Triton quantization: W8A16 weight-quantized fused GEMM"
+ *                 (datawhalechina llm-algo-leetcode, chapter 10), Steps 1-3.
+ *   MXFP4 page -- "MXFP4 matrix-multiplication kernel principle" (pwwt.cn),
+ *                 sections 1-3, eqs. (1) and (2).
+ *   FP8 page   -- "FP8 GEMM kernel in Triton via CUTLASS naming"
+ *                 (blog.hotdry.top), kernel and parameter list.
+ *
+ * Conventions for every entry point
+ *   - Array pointers are DEVICE pointers owned by the caller; one may be NULL
+ *     only when its array holds no elements.  The library
+ *     never allocates device memory and never synchronises; it enqueues its
+ *     kernels on `stream` (a hipStream_t; NULL means the null stream) and
+ *     returns.  Scalar-scale pointers (FP8) are device pointers too, so a
+ *     scale computed on the device never forces a host round trip.
+ *   - Matrices are dense and row-major with no padding between rows.
+ *   - Every array pointer must be 16-byte aligned (the kernels move 128-bit
+ *     words; MXFP4 page, section 1); fp32 scale pointers 4-byte aligned.
+ *   - Arguments are checked on the host before anything is launched.  A
+ *     status < 0 means nothing was enqueued (except QGEMM_ERR_LAUNCH, which
+ *     reports a failed launch).  No entry point prints or throws.
+ *   - M == 0 or N == 0 is a valid no-op.  Results are deterministic: the same
+ *     inputs give bit-identical outputs (no atomics in any GEMM).
+ *   - Accumulation is fp32; the output is rounded to nearest-even once.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats accepted by qgemm_prepack / qgemm_prepack_bytes. */
+enum qgemm_format {
+  QGEMM_W4A16 = 1,
+  QGEMM_W8A16 = 2,
+  QGEMM_MXFP4 = 3,
+  QGEMM_FP8 = 4
+};
+
+/* Status codes. */
+enum qgemm_status {
+  QGEMM_OK = 0,
+  QGEMM_ERR_NULL = -1,    /* a required pointer is NULL                     */
+  QGEMM_ERR_SHAPE = -2,   /* negative size, or K not a multiple the format
+                             needs, or a size too large for 32-bit indexing */
+  QGEMM_ERR_ALIGN = -3,   /* a pointer is not 16-byte (scales: 4-byte)
+                             aligned                                         */
+  QGEMM_ERR_ARCH = -4,    /* the current device is not gfx950               */
+  QGEMM_ERR_LAUNCH = -5,  /* the HIP runtime reported a launch error        */
+  QGEMM_ERR_FORMAT = -6,  /* unknown format id                               */
+  QGEMM_ERR_DEVICE = -7   /* no HIP device could be queried                  */
+};
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* qgemm_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int qgemm_abi_version(void);
+
+/*
+ * qgemm_prepack_bytes -- size in bytes of the opaque packed weight buffer for
+ * a K x N weight (N output columns; for MXFP4, N rows of W[N,K]).  Host-only,
+ * never touches the device.  Returns < 0 (a qgemm_status) on bad arguments.
+ */
+int64_t qgemm_prepack_bytes(int fmt, int64_t K, int64_t N);
+
+/*
+ * qgemm_prepack -- convert a weight from the pages' canonical layout into the
+ * kernel-native packed layout (offline; not part of the timed GEMM).
+ *
+ *   fmt = QGEMM_W4A16: w = uint8 [K/2, N]; byte (j, n) holds k = 2j in its low
+ *         nibble and k = 2j+1 in its high nibble (W4A16 page, section 2).
+ *         K must be even.  w_scales must be NULL (scales go to the GEMM).
+ *   fmt = QGEMM_W8A16: w = int8 [K, N] (W8A16 page, Step 3).  w_scales NULL.
+ *   fmt = QGEMM_MXFP4: w = uint8 codes [N, K/2] (element 2j in the low nibble
+ *         of byte j), w_scales = uint8 E8M0 [N, K/32] (MXFP4 page, sections
+ *         2-3; data and scale segments kept apart as in section 1).
+ *         K % 32 == 0.
+ *   fmt = QGEMM_FP8:   w = e4m3fn bytes B [K, N] (FP8 page kernel, B indexed
+ *         by k then n).  K % 16 == 0.  w_scales NULL (the per-tensor scale
+ *         goes to the GEMM).
+ *
+ * w_packed must hold qgemm_prepack_bytes(fmt, K, N) bytes; the library fills
+ * all of it (padding included).  The packed layout is private to the library
+ * and is consumed only by the matching qgemm_* GEMM with the same K and N.
+ */
+int qgemm_prepack(int fmt, const void* w, const void* w_scales, void* w_packed,
+                  int64_t K, int64_t N, void* stream);
+
+/*
+ * qgemm_quantize_mxfp4 -- quantize fp32 x[rows, K] to MXFP4, bit-identical to
+ * the MXFP4 page's section-3 quantizer read exactly: per row and 32-element K
+ * block, amax = max(max|x|, 1e-8f); e = ceil(log2(amax / 6)) taken exactly;
+ * E8M0 byte E = e + 127; each element goes to the nearest of
+ * {0, .5, 1, 1.5, 2, 3, 4, 6} * 2^e (ties to the smaller magnitude) with the
+ * sign bit set when x < 0.  codes: uint8 [rows, K/2], element 2j in the low
+ * nibble of byte j; e8m0: uint8 [rows, K/32].  K % 32 == 0.  Inputs must be
+ * finite (non-finite input gives unspecified codes).
+ */
+int qgemm_quantize_mxfp4(const float* x, int64_t rows, int64_t K,
+                         uint8_t* codes, uint8_t* e8m0, void* stream);
+
+/*
+ * qgemm_quantize_fp8 -- per-tensor e4m3fn quantization of fp32 x[count]
+ * (FP8 page, precision management: e4m3fn, range +-448, per-tensor scale).
+ * scale = fp32(max|x| / 448) (1.0 for an all-zero tensor) is written to the
+ * device float *scale; codes[i] = e4m3fn(fp32(x[i] / scale)), rounded to
+ * nearest-even and saturated at +-448.  Inputs must be finite.  *scale is
+ * also used as scratch between the kernels this enqueues: do not read it
+ * before the stream reaches the end of this call.
+ */
+int qgemm_quantize_fp8(const float* x, int64_t count, uint8_t* codes,
+                       float* scale, void* stream);
+
+/*
+ * qgemm_w4a16 -- Y[M,N] fp16 = X[M,K] fp16 * W_deq, W_deq[k,n] =
+ * (code[k,n] - 8) * scales[n] (W4A16 page, section 2), fp32 accumulation.
+ * w_packed comes from qgemm_prepack(QGEMM_W4A16, ..., K, N); scales is fp16
+ * [N].  K even.  The scale is applied to the fp32 column sum (equal in exact
+ * arithmetic to scaling each weight).
+ */
+int qgemm_w4a16(const void* x, const void* w_packed, const void* scales,
+                void* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * qgemm_w8a16 -- Y[M,N] fp16 = X[M,K] fp16 * (W_int8 * S) (W8A16 page,
+ * Step 1), fp32 accumulation.  w_packed from qgemm_prepack(QGEMM_W8A16, ...),
+ * scales fp16 [N].  Any K >= 0.
+ */
+int qgemm_w8a16(const void* x, const void* w_packed, const void* scales,
+                void* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * qgemm_mxfp4 -- C[M,N] bf16 = A_deq[M,K] * W_deq[N,K]^T (MXFP4 page,
+ * section 2, eqs. 1-2), each 32-element block scaled by 2^(E_A + E_W - 254)
+ * inside the matrix cores, fp32 accumulation.  a_codes uint8 [M, K/2] and
+ * a_e8m0 uint8 [M, K/32] as produced by qgemm_quantize_mxfp4; w_packed from
+ * qgemm_prepack(QGEMM_MXFP4, ..., K, N).  K % 32 == 0.
+ */
+int qgemm_mxfp4(const void* a_codes, const void* a_e8m0, const void* w_packed,
+                void* c, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * qgemm_fp8 -- C[M,N] bf16 = (A[M,K] * B[K,N]) * (*scale_a) * (*scale_b)
+ * (FP8 page: e4m3fn inputs, fp32 accumulator, per-tensor scales, bf16 out).
+ * a: e4m3fn [M, K]; b_packed from qgemm_prepack(QGEMM_FP8, ..., K, N);
+ * scale_a / scale_b: device fp32 scalars.  K % 16 == 0.
+ */
+int qgemm_fp8(const void* a, const void* b_packed, const float* scale_a,
+              const float* scale_b, void* c, int64_t M, int64_t N, int64_t K,
+              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */
