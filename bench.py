@@ -37,6 +37,7 @@ METRIC = "weight GB/s (%HBM peak) at M≤16; TFLOPS (%MFMA peak) at M=N=K=8192"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 ROTATE_BYTES = 600e6
+CALIB_BYTES = 256 * 1024 * 1024
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "decode": "bit_quantized_gemm_qgemm_amd/csrc/decode_gemm.hip",
@@ -383,6 +384,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of a graph")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run 4 plain device copies of 256 MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -394,6 +397,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calib_copy:
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"bench: ran 4 copies of {CALIB_BYTES} bytes for counter calibration")
     names = sorted(WORKLOADS) if args.all else [args.workload]
     for name in names:
         square = WORKLOADS[name][1][0] > 16
