@@ -266,6 +266,257 @@ __global__ __launch_bounds__(kThreads) void tile_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large tiles: 256 x 256 per workgroup, 128 x 128 per wave (8 x 8 fragments,
+// 256 fp32 accumulators per lane), operands moved global -> LDS by the
+// buffer unit directly (no VGPR staging, no LDS store instructions).  Buffer
+// resources bound every operand, so rows past M, column groups past N and K
+// chunks past K read as zero without predication.  Two LDS stages; the loads
+// of step k+1 run while the matrix cores work on step k.
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kBig = 256;
+
+template <bool FP4>
+struct BigCfg {
+  static constexpr int A = kBig * kKBytes;                      // 32 KB
+  static constexpr int B = kBig * kKBytes;                      // 32 KB
+  static constexpr int SA = FP4 ? kBig * 8 : 0;                 // [row][8 blocks]
+  static constexpr int SB = FP4 ? (kBig / 16) * kScaleTileBytes : 0;
+  static constexpr int STAGE = A + B + SA + SB;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // raw buffer, 32-bit data format; offsets >= bytes read as zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// lane l of the wave deposits its `size` bytes at lds_wave_base + size * l
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds_wave_base,
+                                           uint32_t voffset, int size) {
+  if (size == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 16, voffset, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_wave_base, 4, voffset, 0, 0, 0);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset past every buffer
+
+struct BigArgs {
+  int M, N, K, KT, CG, tiles_m, tiles_n;
+  uint32_t a_bytes, w_bytes, asc_bytes, wsc_bytes;
+};
+
+template <bool FP4>
+__device__ __forceinline__ void big_issue_stage(uint8_t* stage, int kt, int wave, int lane,
+                                                int m0, int cg0, const BigArgs& g,
+                                                __amdgpu_buffer_rsrc_t ra,
+                                                __amdgpu_buffer_rsrc_t rw,
+                                                __amdgpu_buffer_rsrc_t rsa,
+                                                __amdgpu_buffer_rsrc_t rsw) {
+  using C = BigCfg<FP4>;
+  const int row_bytes = FP4 ? g.K / 2 : g.K;
+  // A: 32 chunks of 1 KB (8 rows x 128 B); chunk 16-byte slots XOR-swizzled by row
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = wave * 8 + j;
+    const int r = q * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (r & 7);
+    const int kb = kt * kKBytes + 16 * chunk;
+    const uint32_t off = (kb < row_bytes) ? (uint32_t)(m0 + r) * (uint32_t)row_bytes + kb
+                                          : kOutOfRange;
+    dma_to_lds(ra, stage + q * 1024, off, 16);
+  }
+  // W: 16 fragment tiles of 2 KB, copied as is
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = wave * 8 + j;
+    const uint32_t off =
+        ((uint32_t)(cg0 + (q >> 1)) * g.KT + kt) * kTileBytes + 1024u * (q & 1) + 16u * lane;
+    dma_to_lds(rw, stage + C::A + q * 1024, off, 16);
+  }
+  if constexpr (FP4) {
+    // A scales: 256 rows x 8 bytes, row-major, in 4-byte pieces (K % 128 == 0)
+    const int sc_cols = g.K / 32;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int q = wave * 2 + j;
+      const int d = q * 64 + lane;
+      const int r = d >> 1;
+      const int blk = 8 * kt + 4 * (d & 1);
+      const uint32_t off = (blk < sc_cols) ? (uint32_t)(m0 + r) * (uint32_t)sc_cols + blk
+                                           : kOutOfRange;
+      dma_to_lds(rsa, stage + C::A + C::B + q * 256, off, 4);
+    }
+    // W scales: 16 tiles x 128 B
+    if (wave < 2) {
+      const int t = 8 * wave + (lane >> 3);
+      const uint32_t off =
+          ((uint32_t)(cg0 + t) * g.KT + kt) * kScaleTileBytes + 16u * (lane & 7);
+      dma_to_lds(rsw, stage + C::A + C::B + C::SA + wave * 1024, off, 16);
+    }
+  }
+}
+
+template <bool FP4>
+__device__ __forceinline__ void big_compute_stage(const uint8_t* stage, floatx4 (&acc)[8][8],
+                                                  int wm, int wn, int lane) {
+  using C = BigCfg<FP4>;
+  const uint8_t* la = stage;
+  const uint8_t* lb = stage + C::A;
+  const int g = lane >> 4;
+  if constexpr (!FP4) {
+    intx8 af[8];
+#pragma unroll
+    for (int fm = 0; fm < 8; ++fm) {
+      const int row = wm * 128 + fm * 16 + (lane & 15);
+      const uint8_t* rp = la + row * kKBytes;
+      const uintx4 lo = *reinterpret_cast<const uintx4*>(rp + 16 * ((2 * g) ^ (row & 7)));
+      const uintx4 hi = *reinterpret_cast<const uintx4*>(rp + 16 * ((2 * g + 1) ^ (row & 7)));
+      af[fm] = intx8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+#pragma unroll
+    for (int fn = 0; fn < 8; ++fn) {
+      const uint8_t* tp = lb + (wn * 8 + fn) * kTileBytes + 16 * lane;
+      const uintx4 lo = *reinterpret_cast<const uintx4*>(tp);
+      const uintx4 hi = *reinterpret_cast<const uintx4*>(tp + 1024);
+      const intx8 bf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+      for (int fm = 0; fm < 8; ++fm)
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            af[fm], bf, acc[fm][fn], kFmtFP8, kFmtFP8, 0, kE8M0One, 0, kE8M0One);
+    }
+  } else {
+    const uint8_t* lsa = stage + C::A + C::B;
+    const uint8_t* lsb = lsa + C::SA;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      intx8 af[8];
+      int sa[8];
+#pragma unroll
+      for (int fm = 0; fm < 8; ++fm) {
+        const int row = wm * 128 + fm * 16 + (lane & 15);
+        const uintx4 v = *reinterpret_cast<const uintx4*>(la + row * kKBytes +
+                                                          16 * ((g + 4 * h) ^ (row & 7)));
+        af[fm] = intx8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        sa[fm] = lsa[row * 8 + g + 4 * h];
+      }
+#pragma unroll
+      for (int fn = 0; fn < 8; ++fn) {
+        const int t = wn * 8 + fn;
+        const uintx4 v =
+            *reinterpret_cast<const uintx4*>(lb + t * kTileBytes + 1024 * h + 16 * lane);
+        const intx8 bf = {(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(lsb + t * 128 + 2 * lane);
+        const int sb = (int)((s2 >> (8 * h)) & 0xffu);
+#pragma unroll
+        for (int fm = 0; fm < 8; ++fm)
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[fm], bf, acc[fm][fn], kFmtFP4, kFmtFP4, 0, sa[fm], 0, sb);
+      }
+    }
+  }
+}
+
+template <bool FP4>
+__global__ __launch_bounds__(kThreads) void tile256_kernel(
+    const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_sc,
+    const uint8_t* __restrict__ wp, const uint8_t* __restrict__ w_sc,
+    const float* __restrict__ scale_a, const float* __restrict__ scale_b,
+    uint16_t* __restrict__ c, BigArgs g) {
+  using C = BigCfg<FP4>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2).  Give each XCD a contiguous range of tile ids, and walk that range in
+  // groups of 4 tile rows so the tiles resident on one XCD share A rows and W
+  // columns in its L2.
+  const int T = g.tiles_m * g.tiles_n;
+  const int bid = blockIdx.x;
+  const int id = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  constexpr int GM = 4;
+  const int group = id / (GM * g.tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(g.tiles_m - first_m, GM);
+  const int in_group = id - group * GM * g.tiles_n;
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
+  const int m0 = tm * kBig;
+  const int cg0 = tn * (kBig / 16);
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, g.a_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wp, g.w_bytes);
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(FP4 ? a_sc : a, FP4 ? g.asc_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(FP4 ? w_sc : wp, FP4 ? g.wsc_bytes : 0u);
+
+  floatx4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (g.KT > 0) big_issue_stage<FP4>(smem, 0, wave, lane, m0, cg0, g, ra, rw, rsa, rsw);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < g.KT; ++kt) {
+    uint8_t* cur = smem + (kt & 1) * C::STAGE;
+    if (kt + 1 < g.KT)
+      big_issue_stage<FP4>(smem + ((kt + 1) & 1) * C::STAGE, kt + 1, wave, lane, m0, cg0, g, ra,
+                           rw, rsa, rsw);
+    big_compute_stage<FP4>(cur, acc, wm, wn, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  const float s = FP4 ? 1.0f : (*scale_a) * (*scale_b);
+#pragma unroll
+  for (int fm = 0; fm < 8; ++fm) {
+#pragma unroll
+    for (int fn = 0; fn < 8; ++fn) {
+      const int gn = (cg0 + wn * 8 + fn) * 16 + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gm = m0 + wm * 128 + fm * 16 + 4 * (lane >> 4) + i;
+        if (gm < g.M && gn < g.N) c[(int64_t)gm * g.N + gn] = f32_to_bf16_rne(acc[fm][fn][i] * s);
+      }
+    }
+  }
+}
+
+template <bool FP4>
+hipError_t launch_big(const void* a, const void* a_sc, const void* wp, const float* sa,
+                      const float* sb, void* c, int64_t M, int64_t N, int64_t K,
+                      hipStream_t stream) {
+  const PackGeom pg = pack_geom(FP4 ? 3 : 4, K, N);
+  BigArgs g;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.KT = (int)pg.kt;
+  g.CG = (int)pg.cg;
+  g.tiles_m = (int)cdiv(M, kBig);
+  g.tiles_n = (int)cdiv(N, kBig);
+  g.a_bytes = (uint32_t)(M * (FP4 ? K / 2 : K));
+  g.w_bytes = (uint32_t)pg.codes;
+  g.asc_bytes = FP4 ? (uint32_t)(M * (K / 32)) : 0u;
+  g.wsc_bytes = FP4 ? (uint32_t)(pg.total - pg.scales) : 0u;
+  const uint8_t* w_sc = FP4 ? static_cast<const uint8_t*>(wp) + pg.scales : nullptr;
+  hipLaunchKernelGGL((tile256_kernel<FP4>), dim3((unsigned)(g.tiles_m * g.tiles_n)),
+                     dim3(kThreads), 0, stream, static_cast<const uint8_t*>(a),
+                     static_cast<const uint8_t*>(a_sc), static_cast<const uint8_t*>(wp), w_sc,
+                     sa, sb, static_cast<uint16_t*>(c), g);
+  return hipGetLastError();
+}
+
 template <bool FP4, int FM, int FN>
 hipError_t launch_tiles(const void* a, const void* a_sc, const void* wp, const float* sa,
                         const float* sb, void* c, int64_t M, int64_t N, int64_t K,
@@ -288,10 +539,18 @@ hipError_t launch_tiles(const void* a, const void* a_sc, const void* wp, const f
 hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const void* w_packed,
                             const float* scale_a, const float* scale_b, void* c, int64_t M,
                             int64_t N, int64_t K, hipStream_t stream) {
-  if (fmt == 3)
+  // large tiles once both output dimensions fill them; the 128 x 128 kernel
+  // covers the rest (and MXFP4 K that is not a multiple of 128)
+  const bool big = M > 128 && N > 128;
+  if (fmt == 3) {
+    if (big && K % 128 == 0)
+      return launch_big<true>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
     return launch_tiles<true, 4, 4>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
-  if (fmt == 4)
+  }
+  if (fmt == 4) {
+    if (big) return launch_big<false>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
     return launch_tiles<false, 4, 4>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -257,6 +257,9 @@ MX_CASES = [
     (257, 129, 544),
     (256, 256, 1024),
     (16, 300, 2048),
+    (300, 260, 640),    # 256 x 256 tiles: ragged M and N, K a multiple of 128
+    (512, 512, 1024),
+    (129, 1000, 384),   # K = 384: a half 256-wide step at the end
 ]
 
 
@@ -366,6 +369,9 @@ FP8_CASES = [
     (200, 72, 160),     # tile path, ragged
     (256, 256, 512),
     (17, 16, 16),
+    (300, 260, 528),    # 256 x 256 tiles with a 16-wide K tail
+    (512, 512, 1024),
+    (129, 1000, 256),
 ]
 
 
