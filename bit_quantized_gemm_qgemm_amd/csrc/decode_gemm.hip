@@ -10,11 +10,17 @@
 //
 // Work split: a workgroup owns G column groups (16 columns each) and one
 // 16-row slab of X; its NW waves split the K tiles round-robin, so at any time
-// the waves of a workgroup read neighbouring tiles.  Each wave keeps its fp32
-// partial sums in registers; the workgroup reduces them through LDS in a fixed
-// order (deterministic, no atomics, no workspace) and the epilogue applies the
+// the waves of a workgroup read neighbouring tiles.  Each wave keeps D K tiles
+// of loads in flight in a register ring and its fp32 partial sums in
+// registers; the workgroup reduces them through LDS in a fixed order
+// (deterministic, no atomics, no workspace) and the epilogue applies the
 // per-column scale (or the per-tensor FP8 scales) once to the fp32 sum before
 // rounding to the output type.
+//
+// K order inside a 128-wide tile (fp16 formats): matrix step s (0..3) of lane
+// group g = lane >> 4 covers k = 32 s + 8 g + [0, 8).  Both operands use the
+// same order, so the product is unchanged, and the four lanes of one X row
+// read 64 contiguous bytes per load.
 //
 // Dequantization without conversions: an fp16 with exponent field 25 and
 // mantissa field m has value 1024 + m, so OR-ing a code into the mantissa of
@@ -34,7 +40,7 @@ template <> struct DecodeTraits<1> {
 template <> struct DecodeTraits<2> {
   static constexpr int WV = 2, XV = 4, TB = kTileBytes;
 };
-// FP8: 32 B of W, 32 B of e4m3 A.
+// FP8: 32 B of W, 32 B of e4m3 A (lane holds k = 32 g + [0, 32)).
 template <> struct DecodeTraits<4> {
   static constexpr int WV = 2, XV = 2, TB = kTileBytes;
 };
@@ -95,37 +101,45 @@ struct Chunk {
 // parts stay in SGPRs; each lane adds a 32-bit offset.
 struct DecodeAddr {
   const uint8_t* x;       // activations
-  uint32_t xlane;         // byte offset of this lane's row and K segment
+  uint32_t xlane;         // byte offset of this lane's row and first K piece
   const uint8_t* w;       // first weight tile of this workgroup
   int64_t cg_stride;      // bytes between column groups
   int cg_last;            // last valid group index relative to this workgroup
   uint32_t wlane;         // 16 * lane
   int K;
-  int kseg;               // this lane's K offset inside a tile (0, 32, 64, 96)
+  int g;                  // lane group, lane >> 4
 };
 
-// Load lane data of K tile `kt`: the lane's 32-element K segment of X (or A)
-// and of each of the G weight tiles.  X pieces past K read as zero.  Rows past
-// M load row M-1 instead (their outputs are never stored); groups past the
-// last column load the last group (likewise discarded).
+// K index of the first element of X piece p of lane group g in tile kt.
+template <int FMT>
+__device__ __forceinline__ int piece_k(int kt, int g, int p) {
+  if constexpr (FMT == 4) return kt * kTileK8 + 32 * g + 16 * p;   // e4m3: contiguous 32
+  else return kt * kTileK8 + 32 * p + 8 * g;                        // fp16: step p
+}
+
+// Load lane data of K tile `kt`: the lane's X (or A) pieces and each of the G
+// weight tiles.  X pieces past K read as zero.  Rows past M load row M-1
+// instead (their outputs are never stored); groups past the last column load
+// the last group (likewise discarded).
 template <int FMT, int G, bool X_ELEMENTWISE>
 __device__ __forceinline__ void load_chunk(Chunk<FMT, G>& ch, const DecodeAddr& ad, int kt) {
   constexpr int XV = DecodeTraits<FMT>::XV;
   constexpr int TB = DecodeTraits<FMT>::TB;
-  constexpr int XB = (FMT == 4) ? 1 : 2;          // bytes per activation element
-  constexpr int PIECE = 16 / XB;                  // elements per 16-byte piece
+  constexpr int XB = (FMT == 4) ? 1 : 2;           // bytes per activation element
+  constexpr int PSTRIDE = (FMT == 4) ? 16 : 64;    // bytes between a lane's pieces
   const uint8_t* xk = ad.x + (int64_t)kt * kTileK8 * XB;   // uniform
   const bool full = (kt + 1) * kTileK8 <= ad.K;            // uniform
   if constexpr (!X_ELEMENTWISE) {
     if (full) {
 #pragma unroll
       for (int p = 0; p < XV; ++p)
-        ch.x[p] = *reinterpret_cast<const uintx4*>(xk + ad.xlane + 16 * p);
+        ch.x[p] = *reinterpret_cast<const uintx4*>(xk + ad.xlane + PSTRIDE * p);
     } else {
+      // K % 8 == 0 (fp16) or K % 16 == 0 (e4m3): a piece is wholly in or out
 #pragma unroll
       for (int p = 0; p < XV; ++p) {
-        const int k = kt * kTileK8 + ad.kseg + PIECE * p;
-        ch.x[p] = (k < ad.K) ? *reinterpret_cast<const uintx4*>(xk + ad.xlane + 16 * p)
+        const int k = piece_k<FMT>(kt, ad.g, p);
+        ch.x[p] = (k < ad.K) ? *reinterpret_cast<const uintx4*>(xk + ad.xlane + PSTRIDE * p)
                              : uintx4{0, 0, 0, 0};
       }
     }
@@ -137,9 +151,10 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G>& ch, const DecodeAddr& 
       uint32_t d[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int k = kt * kTileK8 + ad.kseg + 8 * p + 2 * j;
-        const uint32_t lo = (k < ad.K) ? xr[8 * p + 2 * j] : 0u;
-        const uint32_t hi = (k + 1 < ad.K) ? xr[8 * p + 2 * j + 1] : 0u;
+        const int k = piece_k<FMT>(kt, ad.g, p) + 2 * j;
+        const int e = (PSTRIDE / 2) * p + 2 * j;
+        const uint32_t lo = (k < ad.K) ? xr[e] : 0u;
+        const uint32_t hi = (k + 1 < ad.K) ? xr[e + 1] : 0u;
         d[j] = lo | (hi << 16);
       }
       ch.x[p] = uintx4{d[0], d[1], d[2], d[3]};
@@ -189,13 +204,14 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G>& ch, floatx4 (
   }
 }
 
-template <int FMT, int G, int NW, bool X_ELEMENTWISE>
+template <int FMT, int G, int NW, int D, bool X_ELEMENTWISE>
 __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ wp,
     const _Float16* __restrict__ scales, const float* __restrict__ scale_a,
     const float* __restrict__ scale_b, uint16_t* __restrict__ y, int M, int N, int K, int KT,
     int CG) {
   static_assert(NW >= 2, "the K split needs at least two waves");
+  static_assert(D >= 2 && D <= 4, "prefetch depth 2..4");
   constexpr int TB = DecodeTraits<FMT>::TB;
   constexpr int XB = (FMT == 4) ? 1 : 2;
   __shared__ floatx4 red[NW][G][kWave];
@@ -207,9 +223,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   const int row = min(m0 + (lane & 15), M - 1);
 
   DecodeAddr ad;
-  ad.kseg = 32 * (lane >> 4);
+  ad.g = lane >> 4;
   ad.x = x;
-  ad.xlane = (uint32_t)(((int64_t)row * K + ad.kseg) * XB);
+  ad.xlane = (uint32_t)(((int64_t)row * K + (FMT == 4 ? 32 : 8) * ad.g) * XB);
   ad.cg_stride = (int64_t)KT * TB;
   ad.w = wp + (int64_t)cg0 * ad.cg_stride;
   ad.cg_last = CG - 1 - cg0;
@@ -223,18 +239,21 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // K tiles wave, wave + NW, ...; two register buffers, one tile of look-ahead
-  Chunk<FMT, G> b0, b1;
-  int kt = wave;
-  if (kt < KT) load_chunk<FMT, G, X_ELEMENTWISE>(b0, ad, kt);
-  while (kt < KT) {
-    if (kt + NW < KT) load_chunk<FMT, G, X_ELEMENTWISE>(b1, ad, kt + NW);
-    compute_chunk<FMT, G>(b0, acc, mk);
-    kt += NW;
-    if (kt >= KT) break;
-    if (kt + NW < KT) load_chunk<FMT, G, X_ELEMENTWISE>(b0, ad, kt + NW);
-    compute_chunk<FMT, G>(b1, acc, mk);
-    kt += NW;
+  // K tiles wave, wave + NW, ...; a ring of D register buffers keeps D tiles
+  // of loads in flight per wave
+  Chunk<FMT, G> ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (wave + d * NW < KT) load_chunk<FMT, G, X_ELEMENTWISE>(ring[d], ad, wave + d * NW);
+  for (int base = wave; base < KT; base += D * NW) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int kt = base + d * NW;
+      if (kt < KT) {
+        compute_chunk<FMT, G>(ring[d], acc, mk);
+        if (kt + D * NW < KT) load_chunk<FMT, G, X_ELEMENTWISE>(ring[d], ad, kt + D * NW);
+      }
+    }
   }
 
   // ---- reduce the NW partial tiles in a fixed order
@@ -269,38 +288,68 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
 }
 
 struct DecodeConfig {
-  int g;
-  int nw;
+  int g;   // column groups (of 16) per workgroup
+  int nw;  // waves per workgroup (K split)
+  int d;   // K tiles in flight per wave
 };
 
-// Column groups per workgroup: as many as keep >= ~2 workgroups per CU busy,
-// so each X fragment loaded into registers is reused across more columns.
-DecodeConfig pick_decode_config(int64_t CG, int64_t KT) {
-  DecodeConfig c{1, 8};
-  if (CG >= 4 * 256 + 256) c.g = 4;        // e.g. N = 28672: 448 workgroups
-  else if (CG >= 2 * 256 + 128) c.g = 2;   // e.g. N = 11008: 344 workgroups
-  else c.g = 1;
-  c.nw = KT >= 8 ? 8 : 4;
+// Launch shape by format and M (per 16-row slab), from measurements on
+// MI355X at the decode workloads (W8A16 K=4096 N=11008, W4A16 K=8192
+// N=28672, FP8 K=N=8192): with one or a few rows, more workgroups (small G)
+// stream the weight fastest; with 16 rows each X fragment is worth reusing
+// across more columns (large G), which cuts X traffic from L2 (it scales as
+// X bytes * N / (16 G)).  G then shrinks until at least 128 workgroups exist,
+// and short K uses four waves.
+DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
+  const int64_t rows = M < 16 ? M : 16;
+  DecodeConfig c{2, 8, 2};
+  if (fmt == 1) {
+    c = rows <= 4 ? DecodeConfig{2, 8, 2} : rows <= 8 ? DecodeConfig{4, 4, 2} : DecodeConfig{8, 8, 3};
+  } else if (fmt == 2) {
+    c = rows <= 4 ? DecodeConfig{1, 8, 2} : DecodeConfig{4, 8, 3};
+  } else {
+    c = DecodeConfig{2, 8, 2};
+  }
+  while (c.g > 1 && cdiv(CG, c.g) < 128) c.g /= 2;
+  if (KT < 16) c.nw = 4;
   return c;
 }
 
-template <int FMT, int G, int NW>
+template <int FMT, int G, int NW, int D, bool ELEMENTWISE>
 hipError_t launch_cfg(const void* x, const void* w, const void* s, const float* sa,
                       const float* sb, void* y, int64_t M, int64_t N, int64_t K, int64_t KT,
                       int64_t CG, hipStream_t stream) {
   dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16));
   dim3 block(NW * kWave);
-  const bool elementwise = (FMT != 4) && (K % 8 != 0);
-  if (elementwise) {
-    hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, true>), grid, block, 0, stream,
-                       (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)s, sa, sb,
-                       (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG);
-  } else {
-    hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, false>), grid, block, 0, stream,
-                       (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)s, sa, sb,
-                       (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG);
-  }
+  hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, D, ELEMENTWISE>), grid, block, 0, stream,
+                     (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)s, sa, sb,
+                     (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG);
   return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt_cfg(const DecodeConfig& c, const void* x, const void* w, const void* s,
+                          const float* sa, const float* sb, void* y, int64_t M, int64_t N,
+                          int64_t K, int64_t KT, int64_t CG, hipStream_t stream) {
+  // fp16 X rows that are not 16-byte aligned (K % 8 != 0) take one
+  // element-wise configuration
+  if (FMT != 4 && K % 8 != 0)
+    return launch_cfg<FMT, 1, 4, 2, true>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream);
+#define QG_CASE(GG, WW, DD)                                                                 \
+  if (c.g == GG && c.nw == WW && c.d == DD)                                                 \
+    return launch_cfg<FMT, GG, WW, DD, false>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream);
+#define QG_G(GG) QG_CASE(GG, 4, 2) QG_CASE(GG, 8, 2) QG_CASE(GG, 4, 3) QG_CASE(GG, 8, 3)
+  QG_G(1) QG_G(2) QG_G(4)
+  if constexpr (FMT == 1) {   // eight groups only pay off (and fit in registers) for INT4
+    QG_G(8)
+  }
+#ifdef QGEMM_DECODE_SWEEP
+  QG_CASE(1, 4, 4) QG_CASE(1, 8, 4) QG_CASE(2, 4, 4) QG_CASE(2, 8, 4) QG_CASE(4, 4, 4)
+  QG_CASE(4, 8, 4) QG_CASE(1, 16, 2) QG_CASE(2, 16, 2) QG_CASE(1, 16, 3) QG_CASE(2, 16, 3)
+#endif
+#undef QG_G
+#undef QG_CASE
+  return hipErrorInvalidValue;
 }
 
 template <int FMT>
@@ -308,13 +357,8 @@ hipError_t launch_fmt(const void* x, const void* w, const void* s, const float* 
                       const float* sb, void* y, int64_t M, int64_t N, int64_t K,
                       hipStream_t stream) {
   const PackGeom pg = pack_geom(FMT, K, N);
-  const DecodeConfig c = pick_decode_config(pg.cg, pg.kt);
-#define QG_CASE(GG, WW)                                                                   \
-  if (c.g == GG && c.nw == WW)                                                            \
-    return launch_cfg<FMT, GG, WW>(x, w, s, sa, sb, y, M, N, K, pg.kt, pg.cg, stream);
-  QG_CASE(1, 4) QG_CASE(1, 8) QG_CASE(2, 4) QG_CASE(2, 8) QG_CASE(4, 4) QG_CASE(4, 8)
-#undef QG_CASE
-  return hipErrorInvalidValue;
+  const DecodeConfig c = pick_decode_config(FMT, M, pg.cg, pg.kt);
+  return launch_fmt_cfg<FMT>(c, x, w, s, sa, sb, y, M, N, K, pg.kt, pg.cg, stream);
 }
 
 }  // namespace

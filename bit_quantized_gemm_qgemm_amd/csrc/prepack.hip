@@ -28,7 +28,8 @@ __global__ void prepack_w4_kernel(const uint8_t* __restrict__ in, uint32_t* __re
   const int64_t cg = tile / KT;
   const int64_t kt = tile - cg * KT;
   const int64_t n = cg * kTileN + (lane & 15);
-  const int64_t kbase = kt * kTileK8 + 32 * (lane >> 4) + 8 * j;
+  // word j of lane l feeds matrix step j: k = 32 j + 8 (l >> 4) + [0, 8)
+  const int64_t kbase = kt * kTileK8 + 32 * j + 8 * (lane >> 4);
   // nibble p holds k offset (0, 2, 4, 6, 1, 3, 5, 7)[p]
   uint32_t word = 0;
 #pragma unroll
@@ -39,7 +40,8 @@ __global__ void prepack_w4_kernel(const uint8_t* __restrict__ in, uint32_t* __re
   out[d] = word;
 }
 
-// W8A16 (int8 [K, N], stored biased by +128) and FP8 (e4m3fn [K, N], as is).
+// W8A16 (int8 [K, N], stored biased by +128, bytes in matrix-step order) and
+// FP8 (e4m3fn [K, N], as is, lane l holding k = 32 (l >> 4) + [0, 32)).
 template <bool BIAS>
 __global__ void prepack_k8_kernel(const uint8_t* __restrict__ in, uint32_t* __restrict__ out,
                                   int64_t K, int64_t N, int64_t KT, int64_t words) {
@@ -53,7 +55,10 @@ __global__ void prepack_k8_kernel(const uint8_t* __restrict__ in, uint32_t* __re
   const int64_t cg = tile / KT;
   const int64_t kt = tile - cg * KT;
   const int64_t n = cg * kTileN + (lane & 15);
-  const int64_t k0 = kt * kTileK8 + 32 * (lane >> 4) + 16 * h + b0;
+  // W8A16: byte b of half h feeds step s = 2h + b/8: k = 32 s + 8 (l >> 4) + b % 8
+  // FP8:    byte b of half h is k = 32 (l >> 4) + 16 h + b
+  const int64_t k0 = BIAS ? kt * kTileK8 + 32 * (2 * h + (b0 >> 3)) + 8 * (lane >> 4) + (b0 & 7)
+                          : kt * kTileK8 + 32 * (lane >> 4) + 16 * h + b0;
   uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

@@ -8,20 +8,22 @@
 // wave fetches a tile with fully coalesced 16-byte-per-lane loads and needs no
 // shuffling afterwards.  Tiles are ordered column-group-major:
 //   tile(cg, kt) at byte offset (cg * KT + kt) * TILE_BYTES.
-// Lane l of a wave owns column cg*16 + (l & 15) and the 32-element K segment
-// kt*TK + 32*(l >> 4) + [0, 32) of the tile's first (or only) half.
+// Lane l of a wave owns column cg*16 + (l & 15); g = l >> 4 is its lane group.
 //
 //   W4A16: TK = 128, 1024 B/tile.  Lane l's 16 bytes = four 32-bit words; word
-//          j holds k = base + 8j + [0, 8) as eight nibbles in the order
-//          (k0, k2, k4, k6, k1, k3, k5, k7) from the least significant nibble
-//          up, which lets one AND-OR with an fp16 exponent pattern turn two
-//          nibbles into two fp16 values at once.  Padding code: 8 (value 0).
-//   W8A16: TK = 128, 2048 B/tile, two 1 KB halves; half h holds lane l's
-//          bytes for k = base + 16h + [0, 16) at offset 1024h + 16l.  Bytes
-//          are stored biased (w + 128) so that a byte permute with an fp16
+//          s feeds f16 matrix step s and holds k = kt*128 + 32s + 8g + [0, 8)
+//          as eight nibbles in the order (k0, k2, k4, k6, k1, k3, k5, k7) from
+//          the least significant nibble up, which lets one AND-OR with an fp16
+//          exponent pattern turn two nibbles into two fp16 values at once.
+//          Padding code: 8 (value 0).
+//   W8A16: TK = 128, 2048 B/tile, two 1 KB halves; lane l's 16 bytes of half
+//          h (at offset 1024h + 16l) feed steps 2h and 2h+1, 8 bytes each:
+//          byte b holds k = kt*128 + 32(2h + b/8) + 8g + b%8.  Bytes are
+//          stored biased (w + 128) so that a byte permute with an fp16
 //          exponent pattern yields 1024 + w + 128 exactly.  Padding: 0x80.
-//   FP8:   TK = 128, 2048 B/tile, same geometry as W8A16, e4m3fn bytes
-//          unbiased.  Padding: 0.
+//   FP8:   TK = 128, 2048 B/tile, same geometry; lane l holds the 32-element
+//          segment k = kt*128 + 32g + [0, 32): bytes 16h + [0, 16) of it at
+//          offset 1024h + 16l.  e4m3fn bytes unbiased.  Padding: 0.
 //   MXFP4: TK = 256, 2048 B/tile of codes; half h (h = 0, 1) holds, at offset
 //          1024h + 16l, the 32 E2M1 codes k = kt*256 + 128h + 32(l>>4) +
 //          [0, 32) (even element in the low nibble).  A separate scale

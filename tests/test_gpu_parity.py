@@ -70,6 +70,8 @@ W4_CASES = [
     (40, 512, 64),      # M > 16: several 16-row slabs
     (17, 128, 16),
     (8, 2048, 700),
+    (16, 256, 16400),   # eight column groups per workgroup, ragged last workgroup
+    (6, 384, 9000),     # four groups per workgroup (M in 5..8)
 ]
 
 
@@ -125,6 +127,8 @@ W8_CASES = [
     (16, 1000, 129),    # K % 128 != 0
     (33, 256, 64),      # M > 16
     (2, 64, 1),
+    (9, 200, 9000),     # four groups, three tiles in flight, short K, ragged N
+    (16, 520, 2100),
 ]
 
 
