@@ -101,24 +101,27 @@ __global__ void prepack_mxfp4_codes_kernel(const uint8_t* __restrict__ in,
 
 // MXFP4 scales: canonical uint8 [N, K/32]; tile byte 2l + h is block
 // 8kt + 4h + (l >> 4) of column cg*16 + (l & 15).  Padding: 127 (= 1.0).
+// Scale segment: for each group of 8 column tiles (128 columns) and each
+// 128-element K step ks (two steps per code tile), 512 bytes ordered
+// [lane 64][tile 8]: byte (lane, j) is the E8M0 of column 128*c8 + 16*j +
+// (lane & 15) for block 4*ks + (lane >> 4).
 __global__ void prepack_mxfp4_scales_kernel(const uint8_t* __restrict__ in,
                                             uint32_t* __restrict__ out, int64_t K, int64_t N,
-                                            int64_t KT, int64_t words) {
+                                            int64_t KS, int64_t words) {
   const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (d >= words) return;
-  const int64_t tile = d >> 5;       // 32 words per 128 B tile
-  const int off = (int)(d & 31) * 4;
-  const int64_t cg = tile / KT;
-  const int64_t kt = tile - cg * KT;
+  const int64_t chunk = d >> 7;      // 128 words per 512 B (group, step) chunk
+  const int w = (int)(d & 127);
+  const int64_t c8 = chunk / KS;
+  const int64_t ks = chunk - c8 * KS;
+  const int lane = w >> 1;
   const int64_t blocks = K / 32;
+  const int64_t blk = 4 * ks + (lane >> 4);
   uint32_t word = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int byte = off + i;
-    const int lane = byte >> 1;
-    const int h = byte & 1;
-    const int64_t n = cg * kTileN + (lane & 15);
-    const int64_t blk = 8 * kt + 4 * h + (lane >> 4);
+    const int j = 4 * (w & 1) + i;
+    const int64_t n = (8 * c8 + j) * kTileN + (lane & 15);
     const uint32_t e = (blk < blocks && n < N) ? in[n * blocks + blk] : (uint32_t)kE8M0One;
     word |= e << (8 * i);
   }
@@ -171,7 +174,7 @@ hipError_t launch_prepack(int fmt, const void* w, const void* w_scales, void* pa
       const int64_t swords = (g.total - g.scales) / 4;
       hipLaunchKernelGGL(prepack_mxfp4_scales_kernel, dim3(grid_for(swords, block)),
                          dim3(block), 0, stream, static_cast<const uint8_t*>(w_scales),
-                         out + g.scales / 4, K, N, g.kt, swords);
+                         out + g.scales / 4, K, N, 2 * g.kt, swords);
       break;
     }
     default:

@@ -26,10 +26,14 @@
 //          offset 1024h + 16l.  e4m3fn bytes unbiased.  Padding: 0.
 //   MXFP4: TK = 256, 2048 B/tile of codes; half h (h = 0, 1) holds, at offset
 //          1024h + 16l, the 32 E2M1 codes k = kt*256 + 128h + 32(l>>4) +
-//          [0, 32) (even element in the low nibble).  A separate scale
-//          segment follows the code segment (256-byte aligned): 128 B per
-//          tile, byte 2l + h = E8M0 of block 8kt + 4h + (l >> 4) of lane l's
-//          column.  Padding: code 0, scale 127 (= 1.0).
+//          [0, 32) (even element in the low nibble).  Each half is one
+//          128-element K step ks = 2kt + h.  A separate scale segment follows
+//          the code segment (256-byte aligned), ordered by groups of 8 column
+//          tiles c8 = cg / 8: for each (c8, ks), 512 B at (c8 * 2KT + ks) * 512
+//          laid out [lane 64][j 8]; byte (l, j) = E8M0 of column
+//          (8 c8 + j) * 16 + (l & 15), block 4ks + (l >> 4).  A lane reads the
+//          scales of all 8 tiles of a step with one 8-byte load.
+//          Padding: code 0, scale 127 (= 1.0).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,6 +44,7 @@ namespace qgemm {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef unsigned int uintx2 __attribute__((ext_vector_type(2)));
@@ -86,7 +91,7 @@ inline PackGeom pack_geom(int fmt, int64_t K, int64_t N) {
   g.codes = g.cg * g.kt * g.tile;
   if (fmt == 3) {
     g.scales = cdiv(g.codes, 256) * 256;
-    g.total = g.scales + g.cg * g.kt * kScaleTileBytes;
+    g.total = g.scales + cdiv(g.cg, 8) * g.kt * 8 * kScaleTileBytes;
   } else {
     g.scales = 0;
     g.total = g.codes;

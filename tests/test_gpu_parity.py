@@ -264,6 +264,8 @@ MX_CASES = [
     (300, 260, 640),    # 256 x 256 tiles: ragged M and N, K a multiple of 128
     (512, 512, 1024),
     (129, 1000, 384),   # K = 384: a half 256-wide step at the end
+    (257, 384, 1280),   # 256 x 256 tiles, several pipeline iterations
+    (160, 136, 896),    # last 128-wide step all padding; 9 column tiles
 ]
 
 
@@ -298,6 +300,25 @@ def test_mxfp4_one_hot_reads_back_dequantized_weights():
         ae = np.full((m, k // 32), 127, np.uint8)
         c = host(qg.qgemm_mxfp4(dev(ac), dev(ae), wp, n))
         assert np.array_equal(c, wdeq[:, k0:k0 + m].T)
+
+
+def test_mxfp4_one_hot_through_large_tiles():
+    """One-hot read-back through the 256 x 256 path (M, N > 128): every
+    (row tile, column tile, K step, scale byte) mapping is hit, bit-exact."""
+    n, k = 272, 512
+    case_id("mxfp4 one-hot large tiles", n, k)
+    _, w = wl.mxfp4_operands(1, n, k, seed=9)
+    wc, we = oracle.mxfp4_quantize(w)
+    wdeq = oracle.mxfp4_dequant(wc, we)
+    wp = qg.qgemm_prepack("mxfp4", dev(wc), k, n, w_scales=dev(we))
+    m = 300
+    ks = (np.arange(m) * 37) % k           # row i reads back column k_i of W
+    codes = np.zeros((m, k), np.uint8)
+    codes[np.arange(m), ks] = 0b0010        # +1.0
+    ac = oracle.pack_nibbles_last_axis(codes)
+    ae = np.full((m, k // 32), 127, np.uint8)
+    c = host(qg.qgemm_mxfp4(dev(ac), dev(ae), wp, n))
+    assert np.array_equal(c, wdeq[:, ks].T)
 
 
 def test_mxfp4_scale_product_is_exponent_add_on_device():
@@ -376,6 +397,8 @@ FP8_CASES = [
     (300, 260, 528),    # 256 x 256 tiles with a 16-wide K tail
     (512, 512, 1024),
     (129, 1000, 256),
+    (257, 300, 384),    # 256 x 256 tiles, six 64-wide steps
+    (136, 200, 2064),   # 256 x 256 tiles, K tail of 16 in the last step
 ]
 
 
@@ -410,6 +433,23 @@ def test_fp8_one_hot_reads_back_codes(m):
         a[np.arange(m), k0 + np.arange(m)] = 0x38    # e4m3 1.0
         c = host(qg.qgemm_fp8(dev(a), bp, one, one, n))
         assert np.array_equal(c, oracle.round_bf16(bdeq[k0:k0 + m]))
+
+
+def test_fp8_one_hot_through_large_tiles():
+    """One-hot read-back through the 256 x 256 path (M, N > 128), bit-exact:
+    pins the 32 x 32 accumulator layout and the K order of both operands."""
+    m, n, k = 300, 272, 384
+    case_id("fp8 one-hot large tiles", m, n, k)
+    b = np.random.default_rng(6).integers(0, 256, size=(k, n)).astype(np.uint8)
+    b[(b & 0x7f) == 0x7f] = 0x3c                     # no NaN codes
+    bdeq = oracle.e4m3fn_decode(b)
+    bp = qg.qgemm_prepack("fp8", dev(b), k, n)
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    ks = (np.arange(m) * 37) % k
+    a = np.zeros((m, k), np.uint8)
+    a[np.arange(m), ks] = 0x38                       # e4m3 1.0
+    c = host(qg.qgemm_fp8(dev(a), bp, one, one, n))
+    assert np.array_equal(c, oracle.round_bf16(bdeq[ks]))
 
 
 @pytest.mark.parametrize("m", [16, 8192])
