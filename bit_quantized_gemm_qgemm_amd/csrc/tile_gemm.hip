@@ -323,7 +323,10 @@ struct PipeArgs {
 };
 
 // Stage layout (both formats):
-//   A   [256 rows][64 B]; 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 3)
+//   A   [256 rows][64 B]; 16-byte chunk c of row r sits in slot c ^ swizzle(r),
+//       with swizzle(r) = (r >> 1) & 3 for MXFP4 and (r >> 2) & 3 for FP8: the
+//       row bits that keep each format's fragment reads free of bank
+//       conflicts (16 rows x 4 lane groups for MXFP4, 32 rows x 2 for FP8)
 //   W   16 column tiles x 1 KB
 //   MXFP4 only: A scales [256 rows][4 blocks]; W scales [wn 2][lane 64][tile 8]
 template <bool FP4>
@@ -335,6 +338,11 @@ struct PipeCfg {
   static constexpr int STAGE = A + B + SA + SB;
   static constexpr int DMA = FP4 ? 10 : 8;        // copies per wave per stage
 };
+
+template <bool FP4>
+__device__ __forceinline__ int pipe_swizzle(int r) {
+  return FP4 ? (r >> 1) & 3 : (r >> 2) & 3;
+}
 
 template <bool FP4>
 __device__ __forceinline__ void pipe_issue(uint8_t* st, int ks, int wave, int lane, int m0,
@@ -350,7 +358,7 @@ __device__ __forceinline__ void pipe_issue(uint8_t* st, int ks, int wave, int la
   for (int j = 0; j < 4; ++j) {
     const int q = 4 * wave + j;
     const int r = 16 * q + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 1) & 3);
+    const int c = (lane & 3) ^ pipe_swizzle<FP4>(r);
     const int kb = ks * kStepBytes + 16 * c;
     const uint32_t off = kb < row_bytes ? (uint32_t)(m0 + r) * (uint32_t)row_bytes + kb
                                         : kOutOfRange;
@@ -399,7 +407,7 @@ struct Fp4Pipe {
     using C = PipeCfg<true>;
     const int r = wm * 128 + (lane & 15), grp = lane >> 4;
     Lane L;
-    L.a = r * kStepBytes + 16 * (grp ^ ((lane >> 1) & 3));
+    L.a = r * kStepBytes + 16 * (grp ^ pipe_swizzle<true>(r));
     L.sa = C::A + C::B + r * 4 + grp;
     L.b = C::A + wn * 8 * 1024 + 16 * lane;
     L.sb = C::A + C::B + C::SA + wn * 512 + 8 * lane;
@@ -466,7 +474,7 @@ struct Fp8Pipe {
   };
   __device__ __forceinline__ static Lane lane_offsets(int wm, int wn, int lane) {
     using C = PipeCfg<false>;
-    const int r = wm * 128 + (lane & 31), hh = lane >> 5, swz = (lane >> 1) & 3;
+    const int r = wm * 128 + (lane & 31), hh = lane >> 5, swz = pipe_swizzle<false>(r);
     Lane L;
     L.alo = r * kStepBytes + 16 * ((2 * hh) ^ swz);
     L.ahi = r * kStepBytes + 16 * ((2 * hh + 1) ^ swz);
