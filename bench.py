@@ -372,7 +372,11 @@ def kernel_name(setup, m):
     mangled template instance)."""
     if setup.kind == "decode":
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
-    return f"tile256_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
+    # same rule as the library's dispatch between its two tile kernels
+    k_tiles = -(-setup.k // (256 if setup.fmt == "mxfp4" else 128))
+    big = m > 128 and setup.n > 128 and k_tiles >= 2 and (setup.fmt != "mxfp4" or setup.k % 128 == 0)
+    name = "pipe256_kernel" if big else "tile_gemm_kernel"
+    return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
 
 
 def main():
