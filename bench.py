@@ -52,6 +52,9 @@ WORKLOADS = {
     "mxfp4_square": ("mxfp4", (8192,), 8192, 8192),
     "fp8_square": ("fp8", (8192,), 8192, 8192),
     "fp8_decode": ("fp8", (16,), 8192, 8192),
+    # the W8A16 page's fused-versus-explicit-dequant comparison shape
+    "w8a16_square": ("w8a16", (4096,), 4096, 4096),
+    "w4a16_square": ("w4a16", (4096,), 4096, 4096),
 }
 DEFAULT_WORKLOAD = "w8a16_decode"
 
@@ -80,7 +83,8 @@ class Setup:
         self.name = name
         fmt, ms, n, k = WORKLOADS[name]
         self.fmt, self.ms, self.n, self.k = fmt, ms, n, k
-        self.kind = "decode" if (fmt in ("w4a16", "w8a16") or max(ms) <= 16) else "tile"
+        self.kind = "decode" if max(ms) <= 16 else "tile"
+        self.explicit = None   # W8A16 square: the explicit dequantize-then-matmul comparison
         dev = torch.device("cuda:0")
         mmax = max(ms)
         self.calls = []        # per call: (launch(copy) -> None, alg_bytes, weight_bytes, flops)
@@ -96,6 +100,11 @@ class Setup:
             self.copies = self._rotate(packed, w_bytes)
             fn = qg.qgemm_w4a16 if fmt == "w4a16" else qg.qgemm_w8a16
             self.dtype = "f16"
+            if fmt == "w8a16" and self.kind == "tile":
+                w8 = torch.from_numpy(w).to(dev)
+                xm = x_d
+                # the pages' unfused baseline: W_fp16 = W_int8 * s in HBM, then a GEMM
+                self.explicit = lambda: torch.matmul(xm, w8.to(torch.float16) * s_d)
             for m in ms:
                 xm = x_d[:m].contiguous()
                 out = torch.empty((m, n), dtype=torch.float16, device=dev)
@@ -218,6 +227,22 @@ def per_call_times(setup, reps=60):
     return out
 
 
+def time_callable(fn, reps=20):
+    """Average device time of a torch callable (HIP events on the current stream)."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on the host
 # ---------------------------------------------------------------------------
@@ -237,7 +262,7 @@ def cpu_baseline(name, budget_s=10.0):
 
     fmt, ms, n, k = WORKLOADS[name]
     mmax = max(ms)
-    if fmt in ("w4a16", "w8a16"):
+    if fmt in ("w4a16", "w8a16") and mmax <= 16:
         gen = wl.w4a16 if fmt == "w4a16" else wl.w8a16
         gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16
         # bounded sample: the full K and a column slice sized for ~1 s per step
@@ -258,10 +283,15 @@ def cpu_baseline(name, budget_s=10.0):
         sample = (f"oracle {fmt} steps (M={list(ms)}), K={k}, {cols} of {n} columns, "
                   f"{done} steps in {dt:.1f} s")
     else:
-        # bounded sample: 256 rows of A against all of W (MXFP4) / B (FP8)
+        # bounded sample: 256 rows of X / A against the whole weight
         rows = 256
         unit = "TFLOP/s"
-        if fmt == "mxfp4":
+        if fmt in ("w4a16", "w8a16"):
+            gen = wl.w4a16 if fmt == "w4a16" else wl.w8a16
+            gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16
+            x, w, s = gen(rows, k, n)
+            run = lambda: gemm(x, w, s)  # noqa: E731
+        elif fmt == "mxfp4":
             a, w = wl.mxfp4_operands(rows, n, k)
             ac, ae = oracle.mxfp4_quantize(a)
             wc, we = oracle.mxfp4_quantize(w)
@@ -339,6 +369,8 @@ def run(name, steps, warmup, with_cpu, use_graph):
         if not decode:
             d["pct_mfma"] = round(100 * fl / t / 1e12 / MFMA_PEAK_TFLOPS[setup.dtype], 1)
         detail.append(d)
+    if setup.explicit is not None:
+        detail[0]["explicit_dequant_us"] = round(time_callable(setup.explicit) * 1e6, 3)
     cfg = {"workload": name, "format": setup.fmt, "M": list(setup.ms), "N": setup.n,
            "K": setup.k, "weight_copies": len(setup.copies),
            "timing": "hip-graph replay" if use_graph else "eager launches"}
@@ -372,7 +404,11 @@ def kernel_name(setup, m):
     mangled template instance)."""
     if setup.kind == "decode":
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
-    # same rule as the library's dispatch between its two tile kernels
+    # same rules as the library's dispatch
+    if setup.fmt in ("w4a16", "w8a16"):
+        big = m >= 256 and setup.n > 128 and setup.k % 8 == 0
+        name = "pipe256_kernel" if big else "decode_gemm_kernel"
+        return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     k_tiles = -(-setup.k // (256 if setup.fmt == "mxfp4" else 128))
     big = m > 128 and setup.n > 128 and k_tiles >= 2 and (setup.fmt != "mxfp4" or setup.k % 128 == 0)
     name = "pipe256_kernel" if big else "tile_gemm_kernel"

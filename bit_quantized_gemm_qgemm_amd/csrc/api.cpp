@@ -15,6 +15,8 @@ using qgemm::PackGeom;
 using qgemm::pack_geom;
 
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;   // kernels index with 32-bit ints
+// Smallest M for which the weight-only GEMMs take the tiled kernel.
+constexpr int64_t kWeightOnlyTileMinM = 256;
 constexpr int kDecodeMaxM = 16;                   // small-M (bandwidth) path bound
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -82,7 +84,12 @@ int weight_only(int fmt, const void* x, const void* w_packed, const void* scales
     return QGEMM_ERR_ALIGN;
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
-  // every M runs the register-dequant path in 16-row slabs
+  // Large M: LDS-tiled matrix-core kernel (each weight byte is read once per
+  // 256 rows).  Otherwise the register-dequant kernel in 16-row slabs, the
+  // bandwidth path of decode.
+  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0 && K % 8 == 0)
+    return launched(qgemm::launch_weight_only_tile(fmt, x, w_packed, scales, y, M, N, K,
+                                                   as_stream(stream)));
   return launched(qgemm::launch_decode_gemm(fmt, x, w_packed, scales, nullptr, nullptr, y, M, N,
                                             K, as_stream(stream)));
 }

@@ -115,6 +115,12 @@ hipError_t launch_decode_gemm(int fmt, const void* x, const void* w_packed, cons
                               const float* scale_a, const float* scale_b, void* y,
                               int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// LDS-tiled matrix-core path for W4A16 / W8A16 at large M (fp16 X with K a
+// positive multiple of 8; 256 x 256 output tiles).
+hipError_t launch_weight_only_tile(int fmt, const void* x, const void* w_packed,
+                                  const void* scales, void* y, int64_t M, int64_t N, int64_t K,
+                                  hipStream_t stream);
+
 // LDS-tiled matrix-core path for MXFP4 / FP8 (any M).
 hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const void* w_packed,
                             const float* scale_a, const float* scale_b, void* c,

@@ -22,6 +22,7 @@
 // Double-buffered: the global loads of step k+1 are in flight while the
 // matrix cores work on step k; one barrier per step.
 #include "qgemm_common.h"
+#include "qgemm_dequant.h"
 
 namespace qgemm {
 namespace {
@@ -288,7 +289,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBig = 256;
 constexpr int kStepBytes = 64;      // bytes of K per row per step
-constexpr int kStages = 4;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset past every buffer
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
@@ -322,77 +322,85 @@ struct PipeArgs {
   uint32_t a_bytes, w_bytes, asc_bytes, wsc_bytes;
 };
 
-// Stage layout (both formats):
-//   A   [256 rows][64 B]; 16-byte chunk c of row r sits in slot c ^ swizzle(r),
-//       with swizzle(r) = (r >> 1) & 3 for MXFP4 and (r >> 2) & 3 for FP8: the
-//       row bits that keep each format's fragment reads free of bank
-//       conflicts (16 rows x 4 lane groups for MXFP4, 32 rows x 2 for FP8)
-//   W   16 column tiles x 1 KB
-//   MXFP4 only: A scales [256 rows][4 blocks]; W scales [wn 2][lane 64][tile 8]
-template <bool FP4>
-struct PipeCfg {
-  static constexpr int A = kBig * kStepBytes;
-  static constexpr int B = kBig * kStepBytes;
-  static constexpr int SA = FP4 ? kBig * 4 : 0;
-  static constexpr int SB = FP4 ? 2 * 512 : 0;
-  static constexpr int STAGE = A + B + SA + SB;
-  static constexpr int DMA = FP4 ? 10 : 8;        // copies per wave per stage
-};
+// Stage layout, common part: A [256 rows][64 B] at offset 0; the 16-byte
+// chunk c of row r sits in slot c ^ Ops::swizzle(r), the row bits that keep
+// that format's fragment reads free of LDS bank conflicts (checked with the
+// bank-conflict counter: rows 1-2 for 16-row x 4-group reads, rows 2-3 for
+// 32-row x 2-group reads).  The weight part (and the MXFP4 scales) follow.
+constexpr int kStageA = kBig * kStepBytes;
 
-template <bool FP4>
-__device__ __forceinline__ int pipe_swizzle(int r) {
-  return FP4 ? (r >> 1) & 3 : (r >> 2) & 3;
-}
-
-template <bool FP4>
-__device__ __forceinline__ void pipe_issue(uint8_t* st, int ks, int wave, int lane, int m0,
-                                           int cg0, const PipeArgs& g,
-                                           __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rw,
-                                           __amdgpu_buffer_rsrc_t rsa,
-                                           __amdgpu_buffer_rsrc_t rsw) {
-  using C = PipeCfg<FP4>;
-  const int row_bytes = FP4 ? g.K / 2 : g.K;
-  const int kt = ks >> 1, h = ks & 1;
-  // A: 16 slices of 16 rows x 64 B; wave w copies slices 4w .. 4w+3
+// A copies of step ks: 16 slices of 16 rows x 64 B; wave w takes 4w .. 4w+3.
+template <class Ops>
+__device__ __forceinline__ void pipe_issue_a(uint8_t* st, int ks, int wave, int lane, int m0,
+                                             int row_bytes, __amdgpu_buffer_rsrc_t ra) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int q = 4 * wave + j;
     const int r = 16 * q + (lane >> 2);
-    const int c = (lane & 3) ^ pipe_swizzle<FP4>(r);
+    const int c = (lane & 3) ^ Ops::swizzle(r);
     const int kb = ks * kStepBytes + 16 * c;
     const uint32_t off = kb < row_bytes ? (uint32_t)(m0 + r) * (uint32_t)row_bytes + kb
                                         : kOutOfRange;
     dma16(ra, st + q * 1024, off);
   }
-  // W: the 1 KB of column tile t = 4w + j that belongs to this step
+}
+
+// Operand rsrcs of one workgroup.
+struct PipeRsrc {
+  __amdgpu_buffer_rsrc_t a, w, sa, sw;
+};
+
+// Everything an epilogue may need besides the accumulators.
+struct PipeOut {
+  uint16_t* c;
+  const uint16_t* col_scale;   // W4A16 / W8A16: fp16 scale per output column
+  float s;                     // FP8: scale_a * scale_b
+  int M, N;
+};
+
+// A fragment of a 16 x 16 x K matrix step: lane l reads row l & 15, 16-byte
+// chunk l >> 4 of the step's 64 bytes.
+__device__ __forceinline__ int a16_lane_offset(int wm, int lane, int swz) {
+  const int r = wm * 128 + (lane & 15);
+  return r * kStepBytes + 16 * ((lane >> 4) ^ swz);
+}
+
+// 16 x 16 accumulators: lane holds rows 4 (lane >> 4) + i, column lane & 15.
+template <bool F16_OUT>
+__device__ __forceinline__ void store16(const floatx4 (&acc)[8][8], const PipeOut& o, int m0,
+                                        int n0, int wm, int wn, int lane) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = 4 * wave + j;
-    const uint32_t base = ((uint32_t)(cg0 + t) * g.KT + kt) * kTileBytes;
-    // FP4: half h of the tile as is.  FP8: bytes [16h, 16h + 16) of each
-    // lane group pair 2h, 2h + 1, from both 1 KB halves of the tile.
-    const uint32_t off = FP4 ? base + 1024u * h + 16u * lane
-                             : base + 1024u * (lane >> 5) + 512u * h + 16u * (lane & 31);
-    dma16(rw, st + C::A + t * 1024, off);
-  }
-  if constexpr (FP4) {
-    const int sc_cols = g.K / 32;   // K % 128 == 0: four blocks per row are one dword
-    const int r = 64 * wave + lane;
-    const int blk = 4 * ks;
-    const uint32_t off = blk < sc_cols ? (uint32_t)(m0 + r) * (uint32_t)sc_cols + blk
-                                       : kOutOfRange;
-    dma4(rsa, st + C::A + C::B + 256 * wave, off);
-    const uint32_t soff = ((uint32_t)(cg0 / 8 + (wave >> 1)) * g.KS + ks) * 512u +
-                          256u * (wave & 1) + 4u * lane;
-    dma4(rsw, st + C::A + C::B + C::SA + 256 * wave, soff);
+  for (int fn = 0; fn < 8; ++fn) {
+    const int gn = n0 + wn * 128 + fn * 16 + (lane & 15);
+    float s = o.s;
+    if constexpr (F16_OUT) {
+      const int sn = gn < o.N ? gn : o.N - 1;
+      s = (float)__builtin_bit_cast(_Float16, o.col_scale[sn]);
+    }
+#pragma unroll
+    for (int fm = 0; fm < 8; ++fm)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gm = m0 + wm * 128 + fm * 16 + 4 * (lane >> 4) + i;
+        if (gm < o.M && gn < o.N)
+          o.c[(int64_t)gm * o.N + gn] =
+              F16_OUT ? f32_to_f16_bits(acc[fm][fn][i] * s) : f32_to_bf16_rne(acc[fm][fn][i] * s);
+      }
   }
 }
 
 // MXFP4: 8 x 8 fragments of 16 x 16 per wave; one step = 128 K elements =
 // one v_mfma_scale_f32_16x16x128_f8f6f4 per fragment pair.
+// Stage: A | W 16 tiles x 1 KB (half h of each tile as is) | A scales
+// [256 rows][4 blocks] | W scales [wn 2][lane 64][tile 8].
 struct Fp4Pipe {
-  static constexpr bool FP4 = true;
+  static constexpr int FMT = 3;
   static constexpr int PARTS = 8;
+  static constexpr int STEPS_PER_TILE = 2;
+  static constexpr int B = 16 * 1024, SA = kBig * 4, SB = 2 * 512;
+  static constexpr int STAGE = kStageA + B + SA + SB;
+  static constexpr int DMA = 10;
+  static constexpr int NST = 4;                  // 4 x 34 KB of LDS
   typedef floatx4 Acc[8][8];
   struct Frags {
     uintx4 a[8];
@@ -403,14 +411,35 @@ struct Fp4Pipe {
   struct Lane {
     int a, sa, b, sb;
   };
+  __device__ __forceinline__ static int swizzle(int r) { return (r >> 1) & 3; }
+  __device__ __forceinline__ static int row_bytes(int K) { return K / 2; }
+  __device__ __forceinline__ static void issue_rest(uint8_t* st, int ks, int wave, int lane,
+                                                    int m0, int cg0, const PipeArgs& g,
+                                                    const PipeRsrc& rs) {
+    const int kt = ks >> 1, h = ks & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * wave + j;
+      const uint32_t off = ((uint32_t)(cg0 + t) * g.KT + kt) * kTileBytes + 1024u * h + 16u * lane;
+      dma16(rs.w, st + kStageA + t * 1024, off);
+    }
+    const int sc_cols = g.K / 32;   // K % 128 == 0: four blocks per row are one dword
+    const int r = 64 * wave + lane;
+    const int blk = 4 * ks;
+    const uint32_t off = blk < sc_cols ? (uint32_t)(m0 + r) * (uint32_t)sc_cols + blk
+                                       : kOutOfRange;
+    dma4(rs.sa, st + kStageA + B + 256 * wave, off);
+    const uint32_t soff = ((uint32_t)(cg0 / 8 + (wave >> 1)) * g.KS + ks) * 512u +
+                          256u * (wave & 1) + 4u * lane;
+    dma4(rs.sw, st + kStageA + B + SA + 256 * wave, soff);
+  }
   __device__ __forceinline__ static Lane lane_offsets(int wm, int wn, int lane) {
-    using C = PipeCfg<true>;
-    const int r = wm * 128 + (lane & 15), grp = lane >> 4;
+    const int r = wm * 128 + (lane & 15);
     Lane L;
-    L.a = r * kStepBytes + 16 * (grp ^ pipe_swizzle<true>(r));
-    L.sa = C::A + C::B + r * 4 + grp;
-    L.b = C::A + wn * 8 * 1024 + 16 * lane;
-    L.sb = C::A + C::B + C::SA + wn * 512 + 8 * lane;
+    L.a = a16_lane_offset(wm, lane, swizzle(r));
+    L.sa = kStageA + B + r * 4 + (lane >> 4);
+    L.b = kStageA + wn * 8 * 1024 + 16 * lane;
+    L.sb = kStageA + B + SA + wn * 512 + 8 * lane;
     return L;
   }
   template <int P>
@@ -422,7 +451,7 @@ struct Fp4Pipe {
   }
   // column fragment P against all 8 row fragments
   template <int P>
-  __device__ __forceinline__ static void mma(const Frags& F, Acc& acc) {
+  __device__ __forceinline__ static void mma(const Frags& F, const Lane&, Acc& acc) {
     const intx8 bf = {(int)F.b[P][0], (int)F.b[P][1], (int)F.b[P][2], (int)F.b[P][3], 0, 0, 0, 0};
     const int sb = (int)F.sb[P >> 2];
 #pragma unroll
@@ -440,20 +469,9 @@ struct Fp4Pipe {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  // lane holds rows 4 (lane >> 4) + i, column lane & 15 of each fragment
-  __device__ __forceinline__ static void store(const Acc& acc, uint16_t* __restrict__ c, int m0, int n0, int wm,
-                               int wn, int lane, int M, int N, float s) {
-#pragma unroll
-    for (int fm = 0; fm < 8; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < 8; ++fn) {
-        const int gn = n0 + wn * 128 + fn * 16 + (lane & 15);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int gm = m0 + wm * 128 + fm * 16 + 4 * (lane >> 4) + i;
-          if (gm < M && gn < N) c[(int64_t)gm * N + gn] = f32_to_bf16_rne(acc[fm][fn][i] * s);
-        }
-      }
+  __device__ __forceinline__ static void store(const Acc& acc, const PipeOut& o, int m0, int n0,
+                                               int wm, int wn, int lane) {
+    store16<false>(acc, o, m0, n0, wm, wn, lane);
   }
 };
 
@@ -461,9 +479,16 @@ struct Fp4Pipe {
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) per fragment pair.
 // Lane l feeds row (or column) l & 31 with K elements 32 (l >> 5) + [0, 32)
 // of the step, the same K order on both sides.
+// Stage: A | W 16 tiles x 1 KB: bytes [16h, 16h + 16) of the lane group pair
+// 2s, 2s + 1 (s = step within the tile) from both 1 KB halves h.
 struct Fp8Pipe {
-  static constexpr bool FP4 = false;
+  static constexpr int FMT = 4;
   static constexpr int PARTS = 4;
+  static constexpr int STEPS_PER_TILE = 2;
+  static constexpr int B = 16 * 1024;
+  static constexpr int STAGE = kStageA + B;
+  static constexpr int DMA = 8;
+  static constexpr int NST = 4;                  // 4 x 32 KB
   typedef floatx16 Acc[4][4];
   struct Frags {
     uintx4 alo[4], ahi[4];
@@ -472,14 +497,27 @@ struct Fp8Pipe {
   struct Lane {
     int alo, ahi, b;
   };
+  __device__ __forceinline__ static int swizzle(int r) { return (r >> 2) & 3; }
+  __device__ __forceinline__ static int row_bytes(int K) { return K; }
+  __device__ __forceinline__ static void issue_rest(uint8_t* st, int ks, int wave, int lane,
+                                                    int, int cg0, const PipeArgs& g,
+                                                    const PipeRsrc& rs) {
+    const int kt = ks >> 1, h = ks & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * wave + j;
+      const uint32_t off = ((uint32_t)(cg0 + t) * g.KT + kt) * kTileBytes +
+                           1024u * (lane >> 5) + 512u * h + 16u * (lane & 31);
+      dma16(rs.w, st + kStageA + t * 1024, off);
+    }
+  }
   __device__ __forceinline__ static Lane lane_offsets(int wm, int wn, int lane) {
-    using C = PipeCfg<false>;
-    const int r = wm * 128 + (lane & 31), hh = lane >> 5, swz = pipe_swizzle<false>(r);
+    const int r = wm * 128 + (lane & 31), hh = lane >> 5, swz = swizzle(r);
     Lane L;
     L.alo = r * kStepBytes + 16 * ((2 * hh) ^ swz);
     L.ahi = r * kStepBytes + 16 * ((2 * hh + 1) ^ swz);
     // column tile wn*8 + 2P + ((lane >> 4) & 1); lane group pair half hh
-    L.b = C::A + (wn * 8 + ((lane >> 4) & 1)) * 1024 + 256 * hh + 16 * (lane & 15);
+    L.b = kStageA + (wn * 8 + ((lane >> 4) & 1)) * 1024 + 256 * hh + 16 * (lane & 15);
     return L;
   }
   template <int P>
@@ -490,7 +528,7 @@ struct Fp8Pipe {
     F.bhi[P] = *reinterpret_cast<const uintx4*>(st + L.b + P * 2048 + 512);
   }
   template <int P>
-  __device__ __forceinline__ static void mma(const Frags& F, Acc& acc) {
+  __device__ __forceinline__ static void mma(const Frags& F, const Lane&, Acc& acc) {
     const intx8 bf = {(int)F.blo[P][0], (int)F.blo[P][1], (int)F.blo[P][2], (int)F.blo[P][3],
                       (int)F.bhi[P][0], (int)F.bhi[P][1], (int)F.bhi[P][2], (int)F.bhi[P][3]};
 #pragma unroll
@@ -511,8 +549,8 @@ struct Fp8Pipe {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   }
   // lane holds rows 8 (e >> 2) + 4 (lane >> 5) + (e & 3), column lane & 31
-  __device__ __forceinline__ static void store(const Acc& acc, uint16_t* __restrict__ c, int m0, int n0, int wm,
-                               int wn, int lane, int M, int N, float s) {
+  __device__ __forceinline__ static void store(const Acc& acc, const PipeOut& o, int m0, int n0,
+                                               int wm, int wn, int lane) {
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
@@ -521,9 +559,95 @@ struct Fp8Pipe {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int gm = m0 + wm * 128 + fm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          if (gm < M && gn < N) c[(int64_t)gm * N + gn] = f32_to_bf16_rne(acc[fm][fn][e] * s);
+          if (gm < o.M && gn < o.N)
+            o.c[(int64_t)gm * o.N + gn] = f32_to_bf16_rne(acc[fm][fn][e] * o.s);
         }
       }
+  }
+};
+
+// W4A16 / W8A16 with fp16 X: 8 x 8 fragments of 16 x 16 per wave; one step =
+// 32 K elements = one v_mfma_f32_16x16x32_f16 per fragment pair.  The step's
+// weight bytes of a lane (the word of matrix step s = ks % 4 of its packed
+// 128-wide tile: 4 bytes for W4, 8 for W8) are gathered into LDS with 4-byte
+// copies, read back as one or two words and dequantized in registers right
+// before the matrix instructions that use them (W4A16 page section 2, W8A16
+// page Steps 1-2: the dequantized weight never leaves the registers).  The
+// per-column scale multiplies the fp32 sum in the epilogue.
+// Stage: A (fp16 X) | W: [tile 16][part WV][lane 64][4 B].
+template <int WFMT>
+struct F16Pipe {
+  static constexpr int FMT = WFMT;
+  static constexpr int WV = WFMT == 1 ? 1 : 2;        // weight words per lane per step
+  static constexpr int PARTS = 8;
+  static constexpr int STEPS_PER_TILE = 4;
+  static constexpr int B = 16 * WV * 256;
+  static constexpr int STAGE = kStageA + B;
+  static constexpr int DMA = 4 + 4 * WV;
+  static constexpr int NST = WFMT == 1 ? 8 : 6;  // 8 x 20 KB or 6 x 24 KB
+  typedef floatx4 Acc[8][8];
+  struct Frags {
+    uintx4 a[8];
+    half8_t b[8];   // dequantized right after the LDS read
+  };
+  struct Lane {
+    int a, b;
+  };
+  __device__ __forceinline__ static int swizzle(int r) { return (r >> 1) & 3; }
+  __device__ __forceinline__ static int row_bytes(int K) { return 2 * K; }
+  __device__ __forceinline__ static void issue_rest(uint8_t* st, int ks, int wave, int lane,
+                                                    int, int cg0, const PipeArgs& g,
+                                                    const PipeRsrc& rs) {
+    const int kt = ks >> 2, s = ks & 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * wave + j;
+#pragma unroll
+      for (int p = 0; p < WV; ++p) {
+        // W4: word s of the lane's 16 bytes.  W8: bytes 8 (s & 1) + 4p of
+        // the lane's 16 bytes in half s >> 1.
+        const uint32_t off = WFMT == 1
+            ? ((uint32_t)(cg0 + t) * g.KT + kt) * kTileBytesW4 + 16u * lane + 4u * s
+            : ((uint32_t)(cg0 + t) * g.KT + kt) * kTileBytes + 1024u * (s >> 1) + 16u * lane +
+                  8u * (s & 1) + 4u * p;
+        dma4(rs.w, st + kStageA + (t * WV + p) * 256, off);
+      }
+    }
+  }
+  __device__ __forceinline__ static Lane lane_offsets(int wm, int wn, int lane) {
+    const int r = wm * 128 + (lane & 15);
+    Lane L;
+    L.a = a16_lane_offset(wm, lane, swizzle(r));
+    L.b = kStageA + wn * 8 * WV * 256 + 4 * lane;
+    return L;
+  }
+  template <int P>
+  __device__ __forceinline__ static void read(Frags& F, const uint8_t* st, const Lane& L) {
+    F.a[P] = *reinterpret_cast<const uintx4*>(st + L.a + P * 1024);
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(st + L.b + P * WV * 256);
+    if constexpr (WFMT == 1) {
+      F.b[P] = dequant_w4_shift(w0);
+    } else {
+      const uint32_t w1 = *reinterpret_cast<const uint32_t*>(st + L.b + (P * WV + 1) * 256);
+      F.b[P] = dequant_w8(w0, w1);
+    }
+  }
+  template <int P>
+  __device__ __forceinline__ static void mma(const Frags& F, const Lane&, Acc& acc) {
+#pragma unroll
+    for (int fm = 0; fm < 8; ++fm)
+      acc[fm][P] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, F.a[fm]),
+                                                          F.b[P], acc[fm][P], 0, 0, 0);
+  }
+  __device__ __forceinline__ static void zero(Acc& acc) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ static void store(const Acc& acc, const PipeOut& o, int m0, int n0,
+                                               int wm, int wn, int lane) {
+    store16<true>(acc, o, m0, n0, wm, wn, lane);
   }
 };
 
@@ -534,7 +658,7 @@ __device__ __forceinline__ void pipe_part(typename Ops::Frags& cur, typename Ops
                                           const uint8_t* nx, const typename Ops::Lane& L,
                                           typename Ops::Acc& acc) {
   if (RD) Ops::template read<P>(nxt, nx, L);
-  Ops::template mma<P>(cur, acc);
+  Ops::template mma<P>(cur, L, acc);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -569,17 +693,35 @@ __device__ __forceinline__ void pipe_read_all(typename Ops::Frags& F, const uint
   }
 }
 
-// Requires KS even and >= 4 (checked on the host).
-template <class Ops>
+// Last steps of the pipeline, J = 0 .. NST-1 of them, unrolled: step J
+// computes one register set and reads the other (except the very last), and
+// waits until the copies of step J+2 have landed while those still issued
+// after it stay in flight.
+template <class Ops, int NST, int PER, int J>
+__device__ __forceinline__ void pipe_tail(typename Ops::Frags& F0, typename Ops::Frags& F1,
+                                          uint8_t* smem, int ks, const typename Ops::Lane& L,
+                                          typename Ops::Acc& acc) {
+  if constexpr (J < NST) {
+    constexpr bool RD = J + 1 < NST;
+    const uint8_t* nx = smem + ((ks + J + 1) % NST) * Ops::STAGE;
+    if constexpr (J % 2 == 0) pipe_step<Ops, RD>(F0, F1, nx, L, acc);
+    else pipe_step<Ops, RD>(F1, F0, nx, L, acc);
+    if constexpr (J + 3 <= NST) QG_WAIT_VM_BARRIER((NST - 3 - J) * PER);
+    pipe_tail<Ops, NST, PER, J + 1>(F0, F1, smem, ks, L, acc);
+  }
+}
+
+// NST LDS stages (even, >= 4); requires KS even and >= NST (checked on the
+// host).
+template <class Ops, int NST>
 __global__ __launch_bounds__(kThreads) void pipe256_kernel(
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_sc,
     const uint8_t* __restrict__ wp, const uint8_t* __restrict__ w_sc,
     const float* __restrict__ scale_a, const float* __restrict__ scale_b,
-    uint16_t* __restrict__ c, PipeArgs g) {
-  constexpr bool FP4 = Ops::FP4;
-  using C = PipeCfg<FP4>;
-  constexpr int PER = C::DMA;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * C::STAGE];
+    const uint16_t* __restrict__ col_scale, uint16_t* __restrict__ c, PipeArgs g) {
+  constexpr int PER = Ops::DMA;
+  static_assert(NST % 2 == 0 && NST >= 4, "stage ring");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * Ops::STAGE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1;
@@ -602,74 +744,95 @@ __global__ __launch_bounds__(kThreads) void pipe256_kernel(
   const int m0 = tm * kBig;
   const int cg0 = tn * (kBig / 16);
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a, g.a_bytes);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wp, g.w_bytes);
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(FP4 ? a_sc : a, FP4 ? g.asc_bytes : 0u);
-  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(FP4 ? w_sc : wp, FP4 ? g.wsc_bytes : 0u);
+  PipeRsrc rs;
+  rs.a = make_rsrc(a, g.a_bytes);
+  rs.w = make_rsrc(wp, g.w_bytes);
+  rs.sa = make_rsrc(g.asc_bytes ? a_sc : a, g.asc_bytes);
+  rs.sw = make_rsrc(g.wsc_bytes ? w_sc : wp, g.wsc_bytes);
+  const int row_bytes = Ops::row_bytes(g.K);
   const typename Ops::Lane L = Ops::lane_offsets(wm, wn, lane);
 
   typename Ops::Acc acc;
   Ops::zero(acc);
   const int KS = g.KS;
-  auto stage = [&](int s) { return smem + (s & (kStages - 1)) * C::STAGE; };
-  auto issue = [&](int s) { pipe_issue<FP4>(stage(s), s, wave, lane, m0, cg0, g, ra, rw, rsa, rsw); };
+  auto stage = [&](int s) { return smem + (s % NST) * Ops::STAGE; };
+  auto issue = [&](int s) {
+    uint8_t* st = stage(s);
+    pipe_issue_a<Ops>(st, s, wave, lane, m0, row_bytes, rs.a);
+    Ops::issue_rest(st, s, wave, lane, m0, cg0, g, rs);
+  };
 
-  issue(0);
-  issue(1);
-  issue(2);
-  QG_WAIT_VM_BARRIER(PER);   // steps 0 and 1 landed; 2 may be in flight
+  // Step s lives in stage s % NST; the copies of step s are issued NST - 1
+  // steps ahead, into the stage whose fragments were consumed one step ago.
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue(s);
+  QG_WAIT_VM_BARRIER((NST - 3) * PER);   // steps 0 and 1 landed
   typename Ops::Frags F0, F1;
   pipe_read_all<Ops>(F0, stage(0), L);
 
-  // Two steps per iteration, F0 and F1 trading roles.  Every copy issued in
-  // here is in range (ks + 4 < KS).
+  // Two steps per iteration, F0 and F1 trading roles; every copy issued in
+  // here is in range (ks + NST < KS).  At the end of step ks the copies of
+  // step ks+2 must have landed (its fragments are read during step ks+1).
   int ks = 0;
-  for (; ks + 4 < KS; ks += 2) {
-    issue(ks + 3);
+  for (; ks + NST < KS; ks += 2) {
+    issue(ks + NST - 1);
     pipe_step<Ops, true>(F0, F1, stage(ks + 1), L, acc);
-    QG_WAIT_VM_BARRIER(PER);   // step ks+2 landed
-    issue(ks + 4);
+    QG_WAIT_VM_BARRIER((NST - 3) * PER);
+    issue(ks + NST);
     pipe_step<Ops, true>(F1, F0, stage(ks + 2), L, acc);
-    QG_WAIT_VM_BARRIER(PER);   // step ks+3 landed
+    QG_WAIT_VM_BARRIER((NST - 3) * PER);
   }
-  // last four steps: ks == KS - 4, copies issued up to step KS - 2
-  issue(ks + 3);
-  pipe_step<Ops, true>(F0, F1, stage(ks + 1), L, acc);
-  QG_WAIT_VM_BARRIER(PER);
-  pipe_step<Ops, true>(F1, F0, stage(ks + 2), L, acc);
-  QG_WAIT_VM_BARRIER(0);
-  pipe_step<Ops, true>(F0, F1, stage(ks + 3), L, acc);
-  pipe_step<Ops, false>(F1, F0, stage(ks + 3), L, acc);
+  // last NST steps (ks == KS - NST), copies issued up to step KS - 2
+  issue(ks + NST - 1);
+  pipe_tail<Ops, NST, PER, 0>(F0, F1, smem, ks, L, acc);
 
-  const float s = FP4 ? 1.0f : (*scale_a) * (*scale_b);
-  Ops::store(acc, c, m0, cg0 * 16, wm, wn, lane, g.M, g.N, s);
+  PipeOut o;
+  o.c = c;
+  o.col_scale = col_scale;
+  o.s = (Ops::FMT == 4) ? (*scale_a) * (*scale_b) : 1.0f;
+  o.M = g.M;
+  o.N = g.N;
+  Ops::store(acc, o, m0, cg0 * 16, wm, wn, lane);
+}
+
+// a_sc: MXFP4 activation scales; col_scale: W4A16/W8A16 column scales;
+// sa, sb: FP8 per-tensor scales (unused arguments may be null).
+template <class Ops, int NST>
+hipError_t launch_pipe_nst(const PipeArgs& g, const void* a, const void* a_sc, const void* wp,
+                           const uint8_t* w_sc, const float* sa, const float* sb,
+                           const void* col_scale, void* c, hipStream_t stream) {
+  hipLaunchKernelGGL((pipe256_kernel<Ops, NST>), dim3((unsigned)(g.tiles_m * g.tiles_n)),
+                     dim3(kThreads), 0, stream, static_cast<const uint8_t*>(a),
+                     static_cast<const uint8_t*>(a_sc), static_cast<const uint8_t*>(wp), w_sc,
+                     sa, sb, static_cast<const uint16_t*>(col_scale), static_cast<uint16_t*>(c), g);
+  return hipGetLastError();
 }
 
 template <class Ops>
 hipError_t launch_pipe(const void* a, const void* a_sc, const void* wp, const float* sa,
-                       const float* sb, void* c, int64_t M, int64_t N, int64_t K,
-                       hipStream_t stream) {
-  constexpr bool FP4 = Ops::FP4;
-  const PackGeom pg = pack_geom(FP4 ? 3 : 4, K, N);
+                       const float* sb, const void* col_scale, void* c, int64_t M, int64_t N,
+                       int64_t K, hipStream_t stream) {
+  constexpr int FMT = Ops::FMT;
+  const PackGeom pg = pack_geom(FMT, K, N);
   PipeArgs g;
   g.M = (int)M;
   g.N = (int)N;
   g.K = (int)K;
   g.KT = (int)pg.kt;
-  g.KS = 2 * (int)pg.kt;
+  g.KS = Ops::STEPS_PER_TILE * (int)pg.kt;
   g.CG = (int)pg.cg;
   g.tiles_m = (int)cdiv(M, kBig);
   g.tiles_n = (int)cdiv(N, kBig);
-  g.a_bytes = (uint32_t)(M * (FP4 ? K / 2 : K));
+  const int64_t a_row = FMT == 3 ? K / 2 : FMT == 4 ? K : 2 * K;
+  g.a_bytes = (uint32_t)(M * a_row);
   g.w_bytes = (uint32_t)pg.codes;
-  g.asc_bytes = FP4 ? (uint32_t)(M * (K / 32)) : 0u;
-  g.wsc_bytes = FP4 ? (uint32_t)(pg.total - pg.scales) : 0u;
-  const uint8_t* w_sc = FP4 ? static_cast<const uint8_t*>(wp) + pg.scales : nullptr;
-  hipLaunchKernelGGL((pipe256_kernel<Ops>), dim3((unsigned)(g.tiles_m * g.tiles_n)),
-                     dim3(kThreads), 0, stream, static_cast<const uint8_t*>(a),
-                     static_cast<const uint8_t*>(a_sc), static_cast<const uint8_t*>(wp), w_sc,
-                     sa, sb, static_cast<uint16_t*>(c), g);
-  return hipGetLastError();
+  g.asc_bytes = FMT == 3 ? (uint32_t)(M * (K / 32)) : 0u;
+  g.wsc_bytes = FMT == 3 ? (uint32_t)(pg.total - pg.scales) : 0u;
+  const uint8_t* w_sc = FMT == 3 ? static_cast<const uint8_t*>(wp) + pg.scales : nullptr;
+  // the deepest ring that fits in LDS, when K has at least that many steps
+  if (Ops::NST > 4 && g.KS >= Ops::NST)
+    return launch_pipe_nst<Ops, Ops::NST>(g, a, a_sc, wp, w_sc, sa, sb, col_scale, c, stream);
+  return launch_pipe_nst<Ops, 4>(g, a, a_sc, wp, w_sc, sa, sb, col_scale, c, stream);
 }
 
 template <bool FP4, int FM, int FN>
@@ -691,6 +854,18 @@ hipError_t launch_tiles(const void* a, const void* a_sc, const void* wp, const f
 
 }  // namespace
 
+hipError_t launch_weight_only_tile(int fmt, const void* x, const void* w_packed,
+                                  const void* scales, void* y, int64_t M, int64_t N, int64_t K,
+                                  hipStream_t stream) {
+  if (fmt == 1)
+    return launch_pipe<F16Pipe<1>>(x, nullptr, w_packed, nullptr, nullptr, scales, y, M, N, K,
+                                   stream);
+  if (fmt == 2)
+    return launch_pipe<F16Pipe<2>>(x, nullptr, w_packed, nullptr, nullptr, scales, y, M, N, K,
+                                   stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const void* w_packed,
                             const float* scale_a, const float* scale_b, void* c, int64_t M,
                             int64_t N, int64_t K, hipStream_t stream) {
@@ -701,11 +876,14 @@ hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const vo
   const bool big = M > 128 && N > 128 && cdiv(K, kTileK8) >= 2;
   if (fmt == 3) {
     if (big && K % 128 == 0 && cdiv(K, kTileK4) >= 2)
-      return launch_pipe<Fp4Pipe>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
+      return launch_pipe<Fp4Pipe>(a, a_e8m0, w_packed, scale_a, scale_b, nullptr, c, M, N, K,
+                                  stream);
     return launch_tiles<true, 4, 4>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
   }
   if (fmt == 4) {
-    if (big) return launch_pipe<Fp8Pipe>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
+    if (big)
+      return launch_pipe<Fp8Pipe>(a, a_e8m0, w_packed, scale_a, scale_b, nullptr, c, M, N, K,
+                                  stream);
     return launch_tiles<false, 4, 4>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
   }
   return hipErrorInvalidValue;

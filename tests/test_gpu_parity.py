@@ -72,6 +72,10 @@ W4_CASES = [
     (8, 2048, 700),
     (16, 256, 16400),   # eight column groups per workgroup, ragged last workgroup
     (6, 384, 9000),     # four groups per workgroup (M in 5..8)
+    (256, 1024, 272),   # M >= 256: 256 x 256 matrix-core tiles, ragged N
+    (300, 1000, 520),   # ragged M, K tail inside the last 128-wide tile
+    (513, 136, 384),    # three row tiles, eight 32-wide K steps
+    (260, 100, 300),    # K % 8 != 0 at large M: 16-row slabs instead
 ]
 
 
@@ -129,6 +133,10 @@ W8_CASES = [
     (2, 64, 1),
     (9, 200, 9000),     # four groups, three tiles in flight, short K, ragged N
     (16, 520, 2100),
+    (256, 2048, 300),   # M >= 256: 256 x 256 matrix-core tiles
+    (300, 1000, 520),   # ragged M, N and K
+    (260, 64, 1000),    # one K tile: the four-step pipeline tail only
+    (257, 333, 200),    # K % 8 != 0 at large M: 16-row slabs instead
 ]
 
 
@@ -180,6 +188,47 @@ def test_w8a16_decode_full_size_sampled(m):
     cols = np.unique(np.concatenate([np.random.default_rng(m).integers(0, n, 128), [0, n - 1]]))
     y_ref, bound = oracle.gemm_w8a16(x, w[:, cols], s[cols])
     assert_within(y[:, cols], y_ref, bound, f"w8a16 full M={m}")
+
+
+@pytest.mark.parametrize("fmt", ["w4a16", "w8a16"])
+def test_weight_only_one_hot_through_large_tiles(fmt):
+    """X = the identity (M = K = 512 rows, the 256 x 256 tile path):
+    Y = fp16(W_deq) exactly, every weight of every tile and K step."""
+    k, n = 512, 272
+    case_id(f"{fmt} one-hot large tiles", k, n)
+    rng = np.random.default_rng(11)
+    s = (rng.uniform(0.002, 0.02, n) * np.where(np.arange(n) % 3 == 0, -1, 1)).astype(np.float16)
+    if fmt == "w4a16":
+        w = rng.integers(0, 256, size=(k // 2, n)).astype(np.uint8)
+        wdeq = oracle.round_fp16(oracle.dequant_w4(w, s))
+        fn = qg.qgemm_w4a16
+    else:
+        w = ((np.arange(k)[:, None] + 37 * np.arange(n)[None, :]) % 256 - 128).astype(np.int8)
+        wdeq = oracle.round_fp16(oracle.dequant_w8(w, s))
+        fn = qg.qgemm_w8a16
+    wp = qg.qgemm_prepack(fmt, dev(w), k, n)
+    x = np.eye(k, dtype=np.float16)
+    y = host(fn(dev(x), wp, dev(s), n))
+    assert np.array_equal(y, wdeq)
+
+
+@pytest.mark.parametrize("fmt", ["w4a16", "w8a16"])
+def test_weight_only_square_full_size_sampled(fmt):
+    """M = N = K = 4096 (the W8A16 page's fused-versus-explicit comparison
+    shape) on sampled rows and columns."""
+    m = k = n = 4096
+    case_id(f"{fmt} square full", m, k, n)
+    gen = wl.w4a16 if fmt == "w4a16" else wl.w8a16
+    x, w, s = gen(m, k, n)
+    wp = qg.qgemm_prepack(fmt, dev(w), k, n)
+    fn = qg.qgemm_w4a16 if fmt == "w4a16" else qg.qgemm_w8a16
+    y = host(fn(dev(x), wp, dev(s), n))
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.integers(0, m, 48), [0, m - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(0, n, 48), [0, n - 1]]))
+    gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16
+    y_ref, bound = gemm(x[rows], w[:, cols], s[cols])
+    assert_within(y[np.ix_(rows, cols)], y_ref, bound, f"{fmt} square sampled")
 
 
 def test_weight_only_empty_and_zero_k():
