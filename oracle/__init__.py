@@ -17,6 +17,9 @@ Sources (the web pages these functions restate; short names used below):
 * "FP8 page"    -- FP8 GEMM kernel in Triton via CUTLASS naming
   (blog.hotdry.top, 2025/10/03), kernel example and parameter list.
 
+Group-wise scales and zero points (grouped.py) follow the W4A16 page's
+section 1 dequant form and the W8A16 page's extensions.
+
 Parity status of each function is stated in its module.  Parity unpinned:
 the FP8 per-tensor scale formula (the FP8 page fixes only the 448 range and
 per-tensor scaling; GEMM parity is taken against the quantized operands, so
@@ -37,6 +40,13 @@ from .formats import (
     round_bf16,
 )
 from .quantize import mxfp4_quantize, mxfp4_dequant, fp8_quantize
+from .grouped import (
+    expand_groups,
+    dequant_w4_grouped,
+    dequant_w8_grouped,
+    gemm_w4a16_grouped,
+    gemm_w8a16_grouped,
+)
 from .gemm import (
     dequant_w4,
     dequant_w8,
@@ -71,4 +81,9 @@ __all__ = [
     "gemm_fp8",
     "tolerance",
     "within_tolerance",
+    "expand_groups",
+    "dequant_w4_grouped",
+    "dequant_w8_grouped",
+    "gemm_w4a16_grouped",
+    "gemm_w8a16_grouped",
 ]

@@ -75,6 +75,36 @@ def w8a16(m, k, n, seed=SEED):
     return x, w, scales
 
 
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def w4a16_grouped(m, k, n, group_k, group_n=1, zeros=True, seed=SEED):
+    """(x fp16 [m,k], packed uint8 [k/2,n], scales fp16 [ceil(k/gk), ceil(n/gn)],
+    zero points uint8 0..15 of the same shape, or None)."""
+    if k % 2:
+        raise ValueError("K must be even for two codes per byte")
+    rng = np.random.default_rng(seed)
+    x = _normal_f16(rng, (m, k))
+    packed = rng.integers(0, 256, size=(k // 2, n), dtype=np.uint8)
+    shape = (_cdiv(k, group_k), _cdiv(n, group_n))
+    scales = rng.uniform(0.005, 0.02, size=shape).astype(np.float16)
+    z = rng.integers(0, 16, size=shape, dtype=np.uint8) if zeros else None
+    return x, packed, scales, z
+
+
+def w8a16_grouped(m, k, n, group_k, group_n=1, zeros=True, seed=SEED):
+    """(x fp16 [m,k], w int8 [k,n] in -127..127, scales fp16 [ceil(k/gk),
+    ceil(n/gn)], zero points int8 -32..32 of the same shape, or None)."""
+    rng = np.random.default_rng(seed)
+    x = _normal_f16(rng, (m, k))
+    w = rng.integers(-127, 128, size=(k, n), dtype=np.int8)
+    shape = (_cdiv(k, group_k), _cdiv(n, group_n))
+    scales = rng.uniform(0.002, 0.01, size=shape).astype(np.float16)
+    z = rng.integers(-32, 33, size=shape, dtype=np.int8) if zeros else None
+    return x, w, scales, z
+
+
 def w8a16_page_test(m=32, k=128, n=256, seed=SEED):
     """The W8A16 page's test distribution: w in -128..126, scales N(0,1)*0.01."""
     rng = np.random.default_rng(seed)
