@@ -55,7 +55,11 @@ WORKLOADS = {
     # the W8A16 page's fused-versus-explicit-dequant comparison shape
     "w8a16_square": ("w8a16", (4096,), 4096, 4096),
     "w4a16_square": ("w4a16", (4096,), 4096, 4096),
+    # group-wise scales along K (128) with zero points, at the decode shapes
+    "w4a16_g128_decode": ("w4a16_grouped", (1, 8, 16), 28672, 8192),
+    "w8a16_g128_decode": ("w8a16_grouped", (1, 4, 16), 11008, 4096),
 }
+GROUP_K = 128   # group size of the grouped workloads
 DEFAULT_WORKLOAD = "w8a16_decode"
 
 
@@ -110,6 +114,27 @@ class Setup:
                 out = torch.empty((m, n), dtype=torch.float16, device=dev)
                 alg = w_bytes + 2 * m * k + 2 * m * n
                 self.calls.append((lambda c, xm=xm, out=out: fn(xm, self.copies[c], s_d, n, out=out),
+                                   alg, w_bytes, 2 * m * n * k))
+        elif fmt in ("w4a16_grouped", "w8a16_grouped"):
+            w4 = fmt == "w4a16_grouped"
+            gen = wl.w4a16_grouped if w4 else wl.w8a16_grouped
+            x, w, s, z = gen(mmax, k, n, GROUP_K)
+            packed = qg.qgemm_prepack_grouped(fmt, torch.from_numpy(w).to(dev), k, n,
+                                              torch.from_numpy(s).to(dev),
+                                              torch.from_numpy(z).to(dev), GROUP_K)
+            x_d = torch.from_numpy(x).to(dev)
+            # codes + the canonical fp16 scale and 1-byte zero point per group
+            groups = -(-k // GROUP_K) * n
+            w_bytes = (k * n // 2 if w4 else k * n) + 3 * groups
+            self.copies = self._rotate(packed, w_bytes)
+            fn = qg.qgemm_w4a16_grouped if w4 else qg.qgemm_w8a16_grouped
+            self.dtype = "f16"
+            for m in ms:
+                xm = x_d[:m].contiguous()
+                out = torch.empty((m, n), dtype=torch.float16, device=dev)
+                alg = w_bytes + 2 * m * k + 2 * m * n
+                self.calls.append((lambda c, xm=xm, out=out: fn(xm, self.copies[c], n, GROUP_K,
+                                                                out=out),
                                    alg, w_bytes, 2 * m * n * k))
         elif fmt == "mxfp4":
             a, w = wl.mxfp4_operands(mmax, n, k)
@@ -262,15 +287,25 @@ def cpu_baseline(name, budget_s=10.0):
 
     fmt, ms, n, k = WORKLOADS[name]
     mmax = max(ms)
-    if fmt in ("w4a16", "w8a16") and mmax <= 16:
-        gen = wl.w4a16 if fmt == "w4a16" else wl.w8a16
-        gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16
-        # bounded sample: the full K and a column slice sized for ~1 s per step
+    if fmt in ("w4a16_grouped", "w8a16_grouped"):
+        w4 = fmt == "w4a16_grouped"
+        gen = wl.w4a16_grouped if w4 else wl.w8a16_grouped
+        ggemm = oracle.gemm_w4a16_grouped if w4 else oracle.gemm_w8a16_grouped
         cols = n if k * n <= 50_000_000 else max(16, int(50_000_000 // k))
-        x, w, s = gen(mmax, k, n)
-        w, s = np.ascontiguousarray(w[:, :cols]), s[:cols]
-        w_bytes_per_step = sum(((k * cols // 2) if fmt == "w4a16" else k * cols) + 2 * cols
-                               for _ in ms)
+        x, w, s, z = gen(mmax, k, n, GROUP_K)
+        w, s, z = np.ascontiguousarray(w[:, :cols]), s[:, :cols], z[:, :cols]
+        gemm = lambda xm, w, s: ggemm(xm, w, s, z, GROUP_K)  # noqa: E731
+        w_bytes_per_step = sum(((k * cols // 2) if w4 else k * cols) + 3 * s.size for _ in ms)
+    if fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped") and mmax <= 16:
+        if fmt in ("w4a16", "w8a16"):
+            gen = wl.w4a16 if fmt == "w4a16" else wl.w8a16
+            gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16
+            # bounded sample: the full K and a column slice sized for ~1 s per step
+            cols = n if k * n <= 50_000_000 else max(16, int(50_000_000 // k))
+            x, w, s = gen(mmax, k, n)
+            w, s = np.ascontiguousarray(w[:, :cols]), s[:cols]
+            w_bytes_per_step = sum(((k * cols // 2) if fmt == "w4a16" else k * cols) + 2 * cols
+                                   for _ in ms)
         unit, done, t0 = "GB/s", 0, time.perf_counter()
         while True:
             for m in ms:

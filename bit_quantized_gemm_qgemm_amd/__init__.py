@@ -18,8 +18,11 @@ QGEMM_W4A16 = 1
 QGEMM_W8A16 = 2
 QGEMM_MXFP4 = 3
 QGEMM_FP8 = 4
+QGEMM_W4A16_GROUPED = 5
+QGEMM_W8A16_GROUPED = 6
 
-FORMATS = {"w4a16": QGEMM_W4A16, "w8a16": QGEMM_W8A16, "mxfp4": QGEMM_MXFP4, "fp8": QGEMM_FP8}
+FORMATS = {"w4a16": QGEMM_W4A16, "w8a16": QGEMM_W8A16, "mxfp4": QGEMM_MXFP4, "fp8": QGEMM_FP8,
+           "w4a16_grouped": QGEMM_W4A16_GROUPED, "w8a16_grouped": QGEMM_W8A16_GROUPED}
 
 # (name, restype, argtypes) of every symbol declared in include/qgemm.h
 _P = ctypes.c_void_p
@@ -35,6 +38,11 @@ _SIGNATURES = [
     ("qgemm_w8a16", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     ("qgemm_mxfp4", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     ("qgemm_fp8", ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    ("qgemm_prepack_grouped_bytes", ctypes.c_int64, [ctypes.c_int, _I64, _I64, _I64]),
+    ("qgemm_prepack_grouped", ctypes.c_int,
+     [ctypes.c_int, _P, _P, _P, _I64, _I64, _P, _I64, _I64, _P]),
+    ("qgemm_w4a16_grouped", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    ("qgemm_w8a16_grouped", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _P]),
 ]
 
 _lib = None
@@ -225,3 +233,70 @@ def qgemm_fp8(a, b_packed, scale_a, scale_b, N, out=None):
     _check(lib().qgemm_fp8(_ptr(a), _ptr(b_packed), _ptr(scale_a), _ptr(scale_b), _ptr(out), M,
                            N, K, _stream(a)), "qgemm_fp8")
     return out
+
+
+def qgemm_prepack_grouped_bytes(fmt, K, N, group_k):
+    n = lib().qgemm_prepack_grouped_bytes(int(FORMATS.get(fmt, fmt)), int(K), int(N), int(group_k))
+    if n < 0:
+        raise QgemmError(int(n), "qgemm_prepack_grouped_bytes")
+    return int(n)
+
+
+def qgemm_prepack_grouped(fmt, w, K, N, scales, zeros=None, group_k=128, group_n=1):
+    """Codes + group-wise fp16 scales [ceil(K/group_k), ceil(N/group_n)] (+ zero
+    points of the same shape: uint8 0..15 for W4, int8 for W8; None for the
+    symmetric 8 / 0) -> opaque packed uint8 device tensor."""
+    fmt = FORMATS.get(fmt, fmt)
+    if fmt == QGEMM_W4A16_GROUPED:
+        _need(w, torch.uint8, 2, "w")
+        if tuple(w.shape) != (K // 2, N):
+            raise ValueError("grouped W4A16 weight must be uint8 [K/2, N]")
+        zdtype = torch.uint8
+    elif fmt == QGEMM_W8A16_GROUPED:
+        _need(w, torch.int8, 2, "w")
+        if tuple(w.shape) != (K, N):
+            raise ValueError("grouped W8A16 weight must be int8 [K, N]")
+        zdtype = torch.int8
+    else:
+        raise ValueError(f"not a grouped format: {fmt}")
+    shape = (-(-K // group_k), -(-N // group_n))
+    _need(scales, torch.float16, 2, "scales")
+    if tuple(scales.shape) != shape:
+        raise ValueError(f"scales must be {shape}")
+    if zeros is not None:
+        _need(zeros, zdtype, 2, "zeros")
+        if tuple(zeros.shape) != shape:
+            raise ValueError(f"zeros must be {shape}")
+    nbytes = qgemm_prepack_grouped_bytes(fmt, K, N, group_k)
+    out = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=w.device)
+    _check(lib().qgemm_prepack_grouped(fmt, _ptr(w), _ptr(scales), _ptr(zeros), int(group_k),
+                                       int(group_n), _ptr(out), int(K), int(N), _stream(w)),
+           "qgemm_prepack_grouped")
+    return out
+
+
+def _grouped(name, fmt, x, w_packed, N, group_k, out):
+    _need(x, torch.float16, 2, "x")
+    _need(w_packed, torch.uint8, 1, "w_packed")
+    M, K = x.shape
+    if w_packed.numel() < qgemm_prepack_grouped_bytes(fmt, K, N, group_k):
+        raise ValueError("w_packed is smaller than the packed size for this K, N, group_k")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, 2, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    _check(getattr(lib(), name)(_ptr(x), _ptr(w_packed), _ptr(out), M, N, K, int(group_k),
+                                _stream(x)), name)
+    return out
+
+
+def qgemm_w4a16_grouped(x, w_packed, N, group_k, out=None):
+    """Y = X @ ((code - z) * s) with group-wise s, z -> fp16 [M, N]."""
+    return _grouped("qgemm_w4a16_grouped", QGEMM_W4A16_GROUPED, x, w_packed, N, group_k, out)
+
+
+def qgemm_w8a16_grouped(x, w_packed, N, group_k, out=None):
+    """Y = X @ ((w - z) * s) with group-wise s, z -> fp16 [M, N]."""
+    return _grouped("qgemm_w8a16_grouped", QGEMM_W8A16_GROUPED, x, w_packed, N, group_k, out)

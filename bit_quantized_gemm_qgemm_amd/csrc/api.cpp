@@ -13,6 +13,7 @@ namespace {
 
 using qgemm::PackGeom;
 using qgemm::pack_geom;
+using qgemm::grouped_geom;
 
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;   // kernels index with 32-bit ints
 // Smallest M for which the weight-only GEMMs take the tiled kernel.
@@ -94,6 +95,28 @@ int weight_only(int fmt, const void* x, const void* w_packed, const void* scales
                                             K, as_stream(stream)));
 }
 
+// Grouped weight-only formats: K and group_k multiples of 32 (a 32-element
+// matrix step never straddles two groups), the sizes of the per-column format.
+int check_grouped(int fmt, int64_t M, int64_t N, int64_t K, int64_t group_k) {
+  if (fmt != QGEMM_W4A16_GROUPED && fmt != QGEMM_W8A16_GROUPED) return QGEMM_ERR_FORMAT;
+  if (group_k <= 0 || group_k % 32 != 0 || K % 32 != 0) return QGEMM_ERR_SHAPE;
+  if (group_k >= kMaxIndex) return QGEMM_ERR_SHAPE;
+  return check_sizes(fmt == QGEMM_W4A16_GROUPED ? QGEMM_W4A16 : QGEMM_W8A16, M, N, K);
+}
+
+int grouped_gemm(int fmt, const void* x, const void* w_packed, void* y, int64_t M, int64_t N,
+                 int64_t K, int64_t group_k, void* stream) {
+  int st = check_grouped(fmt, M, N, K, group_k);
+  if (st != QGEMM_OK) return st;
+  if (!present(x, M * K) || !present(w_packed, K * N) || !present(y, M * N))
+    return QGEMM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 16)) return QGEMM_ERR_ALIGN;
+  if (M == 0 || N == 0) return QGEMM_OK;
+  if ((st = check_device()) != QGEMM_OK) return st;
+  return launched(qgemm::launch_decode_grouped(fmt, x, w_packed, y, M, N, K, group_k,
+                                               as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,7 +135,7 @@ const char* qgemm_status_string(int status) {
   }
 }
 
-int qgemm_abi_version(void) { return 100; }
+int qgemm_abi_version(void) { return 101; }
 
 int64_t qgemm_prepack_bytes(int fmt, int64_t K, int64_t N) {
   if (!valid_format(fmt)) return QGEMM_ERR_FORMAT;
@@ -134,6 +157,39 @@ int qgemm_prepack(int fmt, const void* w, const void* w_scales, void* w_packed, 
   if (pack_geom(fmt, K, N).total == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
   return launched(qgemm::launch_prepack(fmt, w, w_scales, w_packed, K, N, as_stream(stream)));
+}
+
+int64_t qgemm_prepack_grouped_bytes(int fmt, int64_t K, int64_t N, int64_t group_k) {
+  const int st = check_grouped(fmt, 0, N, K, group_k);
+  if (st != QGEMM_OK) return st;
+  return grouped_geom(fmt, K, N, group_k).total;
+}
+
+int qgemm_prepack_grouped(int fmt, const void* w, const void* scales, const void* zeros,
+                          int64_t group_k, int64_t group_n, void* w_packed, int64_t K,
+                          int64_t N, void* stream) {
+  int st = check_grouped(fmt, 0, N, K, group_k);
+  if (st != QGEMM_OK) return st;
+  if (group_n < 1 || group_n >= kMaxIndex) return QGEMM_ERR_SHAPE;
+  if (!w_packed) return QGEMM_ERR_NULL;
+  const bool empty = (K == 0 || N == 0);
+  if (!empty && (!w || !scales)) return QGEMM_ERR_NULL;
+  if (!aligned(w_packed, 16) || !aligned(w, 16) || !aligned(scales, 16) || !aligned(zeros, 16))
+    return QGEMM_ERR_ALIGN;
+  if (grouped_geom(fmt, K, N, group_k).total == 0) return QGEMM_OK;
+  if ((st = check_device()) != QGEMM_OK) return st;
+  return launched(qgemm::launch_prepack_grouped(fmt, w, scales, zeros, group_k, group_n,
+                                                w_packed, K, N, as_stream(stream)));
+}
+
+int qgemm_w4a16_grouped(const void* x, const void* w_packed, void* y, int64_t M, int64_t N,
+                        int64_t K, int64_t group_k, void* stream) {
+  return grouped_gemm(QGEMM_W4A16_GROUPED, x, w_packed, y, M, N, K, group_k, stream);
+}
+
+int qgemm_w8a16_grouped(const void* x, const void* w_packed, void* y, int64_t M, int64_t N,
+                        int64_t K, int64_t group_k, void* stream) {
+  return grouped_gemm(QGEMM_W8A16_GROUPED, x, w_packed, y, M, N, K, group_k, stream);
 }
 
 int qgemm_quantize_mxfp4(const float* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* e8m0,

@@ -46,10 +46,13 @@ template <> struct DecodeTraits<4> {
   static constexpr int WV = 2, XV = 2, TB = kTileBytes;
 };
 
-template <int FMT, int G>
+// NGT > 0: grouped formats, NGT metadata words {1024 + z (+128), s} per
+// column and K tile (layout in qgemm_common.h).
+template <int FMT, int G, int NGT = 0>
 struct Chunk {
   uintx4 x[DecodeTraits<FMT>::XV];
   uintx4 w[G][DecodeTraits<FMT>::WV];
+  uint32_t meta[G][NGT > 0 ? NGT : 1];
 };
 
 // Per-lane and per-workgroup addressing of one launch.  Scalar (wave-uniform)
@@ -63,6 +66,9 @@ struct DecodeAddr {
   uint32_t wlane;         // 16 * lane
   int K;
   int g;                  // lane group, lane >> 4
+  const uint8_t* meta;    // grouped formats: first metadata tile of this workgroup
+  int64_t meta_cg_stride; // bytes between column groups of metadata
+  uint32_t mlane;         // this lane's column entries within a tile
 };
 
 // K index of the first element of X piece p of lane group g in tile kt.
@@ -76,8 +82,8 @@ __device__ __forceinline__ int piece_k(int kt, int g, int p) {
 // weight tiles.  X pieces past K read as zero.  Rows past M load row M-1
 // instead (their outputs are never stored); groups past the last column load
 // the last group (likewise discarded).
-template <int FMT, int G, bool X_ELEMENTWISE>
-__device__ __forceinline__ void load_chunk(Chunk<FMT, G>& ch, const DecodeAddr& ad, int kt) {
+template <int FMT, int G, bool X_ELEMENTWISE, int NGT = 0>
+__device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT>& ch, const DecodeAddr& ad, int kt) {
   constexpr int XV = DecodeTraits<FMT>::XV;
   constexpr int TB = DecodeTraits<FMT>::TB;
   constexpr int XB = (FMT == 4) ? 1 : 2;           // bytes per activation element
@@ -123,11 +129,23 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G>& ch, const DecodeAddr& 
     if constexpr (DecodeTraits<FMT>::WV == 2)
       ch.w[g][1] =
           __builtin_nontemporal_load(reinterpret_cast<const uintx4*>(t + 1024 + ad.wlane));
+    if constexpr (NGT > 0) {
+      const uint8_t* mt = ad.meta + gg * ad.meta_cg_stride + (int64_t)kt * (16 * NGT * 4);
+      if constexpr (NGT == 4) {
+        const uintx4 v = *reinterpret_cast<const uintx4*>(mt + ad.mlane);
+        ch.meta[g][0] = v[0]; ch.meta[g][1] = v[1]; ch.meta[g][2] = v[2]; ch.meta[g][3] = v[3];
+      } else if constexpr (NGT == 2) {
+        const uintx2 v = *reinterpret_cast<const uintx2*>(mt + ad.mlane);
+        ch.meta[g][0] = v[0]; ch.meta[g][1] = v[1];
+      } else {
+        ch.meta[g][0] = *reinterpret_cast<const uint32_t*>(mt + ad.mlane);
+      }
+    }
   }
 }
 
-template <int FMT, int G>
-__device__ __forceinline__ void compute_chunk(const Chunk<FMT, G>& ch, floatx4 (&acc)[G],
+template <int FMT, int G, int NGT = 0>
+__device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT>& ch, floatx4 (&acc)[G],
                                               W4Masks mk) {
   if constexpr (FMT == 4) {
     const intx8 a = {(int)ch.x[0][0], (int)ch.x[0][1], (int)ch.x[0][2], (int)ch.x[0][3],
@@ -147,7 +165,16 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G>& ch, floatx4 (
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         half8_t b;
-        if constexpr (FMT == 1) {
+        if constexpr (NGT > 0) {
+          // (w - z) * s rounded once to fp16, z and s of this step's group
+          const uint32_t e = ch.meta[g][(s * NGT) >> 2];
+          if constexpr (FMT == 1) {
+            b = dequant_w4_group(ch.w[g][0][s], e);
+          } else {
+            const uintx4& h = ch.w[g][s >> 1];
+            b = dequant_w8_group(h[2 * (s & 1)], h[2 * (s & 1) + 1], e);
+          }
+        } else if constexpr (FMT == 1) {
           b = dequant_w4(ch.w[g][0][s], mk);
         } else {
           const uintx4& h = ch.w[g][s >> 1];
@@ -159,12 +186,14 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G>& ch, floatx4 (
   }
 }
 
-template <int FMT, int G, int NW, int D, bool X_ELEMENTWISE>
+// NGT > 0: grouped W4A16 / W8A16 (scales and zero points in the metadata
+// segment at wp + meta_offset; `scales` unused).
+template <int FMT, int G, int NW, int D, bool X_ELEMENTWISE, int NGT = 0>
 __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ wp,
     const _Float16* __restrict__ scales, const float* __restrict__ scale_a,
     const float* __restrict__ scale_b, uint16_t* __restrict__ y, int M, int N, int K, int KT,
-    int CG) {
+    int CG, int64_t meta_offset) {
   static_assert(NW >= 2, "the K split needs at least two waves");
   static_assert(D >= 2 && D <= 4, "prefetch depth 2..4");
   constexpr int TB = DecodeTraits<FMT>::TB;
@@ -186,6 +215,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   ad.cg_last = CG - 1 - cg0;
   ad.wlane = 16u * lane;
   ad.K = K;
+  ad.meta_cg_stride = (int64_t)KT * (16 * (NGT > 0 ? NGT : 1) * 4);
+  ad.meta = wp + meta_offset + (int64_t)cg0 * ad.meta_cg_stride;
+  ad.mlane = (uint32_t)((lane & 15) * (NGT > 0 ? NGT : 1) * 4);
 
   W4Masks mk{};
   if constexpr (FMT == 1) mk = W4Masks{vgpr_const(0x000f000fu), vgpr_const(0x00f000f0u)};
@@ -196,17 +228,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
 
   // K tiles wave, wave + NW, ...; a ring of D register buffers keeps D tiles
   // of loads in flight per wave
-  Chunk<FMT, G> ring[D];
+  Chunk<FMT, G, NGT> ring[D];
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (wave + d * NW < KT) load_chunk<FMT, G, X_ELEMENTWISE>(ring[d], ad, wave + d * NW);
+    if (wave + d * NW < KT) load_chunk<FMT, G, X_ELEMENTWISE, NGT>(ring[d], ad, wave + d * NW);
   for (int base = wave; base < KT; base += D * NW) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int kt = base + d * NW;
       if (kt < KT) {
-        compute_chunk<FMT, G>(ring[d], acc, mk);
-        if (kt + D * NW < KT) load_chunk<FMT, G, X_ELEMENTWISE>(ring[d], ad, kt + D * NW);
+        compute_chunk<FMT, G, NGT>(ring[d], acc, mk);
+        if (kt + D * NW < KT) load_chunk<FMT, G, X_ELEMENTWISE, NGT>(ring[d], ad, kt + D * NW);
       }
     }
   }
@@ -235,6 +267,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
     if (gm < M && gn < N) {
       if constexpr (FMT == 4) {
         y[(int64_t)gm * N + gn] = f32_to_bf16_rne(sum * fp8_scale);
+      } else if constexpr (NGT > 0) {
+        y[(int64_t)gm * N + gn] = f32_to_f16_bits(sum);   // scales already applied
       } else {
         y[(int64_t)gm * N + gn] = f32_to_f16_bits((float)scales[gn] * sum);
       }
@@ -278,7 +312,7 @@ hipError_t launch_cfg(const void* x, const void* w, const void* s, const float* 
   dim3 block(NW * kWave);
   hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, D, ELEMENTWISE>), grid, block, 0, stream,
                      (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)s, sa, sb,
-                     (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG);
+                     (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG, (int64_t)0);
   return hipGetLastError();
 }
 
@@ -316,7 +350,57 @@ hipError_t launch_fmt(const void* x, const void* w, const void* s, const float* 
   return launch_fmt_cfg<FMT>(c, x, w, s, sa, sb, y, M, N, K, pg.kt, pg.cg, stream);
 }
 
+// Grouped formats: the same kernel with NGT metadata words per column and K
+// tile, D = 2; G and NW as for the per-column formats with fewer rows.
+template <int FMT, int NGT, int G, int NW>
+hipError_t launch_grouped_cfg(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                              int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
+                              hipStream_t stream) {
+  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16));
+  dim3 block(NW * kWave);
+  hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, 2, false, NGT>), grid, block, 0, stream,
+                     (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)nullptr,
+                     (const float*)nullptr, (const float*)nullptr, (uint16_t*)y, (int)M, (int)N,
+                     (int)K, (int)KT, (int)CG, meta_offset);
+  return hipGetLastError();
+}
+
+template <int FMT, int NGT>
+hipError_t launch_grouped_ngt(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                              int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
+                              hipStream_t stream) {
+  const int64_t rows = M < 16 ? M : 16;
+  int g = rows <= 4 ? (FMT == 1 ? 2 : 1) : 4;
+  while (g > 1 && cdiv(CG, g) < 128) g /= 2;
+  const int nw = KT < 16 ? 4 : 8;
+#define QG_GCASE(GG, WW)                                                                   \
+  if (g == GG && nw == WW)                                                                 \
+    return launch_grouped_cfg<FMT, NGT, GG, WW>(x, w, y, M, N, K, KT, CG, meta_offset, stream);
+  QG_GCASE(1, 4) QG_GCASE(1, 8) QG_GCASE(2, 4) QG_GCASE(2, 8) QG_GCASE(4, 4) QG_GCASE(4, 8)
+#undef QG_GCASE
+  return hipErrorInvalidValue;
+}
+
+template <int FMT>
+hipError_t launch_grouped_fmt(const void* x, const void* w, void* y, int64_t M, int64_t N,
+                              int64_t K, int64_t group_k, hipStream_t stream) {
+  const PackGeom g = grouped_geom(FMT == 1 ? 5 : 6, K, N, group_k);
+  switch (grouped_ngt(group_k)) {
+    case 1: return launch_grouped_ngt<FMT, 1>(x, w, y, M, N, K, g.kt, g.cg, g.scales, stream);
+    case 2: return launch_grouped_ngt<FMT, 2>(x, w, y, M, N, K, g.kt, g.cg, g.scales, stream);
+    default: return launch_grouped_ngt<FMT, 4>(x, w, y, M, N, K, g.kt, g.cg, g.scales, stream);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_decode_grouped(int fmt, const void* x, const void* w_packed, void* y,
+                                 int64_t M, int64_t N, int64_t K, int64_t group_k,
+                                 hipStream_t stream) {
+  if (fmt == 5) return launch_grouped_fmt<1>(x, w_packed, y, M, N, K, group_k, stream);
+  if (fmt == 6) return launch_grouped_fmt<2>(x, w_packed, y, M, N, K, group_k, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode_gemm(int fmt, const void* x, const void* w_packed, const void* scales,
                               const float* scale_a, const float* scale_b, void* y, int64_t M,

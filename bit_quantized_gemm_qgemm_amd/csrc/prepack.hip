@@ -128,6 +128,35 @@ __global__ void prepack_mxfp4_scales_kernel(const uint8_t* __restrict__ in,
   out[d] = word;
 }
 
+// Metadata segment of the grouped formats: one thread per 4-byte entry
+// ((cg * KT + kt) * 16 + c) * NGT + j (layout in qgemm_common.h).
+__global__ void prepack_group_meta_kernel(const uint16_t* __restrict__ scales,
+                                          const uint8_t* __restrict__ zeros, bool w4,
+                                          uint32_t* __restrict__ out, int64_t K, int64_t N,
+                                          int64_t KT, int64_t group_k, int64_t group_n, int ngt,
+                                          int64_t entries) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= entries) return;
+  const int j = (int)(d % ngt);
+  const int64_t col = d / ngt;              // (cg * KT + kt) * 16 + c
+  const int c = (int)(col & 15);
+  const int64_t tile = col >> 4;
+  const int64_t cg = tile / KT;
+  const int64_t kt = tile - cg * KT;
+  const int64_t n = cg * kTileN + c;
+  const int64_t k0 = kt * kTileK8 + j * (kTileK8 / ngt);
+  const int64_t ng_count = cdiv(N, group_n);
+  int z = w4 ? 8 : 0;
+  uint16_t s_bits = 0;                      // padding: scale 0
+  if (n < N && k0 < K) {
+    const int64_t e = (k0 / group_k) * ng_count + n / group_n;
+    s_bits = scales[e];
+    if (zeros != nullptr) z = w4 ? (int)zeros[e] : (int)(int8_t)zeros[e];
+  }
+  const float zc = (float)((w4 ? 1024 : 1152) + z);   // exact in fp16
+  out[d] = (uint32_t)f32_to_f16_bits(zc) | ((uint32_t)s_bits << 16);
+}
+
 __global__ void zero_words_kernel(uint32_t* __restrict__ out, int64_t words) {
   const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (d < words) out[d] = 0u;
@@ -180,6 +209,30 @@ hipError_t launch_prepack(int fmt, const void* w, const void* w_scales, void* pa
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prepack_grouped(int fmt, const void* w, const void* scales, const void* zeros,
+                                  int64_t group_k, int64_t group_n, void* packed, int64_t K,
+                                  int64_t N, hipStream_t stream) {
+  const PackGeom g = grouped_geom(fmt, K, N, group_k);
+  hipError_t e = launch_prepack(fmt == 5 ? 1 : 2, w, nullptr, packed, K, N, stream);
+  if (e != hipSuccess) return e;
+  uint32_t* out = static_cast<uint32_t*>(packed);
+  const int64_t gap_words = (g.scales - g.codes) / 4;
+  if (gap_words > 0) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, out + g.codes / 4,
+                       gap_words);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int ngt = grouped_ngt(group_k);
+  const int64_t entries = (g.total - g.scales) / 4;
+  if (entries == 0) return hipSuccess;
+  const int block = 256;
+  hipLaunchKernelGGL(prepack_group_meta_kernel, dim3(grid_for(entries, block)), dim3(block), 0,
+                     stream, static_cast<const uint16_t*>(scales),
+                     static_cast<const uint8_t*>(zeros), fmt == 5, out + g.scales / 4, K, N,
+                     g.kt, group_k, group_n, ngt, entries);
   return hipGetLastError();
 }
 

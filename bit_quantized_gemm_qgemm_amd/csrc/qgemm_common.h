@@ -99,11 +99,36 @@ inline PackGeom pack_geom(int fmt, int64_t K, int64_t N) {
   return g;
 }
 
+// Grouped weight-only formats (5 = W4A16, 6 = W8A16 with group-wise scales
+// and zero points): the code segment of format 1 / 2, then, 256-byte
+// aligned, a metadata segment.  For each tile (cg, kt) and column c of it
+// (16 per tile) there are NGT 4-byte entries at
+//   ((cg * KT + kt) * 16 + c) * NGT + j,
+// entry j covering the 128 / NGT K elements kt*128 + j*128/NGT + [0, 128/NGT)
+// of column cg*16 + c: low half fp16 (1024 + z) for W4 or (1152 + z) for W8
+// (the exponent-pattern subtrahend that leaves w - z), high half the fp16
+// scale.  NGT = 1 when group_k is a multiple of 128, 2 when it is 64,
+// otherwise 4 (one entry per 32-element matrix step; group_k % 32 == 0, so a
+// step never straddles two groups).  Padding entries have scale 0.
+inline int grouped_ngt(int64_t group_k) {
+  return group_k % 128 == 0 ? 1 : group_k == 64 ? 2 : 4;
+}
+
+inline PackGeom grouped_geom(int fmt, int64_t K, int64_t N, int64_t group_k) {
+  PackGeom g = pack_geom(fmt == 5 ? 1 : 2, K, N);
+  g.scales = cdiv(g.codes, 256) * 256;
+  g.total = g.scales + g.cg * g.kt * 16 * grouped_ngt(group_k) * 4;
+  return g;
+}
+
 // ---- launchers (defined in the .hip files; all enqueue on `stream`) -------
 // Each returns hipSuccess or the launch error.
 
 hipError_t launch_prepack(int fmt, const void* w, const void* w_scales, void* packed,
                           int64_t K, int64_t N, hipStream_t stream);
+hipError_t launch_prepack_grouped(int fmt, const void* w, const void* scales, const void* zeros,
+                                  int64_t group_k, int64_t group_n, void* packed, int64_t K,
+                                  int64_t N, hipStream_t stream);
 
 hipError_t launch_quantize_mxfp4(const float* x, int64_t rows, int64_t K, uint8_t* codes,
                                  uint8_t* e8m0, hipStream_t stream);
@@ -114,6 +139,11 @@ hipError_t launch_quantize_fp8(const float* x, int64_t count, uint8_t* codes, fl
 hipError_t launch_decode_gemm(int fmt, const void* x, const void* w_packed, const void* scales,
                               const float* scale_a, const float* scale_b, void* y,
                               int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Grouped W4A16 / W8A16 (formats 5, 6): M rows in 16-row slabs.
+hipError_t launch_decode_grouped(int fmt, const void* x, const void* w_packed, void* y,
+                                 int64_t M, int64_t N, int64_t K, int64_t group_k,
+                                 hipStream_t stream);
 
 // LDS-tiled matrix-core path for W4A16 / W8A16 at large M (fp16 X with K a
 // positive multiple of 8; 256 x 256 output tiles).

@@ -57,6 +57,32 @@ __device__ __forceinline__ half8_t dequant_w4_shift(uint32_t q) {
   return half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
+// Grouped formats: e = {low: fp16 1024 + z (W4) or 1152 + z (W8), high:
+// fp16 scale}.  (1024 + code) - (1024 + z) is exact, so each weight becomes
+// (w - z) * s rounded once to fp16 (the W4A16 page's section-1 dequant).
+__device__ __forceinline__ half8_t dequant_w4_group(uint32_t q, uint32_t e) {
+  const half2_t me = __builtin_bit_cast(half2_t, e);
+  const half2_t zc = {me.x, me.x};
+  const half2_t sc = {me.y, me.y};
+  const uint32_t magic = 0x64006400u;
+  const half2_t h0 = (__builtin_bit_cast(half2_t, (q & 0x000f000fu) | magic) - zc) * sc;
+  const half2_t h1 = (__builtin_bit_cast(half2_t, ((q >> 4) & 0x000f000fu) | magic) - zc) * sc;
+  const half2_t h2 = (__builtin_bit_cast(half2_t, ((q >> 8) & 0x000f000fu) | magic) - zc) * sc;
+  const half2_t h3 = (__builtin_bit_cast(half2_t, ((q >> 12) & 0x000f000fu) | magic) - zc) * sc;
+  return half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+
+__device__ __forceinline__ half8_t dequant_w8_group(uint32_t lo, uint32_t hi, uint32_t e) {
+  const half2_t me = __builtin_bit_cast(half2_t, e);
+  const half2_t zc = {me.x, me.x};
+  const half2_t sc = {me.y, me.y};
+  const half2_t a = (__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) - zc) * sc;
+  const half2_t b = (__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) - zc) * sc;
+  const half2_t c = (__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) - zc) * sc;
+  const half2_t d = (__builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) - zc) * sc;
+  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
 // Two biased INT8 bytes (w + 128) of a word, selected by `sel`, -> w as fp16.
 __device__ __forceinline__ half2_t dequant_w8_pair(uint32_t d, uint32_t sel) {
   // byte permute of {0x64646464 : d}: selector 0..3 picks bytes of d, 4 picks 0x64

@@ -46,12 +46,15 @@
 extern "C" {
 #endif
 
-/* Weight formats accepted by qgemm_prepack / qgemm_prepack_bytes. */
+/* Weight formats accepted by qgemm_prepack / qgemm_prepack_bytes (1-4) and
+ * by qgemm_prepack_grouped / qgemm_prepack_grouped_bytes (5, 6). */
 enum qgemm_format {
   QGEMM_W4A16 = 1,
   QGEMM_W8A16 = 2,
   QGEMM_MXFP4 = 3,
-  QGEMM_FP8 = 4
+  QGEMM_FP8 = 4,
+  QGEMM_W4A16_GROUPED = 5,   /* INT4 codes, group-wise scales, zero points */
+  QGEMM_W8A16_GROUPED = 6    /* INT8 weights, group-wise scales, zero points */
 };
 
 /* Status codes. */
@@ -166,6 +169,50 @@ int qgemm_mxfp4(const void* a_codes, const void* a_e8m0, const void* w_packed,
 int qgemm_fp8(const void* a, const void* b_packed, const float* scale_a,
               const float* scale_b, void* c, int64_t M, int64_t N, int64_t K,
               void* stream);
+
+/*
+ * Group-wise scales and asymmetric zero points (W4A16 page, section 1: the
+ * dequant (w - zero_point) * scale; W8A16 page, extensions: scales shared by
+ * groups of columns, and zero points for asymmetric quantization).  The scale
+ * and zero point of weight (k, n) are entry (k / group_k, n / group_n) of
+ * row-major tables with KG = ceil(K / group_k) rows and NG = ceil(N / group_n)
+ * columns; group_k = K, group_n = 1 is the per-column scheme of
+ * qgemm_w4a16 / qgemm_w8a16.
+ *
+ * qgemm_prepack_grouped_bytes -- size of the packed buffer (host-only).
+ * group_k must be a positive multiple of 32 and K a multiple of 32.
+ */
+int64_t qgemm_prepack_grouped_bytes(int fmt, int64_t K, int64_t N, int64_t group_k);
+
+/*
+ * qgemm_prepack_grouped -- pack codes, scales and zero points into one
+ * buffer for qgemm_w4a16_grouped / qgemm_w8a16_grouped.
+ *
+ *   fmt = QGEMM_W4A16_GROUPED: w = uint8 [K/2, N] as for QGEMM_W4A16;
+ *         zeros = uint8 [KG, NG] with values 0..15, or NULL for 8.
+ *   fmt = QGEMM_W8A16_GROUPED: w = int8 [K, N]; zeros = int8 [KG, NG], or
+ *         NULL for 0.
+ *   scales = fp16 [KG, NG], any finite values.  group_n >= 1.
+ *
+ * W_deq[k, n] = (w[k, n] - z) * s with (s, z) the entry of (k, n).  The
+ * GEMMs form each dequantized weight in fp16 as (w - z) * s rounded once to
+ * nearest-even (the W4A16 page's section-1 arithmetic) and accumulate in
+ * fp32.  Zero points are device data and are not range-checked (that would
+ * need a host sync): W4 values outside 0..15 give unspecified results.
+ */
+int qgemm_prepack_grouped(int fmt, const void* w, const void* scales, const void* zeros,
+                          int64_t group_k, int64_t group_n, void* w_packed, int64_t K,
+                          int64_t N, void* stream);
+
+/*
+ * qgemm_w4a16_grouped / qgemm_w8a16_grouped -- Y[M,N] fp16 = X[M,K] fp16 *
+ * W_deq with the grouped W_deq above; w_packed from qgemm_prepack_grouped with
+ * the same K, N and group_k.  K % 32 == 0.
+ */
+int qgemm_w4a16_grouped(const void* x, const void* w_packed, void* y, int64_t M, int64_t N,
+                        int64_t K, int64_t group_k, void* stream);
+int qgemm_w8a16_grouped(const void* x, const void* w_packed, void* y, int64_t M, int64_t N,
+                        int64_t K, int64_t group_k, void* stream);
 
 #ifdef __cplusplus
 }

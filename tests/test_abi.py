@@ -38,7 +38,8 @@ def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for want in ("qgemm_w4a16", "qgemm_w8a16", "qgemm_mxfp4", "qgemm_fp8", "qgemm_prepack",
                  "qgemm_prepack_bytes", "qgemm_quantize_mxfp4", "qgemm_quantize_fp8",
-                 "qgemm_status_string", "qgemm_abi_version"):
+                 "qgemm_status_string", "qgemm_abi_version", "qgemm_prepack_grouped",
+                 "qgemm_prepack_grouped_bytes", "qgemm_w4a16_grouped", "qgemm_w8a16_grouped"):
         assert want in names
 
 
@@ -55,7 +56,7 @@ def test_status_strings(lib):
         s = qg.status_string(st)
         assert s and s != "unknown status"
     assert qg.status_string(12345) == "unknown status"
-    assert lib.qgemm_abi_version() == 100
+    assert lib.qgemm_abi_version() == 101
 
 
 def test_prepack_bytes(lib):
@@ -123,6 +124,42 @@ def test_prepack_and_quantize_argument_errors(lib):
     assert lib.qgemm_quantize_fp8(GOOD, 16, GOOD, None, s) == ERR_NULL
     assert lib.qgemm_quantize_fp8(GOOD, -1, GOOD, GOOD, s) == ERR_SHAPE
     assert lib.qgemm_quantize_fp8(GOOD, 16, GOOD, P(0x10001), s) == ERR_ALIGN
+
+
+def test_grouped_prepack_bytes(lib):
+    # codes as for the per-column format, 256-aligned, then 4 bytes per column,
+    # K tile and metadata entry (1 entry per tile for group_k % 128 == 0,
+    # 2 for 64, else 4)
+    codes_w4 = 4096 * 4096 // 2
+    assert lib.qgemm_prepack_grouped_bytes(5, 4096, 4096, 128) == codes_w4 + 4096 * 32 * 4
+    assert lib.qgemm_prepack_grouped_bytes(5, 4096, 4096, 4096) == codes_w4 + 4096 * 32 * 4
+    assert lib.qgemm_prepack_grouped_bytes(5, 4096, 4096, 64) == codes_w4 + 4096 * 32 * 8
+    assert lib.qgemm_prepack_grouped_bytes(6, 4096, 4096, 32) == 4096 * 4096 + 4096 * 32 * 16
+    assert lib.qgemm_prepack_grouped_bytes(6, 4096, 4096, 96) == 4096 * 4096 + 4096 * 32 * 16
+    # 9 column groups x 2 K tiles: codes 9*2*2048 = 36864 (256-aligned), metadata 9*2*16*4
+    assert lib.qgemm_prepack_grouped_bytes(6, 160, 130, 32) == 36864 + 9 * 2 * 16 * 16
+    assert lib.qgemm_prepack_grouped_bytes(5, 4096, 4096, 48) == ERR_SHAPE   # group_k % 32
+    assert lib.qgemm_prepack_grouped_bytes(5, 4100, 4096, 128) == ERR_SHAPE  # K % 32
+    assert lib.qgemm_prepack_grouped_bytes(5, 4096, 4096, 0) == ERR_SHAPE
+    assert lib.qgemm_prepack_grouped_bytes(1, 4096, 4096, 128) == ERR_FORMAT
+    assert lib.qgemm_prepack_grouped_bytes(5, 0, 16, 128) == 0
+
+
+def test_grouped_argument_errors_need_no_device(lib):
+    s = P(0)
+    pg = lib.qgemm_prepack_grouped
+    assert pg(1, GOOD, GOOD, None, 128, 1, GOOD, 128, 16, s) == ERR_FORMAT
+    assert pg(5, GOOD, None, None, 128, 1, GOOD, 128, 16, s) == ERR_NULL    # scales required
+    assert pg(5, GOOD, GOOD, None, 128, 0, GOOD, 128, 16, s) == ERR_SHAPE   # group_n >= 1
+    assert pg(5, GOOD, GOOD, None, 100, 1, GOOD, 128, 16, s) == ERR_SHAPE
+    assert pg(6, GOOD, GOOD, ODD, 128, 1, GOOD, 128, 16, s) == ERR_ALIGN
+    assert pg(6, None, None, None, 128, 1, GOOD, 0, 16, s) == OK            # nothing to pack
+    for fn in (lib.qgemm_w4a16_grouped, lib.qgemm_w8a16_grouped):
+        assert fn(None, GOOD, GOOD, 4, 16, 128, 128, s) == ERR_NULL
+        assert fn(GOOD, GOOD, GOOD, 4, 16, 120, 128, s) == ERR_SHAPE       # K % 32
+        assert fn(GOOD, GOOD, GOOD, 4, 16, 128, 48, s) == ERR_SHAPE        # group_k % 32
+        assert fn(GOOD, ODD, GOOD, 4, 16, 128, 128, s) == ERR_ALIGN
+        assert fn(GOOD, GOOD, GOOD, 0, 16, 128, 128, s) == OK              # empty: no-op
 
 
 def test_binding_refuses_to_run_without_the_library(monkeypatch, tmp_path):
