@@ -18,7 +18,8 @@ Sources (the web pages these functions restate; short names used below):
   (blog.hotdry.top, 2025/10/03), kernel example and parameter list.
 
 Group-wise scales and zero points (grouped.py) follow the W4A16 page's
-section 1 dequant form and the W8A16 page's extensions.
+section 1 dequant form and the W8A16 page's extensions; NVFP4-style two-level
+block scaling (nvfp4.py) the W4A16 page's section 3.
 
 Parity status of each function is stated in its module.  Parity unpinned:
 the FP8 per-tensor scale formula (the FP8 page fixes only the 448 range and
@@ -40,6 +41,7 @@ from .formats import (
     round_bf16,
 )
 from .quantize import mxfp4_quantize, mxfp4_dequant, fp8_quantize
+from .nvfp4 import NVFP4_BLOCK, dequant_nvfp4, gemm_nvfp4
 from .grouped import (
     expand_groups,
     dequant_w4_grouped,
@@ -86,4 +88,7 @@ __all__ = [
     "dequant_w8_grouped",
     "gemm_w4a16_grouped",
     "gemm_w8a16_grouped",
+    "NVFP4_BLOCK",
+    "dequant_nvfp4",
+    "gemm_nvfp4",
 ]

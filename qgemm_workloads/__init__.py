@@ -105,6 +105,20 @@ def w8a16_grouped(m, k, n, group_k, group_n=1, zeros=True, seed=SEED):
     return x, w, scales, z
 
 
+def nvfp4_weight(m, k, n, seed=SEED):
+    """(x fp16 [m,k], codes uint8 [n,k/2], block scales uint8 e4m3 [n,k/16],
+    global fp32).  Codes: uniform bytes.  Block scales: positive normal e4m3
+    with exponent field 4..10 (values 2^-3 .. 2^3 * (1 + m/8)).  The global
+    scale 0.01 keeps |Y| of order one."""
+    rng = np.random.default_rng(seed)
+    x = _normal_f16(rng, (m, k))
+    codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    exp = rng.integers(4, 11, size=(n, k // 16))
+    man = rng.integers(0, 8, size=(n, k // 16))
+    scales = ((exp << 3) | man).astype(np.uint8)
+    return x, codes, scales, np.float32(0.01)
+
+
 def w8a16_page_test(m=32, k=128, n=256, seed=SEED):
     """The W8A16 page's test distribution: w in -128..126, scales N(0,1)*0.01."""
     rng = np.random.default_rng(seed)
