@@ -58,6 +58,8 @@ WORKLOADS = {
     # group-wise scales along K (128) with zero points, at the decode shapes
     "w4a16_g128_decode": ("w4a16_grouped", (1, 8, 16), 28672, 8192),
     "w8a16_g128_decode": ("w8a16_grouped", (1, 4, 16), 11008, 4096),
+    # NVFP4-style weights (e4m3 scale per 16 elements, fp32 per tensor), fp16 X
+    "nvfp4_decode": ("nvfp4", (1, 8, 16), 28672, 8192),
 }
 GROUP_K = 128   # group size of the grouped workloads
 DEFAULT_WORKLOAD = "w8a16_decode"
@@ -135,6 +137,22 @@ class Setup:
                 alg = w_bytes + 2 * m * k + 2 * m * n
                 self.calls.append((lambda c, xm=xm, out=out: fn(xm, self.copies[c], n, GROUP_K,
                                                                 out=out),
+                                   alg, w_bytes, 2 * m * n * k))
+        elif fmt == "nvfp4":
+            x, codes, scales, g = wl.nvfp4_weight(mmax, k, n)
+            packed = qg.qgemm_prepack("nvfp4", torch.from_numpy(codes).to(dev), k, n,
+                                      w_scales=torch.from_numpy(scales).to(dev))
+            gs = torch.tensor([g], dtype=torch.float32, device=dev)
+            x_d = torch.from_numpy(x).to(dev)
+            w_bytes = k * n // 2 + k * n // 16          # codes + one e4m3 byte per 16
+            self.copies = self._rotate(packed, w_bytes)
+            self.dtype = "f16"
+            for m in ms:
+                xm = x_d[:m].contiguous()
+                out = torch.empty((m, n), dtype=torch.float16, device=dev)
+                alg = w_bytes + 2 * m * k + 2 * m * n
+                self.calls.append((lambda c, xm=xm, out=out: qg.qgemm_nvfp4(xm, self.copies[c], gs,
+                                                                            n, out=out),
                                    alg, w_bytes, 2 * m * n * k))
         elif fmt == "mxfp4":
             a, w = wl.mxfp4_operands(mmax, n, k)
@@ -296,7 +314,13 @@ def cpu_baseline(name, budget_s=10.0):
         w, s, z = np.ascontiguousarray(w[:, :cols]), s[:, :cols], z[:, :cols]
         gemm = lambda xm, w, s: ggemm(xm, w, s, z, GROUP_K)  # noqa: E731
         w_bytes_per_step = sum(((k * cols // 2) if w4 else k * cols) + 3 * s.size for _ in ms)
-    if fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped") and mmax <= 16:
+    if fmt == "nvfp4":
+        cols = n if k * n <= 50_000_000 else max(16, int(50_000_000 // k))
+        x, codes, scales, g = wl.nvfp4_weight(mmax, k, n)
+        w, s = np.ascontiguousarray(codes[:cols]), np.ascontiguousarray(scales[:cols])
+        gemm = lambda xm, w, s: oracle.gemm_nvfp4(xm, w, s, g)  # noqa: E731
+        w_bytes_per_step = sum(k * cols // 2 + k * cols // 16 for _ in ms)
+    if fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped", "nvfp4") and mmax <= 16:
         if fmt in ("w4a16", "w8a16"):
             gen = wl.w4a16 if fmt == "w4a16" else wl.w8a16
             gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16

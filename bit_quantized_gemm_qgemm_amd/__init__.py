@@ -20,9 +20,11 @@ QGEMM_MXFP4 = 3
 QGEMM_FP8 = 4
 QGEMM_W4A16_GROUPED = 5
 QGEMM_W8A16_GROUPED = 6
+QGEMM_NVFP4 = 7
 
 FORMATS = {"w4a16": QGEMM_W4A16, "w8a16": QGEMM_W8A16, "mxfp4": QGEMM_MXFP4, "fp8": QGEMM_FP8,
-           "w4a16_grouped": QGEMM_W4A16_GROUPED, "w8a16_grouped": QGEMM_W8A16_GROUPED}
+           "w4a16_grouped": QGEMM_W4A16_GROUPED, "w8a16_grouped": QGEMM_W8A16_GROUPED,
+           "nvfp4": QGEMM_NVFP4}
 
 # (name, restype, argtypes) of every symbol declared in include/qgemm.h
 _P = ctypes.c_void_p
@@ -43,6 +45,7 @@ _SIGNATURES = [
      [ctypes.c_int, _P, _P, _P, _I64, _I64, _P, _I64, _I64, _P]),
     ("qgemm_w4a16_grouped", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     ("qgemm_w8a16_grouped", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    ("qgemm_nvfp4", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
 ]
 
 _lib = None
@@ -123,6 +126,12 @@ def qgemm_prepack(fmt, w, K, N, w_scales=None):
         _need(w_scales, torch.uint8, 2, "w_scales")
         if tuple(w.shape) != (N, K // 2) or tuple(w_scales.shape) != (N, K // 32):
             raise ValueError("MXFP4 weight must be codes uint8 [N, K/2] and scales uint8 [N, K/32]")
+    elif fmt == QGEMM_NVFP4:
+        _need(w, torch.uint8, 2, "w")
+        _need(w_scales, torch.uint8, 2, "w_scales")
+        if tuple(w.shape) != (N, K // 2) or tuple(w_scales.shape) != (N, K // 16) or K % 16:
+            raise ValueError("NVFP4 weight must be codes uint8 [N, K/2] and e4m3 scales "
+                             "uint8 [N, K/16], K a multiple of 16")
     elif fmt == QGEMM_FP8:
         if w.dtype == torch.float8_e4m3fn:
             w = w.view(torch.uint8)
@@ -300,3 +309,24 @@ def qgemm_w4a16_grouped(x, w_packed, N, group_k, out=None):
 def qgemm_w8a16_grouped(x, w_packed, N, group_k, out=None):
     """Y = X @ ((w - z) * s) with group-wise s, z -> fp16 [M, N]."""
     return _grouped("qgemm_w8a16_grouped", QGEMM_W8A16_GROUPED, x, w_packed, N, group_k, out)
+
+
+def qgemm_nvfp4(x, w_packed, global_scale, N, out=None):
+    """Y = X @ (e2m1 * e4m3 block scale * global)^T -> fp16 [M, N]; global_scale
+    is a one-element float32 device tensor."""
+    _need(x, torch.float16, 2, "x")
+    _need(w_packed, torch.uint8, 1, "w_packed")
+    if global_scale.dtype != torch.float32 or not global_scale.is_cuda or global_scale.numel() != 1:
+        raise TypeError("global_scale must be a one-element float32 device tensor")
+    M, K = x.shape
+    if w_packed.numel() < qgemm_prepack_bytes(QGEMM_NVFP4, K, N):
+        raise ValueError("w_packed is smaller than the packed size for this K, N")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, 2, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must be [M, N]")
+    _check(lib().qgemm_nvfp4(_ptr(x), _ptr(w_packed), _ptr(global_scale), _ptr(out), M, N, K,
+                             _stream(x)), "qgemm_nvfp4")
+    return out

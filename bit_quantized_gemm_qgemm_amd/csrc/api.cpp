@@ -22,7 +22,10 @@ constexpr int kDecodeMaxM = 16;                   // small-M (bandwidth) path bo
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-bool valid_format(int fmt) { return fmt >= QGEMM_W4A16 && fmt <= QGEMM_FP8; }
+// formats of qgemm_prepack (the grouped ones have their own prepack)
+bool valid_format(int fmt) {
+  return (fmt >= QGEMM_W4A16 && fmt <= QGEMM_FP8) || fmt == QGEMM_NVFP4;
+}
 
 // K constraints per format (see qgemm.h).
 bool k_ok(int fmt, int64_t K) {
@@ -31,6 +34,7 @@ bool k_ok(int fmt, int64_t K) {
     case QGEMM_W8A16: return true;
     case QGEMM_MXFP4: return K % 32 == 0;
     case QGEMM_FP8: return K % 16 == 0;
+    case QGEMM_NVFP4: return K % 16 == 0;
     default: return false;
   }
 }
@@ -152,7 +156,7 @@ int qgemm_prepack(int fmt, const void* w, const void* w_scales, void* w_packed, 
   if (st != QGEMM_OK) return st;
   const bool empty = (K == 0 || N == 0);
   if (!empty && !w) return QGEMM_ERR_NULL;
-  if (fmt == QGEMM_MXFP4 && !empty && !w_scales) return QGEMM_ERR_NULL;
+  if ((fmt == QGEMM_MXFP4 || fmt == QGEMM_NVFP4) && !empty && !w_scales) return QGEMM_ERR_NULL;
   if (!aligned(w_packed, 16)) return QGEMM_ERR_ALIGN;
   if (pack_geom(fmt, K, N).total == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
@@ -180,6 +184,20 @@ int qgemm_prepack_grouped(int fmt, const void* w, const void* scales, const void
   if ((st = check_device()) != QGEMM_OK) return st;
   return launched(qgemm::launch_prepack_grouped(fmt, w, scales, zeros, group_k, group_n,
                                                 w_packed, K, N, as_stream(stream)));
+}
+
+int qgemm_nvfp4(const void* x, const void* w_packed, const float* global_scale, void* y,
+                int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_sizes(QGEMM_NVFP4, M, N, K);
+  if (st != QGEMM_OK) return st;
+  if (!present(x, M * K) || !present(w_packed, K * N) || !present(y, M * N) || !global_scale)
+    return QGEMM_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 16) || !aligned(global_scale, 4))
+    return QGEMM_ERR_ALIGN;
+  if (M == 0 || N == 0) return QGEMM_OK;
+  if ((st = check_device()) != QGEMM_OK) return st;
+  return launched(qgemm::launch_decode_nvfp4(x, w_packed, global_scale, y, M, N, K,
+                                             as_stream(stream)));
 }
 
 int qgemm_w4a16_grouped(const void* x, const void* w_packed, void* y, int64_t M, int64_t N,

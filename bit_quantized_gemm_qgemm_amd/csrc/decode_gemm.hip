@@ -41,6 +41,10 @@ template <> struct DecodeTraits<1> {
 template <> struct DecodeTraits<2> {
   static constexpr int WV = 2, XV = 4, TB = kTileBytes;
 };
+// NVFP4 weights: 16 B of E2M1 codes per lane per tile, 64 B of fp16 X.
+template <> struct DecodeTraits<7> {
+  static constexpr int WV = 1, XV = 4, TB = kTileBytesW4;
+};
 // FP8: 32 B of W, 32 B of e4m3 A (lane holds k = 32 g + [0, 32)).
 template <> struct DecodeTraits<4> {
   static constexpr int WV = 2, XV = 2, TB = kTileBytes;
@@ -66,9 +70,10 @@ struct DecodeAddr {
   uint32_t wlane;         // 16 * lane
   int K;
   int g;                  // lane group, lane >> 4
-  const uint8_t* meta;    // grouped formats: first metadata tile of this workgroup
+  const uint8_t* meta;    // grouped / NVFP4: first metadata tile of this workgroup
   int64_t meta_cg_stride; // bytes between column groups of metadata
-  uint32_t mlane;         // this lane's column entries within a tile
+  int meta_kt_stride;     // bytes of metadata per K tile
+  uint32_t mlane;         // this lane's entries within a tile
 };
 
 // K index of the first element of X piece p of lane group g in tile kt.
@@ -130,8 +135,10 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT>& ch, const DecodeA
       ch.w[g][1] =
           __builtin_nontemporal_load(reinterpret_cast<const uintx4*>(t + 1024 + ad.wlane));
     if constexpr (NGT > 0) {
-      const uint8_t* mt = ad.meta + gg * ad.meta_cg_stride + (int64_t)kt * (16 * NGT * 4);
-      if constexpr (NGT == 4) {
+      const uint8_t* mt = ad.meta + gg * ad.meta_cg_stride + (int64_t)kt * ad.meta_kt_stride;
+      if constexpr (FMT == 7) {
+        ch.meta[g][0] = *reinterpret_cast<const uint32_t*>(mt + ad.mlane);   // 4 block scales
+      } else if constexpr (NGT == 4) {
         const uintx4 v = *reinterpret_cast<const uintx4*>(mt + ad.mlane);
         ch.meta[g][0] = v[0]; ch.meta[g][1] = v[1]; ch.meta[g][2] = v[2]; ch.meta[g][3] = v[3];
       } else if constexpr (NGT == 2) {
@@ -165,7 +172,9 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT>& ch, floa
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         half8_t b;
-        if constexpr (NGT > 0) {
+        if constexpr (FMT == 7) {
+          b = dequant_nvfp4(ch.w[g][0][s], ch.meta[g][0] >> (8 * s));
+        } else if constexpr (NGT > 0) {
           // (w - z) * s rounded once to fp16, z and s of this step's group
           const uint32_t e = ch.meta[g][(s * NGT) >> 2];
           if constexpr (FMT == 1) {
@@ -215,9 +224,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   ad.cg_last = CG - 1 - cg0;
   ad.wlane = 16u * lane;
   ad.K = K;
-  ad.meta_cg_stride = (int64_t)KT * (16 * (NGT > 0 ? NGT : 1) * 4);
+  // grouped: NGT words per column and tile; NVFP4: 8 scale bytes per column
+  // and tile, the lanes of group g reading the dword of blocks 2s + (g >> 1)
+  ad.meta_kt_stride = FMT == 7 ? kScaleTileBytes : 16 * (NGT > 0 ? NGT : 1) * 4;
+  ad.meta_cg_stride = (int64_t)KT * ad.meta_kt_stride;
   ad.meta = wp + meta_offset + (int64_t)cg0 * ad.meta_cg_stride;
-  ad.mlane = (uint32_t)((lane & 15) * (NGT > 0 ? NGT : 1) * 4);
+  ad.mlane = FMT == 7 ? (uint32_t)((lane & 15) * 8 + 4 * (ad.g >> 1))
+                      : (uint32_t)((lane & 15) * (NGT > 0 ? NGT : 1) * 4);
 
   W4Masks mk{};
   if constexpr (FMT == 1) mk = W4Masks{vgpr_const(0x000f000fu), vgpr_const(0x00f000f0u)};
@@ -247,7 +260,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
 #pragma unroll
   for (int g = 0; g < G; ++g) red[wave][g][lane] = acc[g];
   __syncthreads();
-  const float fp8_scale = (FMT == 4) ? (*scale_a) * (*scale_b) : 1.0f;
+  const float fp8_scale = (FMT == 4) ? (*scale_a) * (*scale_b) : (FMT == 7) ? *scale_a : 1.0f;
   const float* redf = reinterpret_cast<const float*>(&red[0][0][0]);
   constexpr int OUT = 16 * 16 * G;
   // consecutive threads take consecutive columns of one row (coalesced store);
@@ -267,6 +280,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
     if (gm < M && gn < N) {
       if constexpr (FMT == 4) {
         y[(int64_t)gm * N + gn] = f32_to_bf16_rne(sum * fp8_scale);
+      } else if constexpr (FMT == 7) {
+        y[(int64_t)gm * N + gn] = f32_to_f16_bits(sum * fp8_scale);   // per-tensor scale
       } else if constexpr (NGT > 0) {
         y[(int64_t)gm * N + gn] = f32_to_f16_bits(sum);   // scales already applied
       } else {
@@ -392,7 +407,36 @@ hipError_t launch_grouped_fmt(const void* x, const void* w, void* y, int64_t M, 
   }
 }
 
+template <int G, int NW>
+hipError_t launch_nvfp4_cfg(const void* x, const void* w, const float* gs, void* y, int64_t M,
+                            int64_t N, int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
+                            hipStream_t stream) {
+  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16));
+  dim3 block(NW * kWave);
+  hipLaunchKernelGGL((decode_gemm_kernel<7, G, NW, 2, false, 1>), grid, block, 0, stream,
+                     (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)nullptr, gs,
+                     (const float*)nullptr, (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT,
+                     (int)CG, meta_offset);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_decode_nvfp4(const void* x, const void* w_packed, const float* global_scale,
+                               void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const PackGeom pg = pack_geom(7, K, N);
+  const int64_t rows = M < 16 ? M : 16;
+  int g = rows <= 4 ? 2 : 4;
+  while (g > 1 && cdiv(pg.cg, g) < 128) g /= 2;
+  const int nw = pg.kt < 16 ? 4 : 8;
+#define QG_NCASE(GG, WW)                                                                   \
+  if (g == GG && nw == WW)                                                                 \
+    return launch_nvfp4_cfg<GG, WW>(x, w_packed, global_scale, y, M, N, K, pg.kt, pg.cg,   \
+                                    pg.scales, stream);
+  QG_NCASE(1, 4) QG_NCASE(1, 8) QG_NCASE(2, 4) QG_NCASE(2, 8) QG_NCASE(4, 4) QG_NCASE(4, 8)
+#undef QG_NCASE
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode_grouped(int fmt, const void* x, const void* w_packed, void* y,
                                  int64_t M, int64_t N, int64_t K, int64_t group_k,

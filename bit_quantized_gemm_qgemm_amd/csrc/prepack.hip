@@ -157,6 +157,51 @@ __global__ void prepack_group_meta_kernel(const uint16_t* __restrict__ scales,
   out[d] = (uint32_t)f32_to_f16_bits(zc) | ((uint32_t)s_bits << 16);
 }
 
+// NVFP4 codes: one thread per output word; word s of lane l of tile (cg, kt)
+// = the 4 source bytes holding k = kt*128 + 32s + 8g + [0, 8) of column n.
+__global__ void prepack_nvfp4_codes_kernel(const uint8_t* __restrict__ in,
+                                           uint32_t* __restrict__ out, int64_t K, int64_t N,
+                                           int64_t KT, int64_t words) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= words) return;
+  const int64_t tile = d >> 8;               // 256 words per 1 KB tile
+  const int within = (int)(d & 255);
+  const int lane = within >> 2, s = within & 3;
+  const int64_t cg = tile / KT, kt = tile - cg * KT;
+  const int64_t n = cg * kTileN + (lane & 15);
+  const int64_t k0 = kt * kTileK8 + 32 * s + 8 * (lane >> 4);
+  uint32_t word = 0;
+  if (n < N && k0 < K) {                      // K % 16 == 0: all 8 in range or none
+    const uint8_t* src = in + n * (K / 2) + k0 / 2;
+    word = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16) |
+           ((uint32_t)src[3] << 24);
+  }
+  out[d] = word;
+}
+
+// NVFP4 block scales: one thread per output word; word w of tile (cg, kt) is
+// column w / 2, half h = w % 2, bytes s = 0..3: block kt*8 + 2s + h.
+__global__ void prepack_nvfp4_scales_kernel(const uint8_t* __restrict__ in,
+                                            uint32_t* __restrict__ out, int64_t K, int64_t N,
+                                            int64_t KT, int64_t words) {
+  const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (d >= words) return;
+  const int64_t tile = d >> 5;                // 32 words per 128 B
+  const int w = (int)(d & 31);
+  const int c = w >> 1, h = w & 1;
+  const int64_t cg = tile / KT, kt = tile - cg * KT;
+  const int64_t n = cg * kTileN + c;
+  const int64_t blocks = K / 16;
+  uint32_t word = 0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int64_t b = kt * 8 + 2 * s + h;
+    const uint32_t e = (n < N && b < blocks) ? in[n * blocks + b] : 0u;
+    word |= e << (8 * s);
+  }
+  out[d] = word;
+}
+
 __global__ void zero_words_kernel(uint32_t* __restrict__ out, int64_t words) {
   const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (d < words) out[d] = 0u;
@@ -204,6 +249,24 @@ hipError_t launch_prepack(int fmt, const void* w, const void* w_scales, void* pa
       hipLaunchKernelGGL(prepack_mxfp4_scales_kernel, dim3(grid_for(swords, block)),
                          dim3(block), 0, stream, static_cast<const uint8_t*>(w_scales),
                          out + g.scales / 4, K, N, 2 * g.kt, swords);
+      break;
+    }
+    case 7: {
+      hipLaunchKernelGGL(prepack_nvfp4_codes_kernel, dim3(grid_for(words, block)), dim3(block),
+                         0, stream, in, out, K, N, g.kt, words);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t gap_words = (g.scales - g.codes) / 4;
+      if (gap_words > 0) {
+        hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, out + words,
+                           gap_words);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      const int64_t swords = (g.total - g.scales) / 4;
+      hipLaunchKernelGGL(prepack_nvfp4_scales_kernel, dim3(grid_for(swords, block)),
+                         dim3(block), 0, stream, static_cast<const uint8_t*>(w_scales),
+                         out + g.scales / 4, K, N, g.kt, swords);
       break;
     }
     default:

@@ -34,6 +34,14 @@
 //          (8 c8 + j) * 16 + (l & 15), block 4ks + (l >> 4).  A lane reads the
 //          scales of all 8 tiles of a step with one 8-byte load.
 //          Padding: code 0, scale 127 (= 1.0).
+//   NVFP4 (weight-only, format 7): TK = 128, 1 KB/tile like W4A16, but word s
+//          of lane l holds the 8 E2M1 codes k = kt*128 + 32s + 8g + [0, 8) in
+//          natural order (byte j: elements 2j low nibble, 2j+1 high), which
+//          is the order the gfx950 FP4 -> fp16 conversion consumes.  A block
+//          scale segment follows (256-byte aligned): 128 B per tile, byte
+//          c*8 + 4h + s = e4m3 scale of column c of the tile for the 16-element
+//          block kt*8 + 2s + h, so the lanes of group g read the dword
+//          c*8 + 4*(g >> 1).  Padding: code 0, scale 0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -78,7 +86,7 @@ struct PackGeom {
 inline PackGeom pack_geom(int fmt, int64_t K, int64_t N) {
   PackGeom g{};
   g.cg = cdiv(N, kTileN);
-  if (fmt == 1) {            // W4A16
+  if (fmt == 1 || fmt == 7) {  // W4A16, NVFP4 weights
     g.kt = cdiv(K, kTileK8);
     g.tile = kTileBytesW4;
   } else if (fmt == 3) {     // MXFP4
@@ -92,6 +100,9 @@ inline PackGeom pack_geom(int fmt, int64_t K, int64_t N) {
   if (fmt == 3) {
     g.scales = cdiv(g.codes, 256) * 256;
     g.total = g.scales + cdiv(g.cg, 8) * g.kt * 8 * kScaleTileBytes;
+  } else if (fmt == 7) {
+    g.scales = cdiv(g.codes, 256) * 256;
+    g.total = g.scales + g.cg * g.kt * kScaleTileBytes;
   } else {
     g.scales = 0;
     g.total = g.codes;
@@ -139,6 +150,11 @@ hipError_t launch_quantize_fp8(const float* x, int64_t count, uint8_t* codes, fl
 hipError_t launch_decode_gemm(int fmt, const void* x, const void* w_packed, const void* scales,
                               const float* scale_a, const float* scale_b, void* y,
                               int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// NVFP4 weights (format 7) with fp16 X: M rows in 16-row slabs;
+// global_scale is a device fp32 scalar.
+hipError_t launch_decode_nvfp4(const void* x, const void* w_packed, const float* global_scale,
+                               void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // Grouped W4A16 / W8A16 (formats 5, 6): M rows in 16-row slabs.
 hipError_t launch_decode_grouped(int fmt, const void* x, const void* w_packed, void* y,

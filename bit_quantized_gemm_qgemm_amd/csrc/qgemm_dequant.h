@@ -83,6 +83,22 @@ __device__ __forceinline__ half8_t dequant_w8_group(uint32_t lo, uint32_t hi, ui
   return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
+// NVFP4 weights: the 8 E2M1 codes of word q (natural order) times the e4m3
+// block scale in the low byte of sc8.  The hardware FP4 -> fp16 conversion
+// is exact at scale 1.0, and an E2M1 value (2 significant bits) times an
+// e4m3 value (4 significant bits, 2^-9 .. 448) is exact in fp16, so each
+// weight is e2m1 * scale exactly (the per-tensor scale multiplies the fp32
+// sum later).
+__device__ __forceinline__ half8_t dequant_nvfp4(uint32_t q, uint32_t sc8) {
+  const _Float16 sh = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)sc8, 0);
+  const half2_t sc = {sh, sh};
+  const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0) * sc;
+  const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1) * sc;
+  const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2) * sc;
+  const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3) * sc;
+  return half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+
 // Two biased INT8 bytes (w + 128) of a word, selected by `sel`, -> w as fp16.
 __device__ __forceinline__ half2_t dequant_w8_pair(uint32_t d, uint32_t sel) {
   // byte permute of {0x64646464 : d}: selector 0..3 picks bytes of d, 4 picks 0x64

@@ -46,15 +46,16 @@
 extern "C" {
 #endif
 
-/* Weight formats accepted by qgemm_prepack / qgemm_prepack_bytes (1-4) and
- * by qgemm_prepack_grouped / qgemm_prepack_grouped_bytes (5, 6). */
+/* Weight formats accepted by qgemm_prepack / qgemm_prepack_bytes (1-4, 7)
+ * and by qgemm_prepack_grouped / qgemm_prepack_grouped_bytes (5, 6). */
 enum qgemm_format {
   QGEMM_W4A16 = 1,
   QGEMM_W8A16 = 2,
   QGEMM_MXFP4 = 3,
   QGEMM_FP8 = 4,
   QGEMM_W4A16_GROUPED = 5,   /* INT4 codes, group-wise scales, zero points */
-  QGEMM_W8A16_GROUPED = 6    /* INT8 weights, group-wise scales, zero points */
+  QGEMM_W8A16_GROUPED = 6,   /* INT8 weights, group-wise scales, zero points */
+  QGEMM_NVFP4 = 7            /* E2M1 weights, e4m3 per-16 block scales      */
 };
 
 /* Status codes. */
@@ -99,6 +100,11 @@ int64_t qgemm_prepack_bytes(int fmt, int64_t K, int64_t N);
  *   fmt = QGEMM_FP8:   w = e4m3fn bytes B [K, N] (FP8 page kernel, B indexed
  *         by k then n).  K % 16 == 0.  w_scales NULL (the per-tensor scale
  *         goes to the GEMM).
+ *   fmt = QGEMM_NVFP4: w = uint8 E2M1 codes [N, K/2] (element 2j in the low
+ *         nibble of byte j), w_scales = uint8 e4m3fn block scales [N, K/16],
+ *         one per 16 consecutive K elements (W4A16 page, section 3: two-level
+ *         block scaling; the block size and scale format are this library's
+ *         reading).  K % 16 == 0.  NaN scale codes are not checked.
  *
  * w_packed must hold qgemm_prepack_bytes(fmt, K, N) bytes; the library fills
  * all of it (padding included).  The packed layout is private to the library
@@ -169,6 +175,18 @@ int qgemm_mxfp4(const void* a_codes, const void* a_e8m0, const void* w_packed,
 int qgemm_fp8(const void* a, const void* b_packed, const float* scale_a,
               const float* scale_b, void* c, int64_t M, int64_t N, int64_t K,
               void* stream);
+
+/*
+ * qgemm_nvfp4 -- Y[M,N] fp16 = X[M,K] fp16 * W_deq^T with
+ * W_deq[n,k] = e2m1(code[n,k]) * e4m3(scale[n, k/16]) * (*global_scale)
+ * (W4A16 page, section 3: NVFP4's two-level block scaling; the second level
+ * is the fp32 per-tensor scale, a device scalar).  Each weight is formed
+ * exactly in fp16 (an E2M1 value times an e4m3 value), the products
+ * accumulate in fp32 and the global scale multiplies the fp32 sum.
+ * w_packed from qgemm_prepack(QGEMM_NVFP4, ..., K, N).  K % 16 == 0.
+ */
+int qgemm_nvfp4(const void* x, const void* w_packed, const float* global_scale, void* y,
+                int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * Group-wise scales and asymmetric zero points (W4A16 page, section 1: the

@@ -39,7 +39,8 @@ def test_header_declares_the_expected_entry_points():
     for want in ("qgemm_w4a16", "qgemm_w8a16", "qgemm_mxfp4", "qgemm_fp8", "qgemm_prepack",
                  "qgemm_prepack_bytes", "qgemm_quantize_mxfp4", "qgemm_quantize_fp8",
                  "qgemm_status_string", "qgemm_abi_version", "qgemm_prepack_grouped",
-                 "qgemm_prepack_grouped_bytes", "qgemm_w4a16_grouped", "qgemm_w8a16_grouped"):
+                 "qgemm_prepack_grouped_bytes", "qgemm_w4a16_grouped", "qgemm_w8a16_grouped",
+                 "qgemm_nvfp4"):
         assert want in names
 
 
@@ -110,7 +111,8 @@ def test_gemm_argument_errors_need_no_device(lib):
 
 def test_prepack_and_quantize_argument_errors(lib):
     s = P(0)
-    assert lib.qgemm_prepack(7, GOOD, None, GOOD, 32, 32, s) == ERR_FORMAT
+    assert lib.qgemm_prepack(9, GOOD, None, GOOD, 32, 32, s) == ERR_FORMAT
+    assert lib.qgemm_prepack(5, GOOD, None, GOOD, 32, 32, s) == ERR_FORMAT   # grouped: own prepack
     assert lib.qgemm_prepack(1, GOOD, None, None, 32, 32, s) == ERR_NULL
     assert lib.qgemm_prepack(1, None, None, GOOD, 32, 32, s) == ERR_NULL
     assert lib.qgemm_prepack(3, GOOD, None, GOOD, 64, 32, s) == ERR_NULL   # MXFP4 needs scales
@@ -124,6 +126,20 @@ def test_prepack_and_quantize_argument_errors(lib):
     assert lib.qgemm_quantize_fp8(GOOD, 16, GOOD, None, s) == ERR_NULL
     assert lib.qgemm_quantize_fp8(GOOD, -1, GOOD, GOOD, s) == ERR_SHAPE
     assert lib.qgemm_quantize_fp8(GOOD, 16, GOOD, P(0x10001), s) == ERR_ALIGN
+
+
+def test_nvfp4_sizes_and_argument_errors(lib):
+    s = P(0)
+    # W4A16 code geometry (1 KB per 16 x 128 tile), then 128 B of block scales per tile
+    assert lib.qgemm_prepack_bytes(7, 8192, 28672) == 8192 * 28672 // 2 + 1792 * 64 * 128
+    assert lib.qgemm_prepack_bytes(7, 48, 20) == 2 * 1024 + 2 * 128
+    assert lib.qgemm_prepack_bytes(7, 40, 16) == ERR_SHAPE                   # K % 16
+    assert lib.qgemm_prepack(7, GOOD, None, GOOD, 64, 32, s) == ERR_NULL     # block scales
+    assert lib.qgemm_nvfp4(GOOD, GOOD, None, GOOD, 4, 16, 64, s) == ERR_NULL  # global scale
+    assert lib.qgemm_nvfp4(GOOD, GOOD, GOOD, GOOD, 4, 16, 72, s) == ERR_SHAPE
+    assert lib.qgemm_nvfp4(GOOD, GOOD, P(0x10002), GOOD, 4, 16, 64, s) == ERR_ALIGN
+    assert lib.qgemm_nvfp4(GOOD, ODD, GOOD, GOOD, 4, 16, 64, s) == ERR_ALIGN
+    assert lib.qgemm_nvfp4(GOOD, GOOD, GOOD, GOOD, 0, 16, 64, s) == OK
 
 
 def test_grouped_prepack_bytes(lib):
