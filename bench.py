@@ -60,6 +60,9 @@ WORKLOADS = {
     "w8a16_g128_decode": ("w8a16_grouped", (1, 4, 16), 11008, 4096),
     # NVFP4-style weights (e4m3 scale per 16 elements, fp32 per tensor), fp16 X
     "nvfp4_decode": ("nvfp4", (1, 8, 16), 28672, 8192),
+    # fp32 activations quantized on the device inside the call, then the GEMM
+    "fp8_act_decode": ("fp8_act", (16,), 8192, 8192),
+    "mxfp4_act_square": ("mxfp4_act", (8192,), 8192, 8192),
 }
 GROUP_K = 128   # group size of the grouped workloads
 DEFAULT_WORKLOAD = "w8a16_decode"
@@ -154,6 +157,45 @@ class Setup:
                 self.calls.append((lambda c, xm=xm, out=out: qg.qgemm_nvfp4(xm, self.copies[c], gs,
                                                                             n, out=out),
                                    alg, w_bytes, 2 * m * n * k))
+        elif fmt == "fp8_act":
+            a, b = wl.fp8_operands(mmax, n, k)
+            qb, sb = qg.qgemm_quantize_fp8(torch.from_numpy(b).to(dev))
+            del b
+            packed = qg.qgemm_prepack("fp8", qb, k, n)
+            del qb
+            a_d = torch.from_numpy(a).to(dev)
+            ws = torch.empty(qg.qgemm_act_workspace_bytes("fp8", mmax, k), dtype=torch.uint8,
+                             device=dev)
+            w_bytes = n * k
+            self.copies = self._rotate(packed, w_bytes)
+            self.dtype = "fp8"
+            out = torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
+            # fp32 A read by the quantizer (twice: amax, cast), codes written and
+            # read, B, C
+            alg = w_bytes + 8 * mmax * k + 2 * mmax * k + 2 * mmax * n
+            self.calls.append((lambda c: qg.qgemm_fp8_act(a_d, self.copies[c], sb, n, workspace=ws,
+                                                          out=out),
+                               alg, w_bytes, 2 * mmax * n * k))
+        elif fmt == "mxfp4_act":
+            a, w = wl.mxfp4_operands(mmax, n, k)
+            wc, we = qg.qgemm_quantize_mxfp4(torch.from_numpy(w).to(dev))
+            del w
+            packed = qg.qgemm_prepack("mxfp4", wc, k, n, w_scales=we)
+            del wc, we
+            a_d = torch.from_numpy(a).to(dev)
+            del a
+            ws = torch.empty(qg.qgemm_act_workspace_bytes("mxfp4", mmax, k), dtype=torch.uint8,
+                             device=dev)
+            w_bytes = n * k // 2 + n * k // 32
+            a_bytes = 4 * mmax * k
+            self.copies = self._rotate(packed, w_bytes + a_bytes)
+            self.a_copies = [a_d] + [a_d.clone() for _ in range(len(self.copies) - 1)]
+            self.dtype = "fp4"
+            out = torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
+            alg = w_bytes + a_bytes + (mmax * k // 2 + mmax * k // 32) * 2 + 2 * mmax * n
+            self.calls.append((lambda c: qg.qgemm_mxfp4_act(self.a_copies[c], self.copies[c], n,
+                                                            workspace=ws, out=out),
+                               alg, w_bytes, 2 * mmax * n * k))
         elif fmt == "mxfp4":
             a, w = wl.mxfp4_operands(mmax, n, k)
             ac, ae = qg.qgemm_quantize_mxfp4(torch.from_numpy(a).to(dev))
@@ -341,6 +383,22 @@ def cpu_baseline(name, budget_s=10.0):
         value = w_bytes_per_step * done / dt / 1e9
         sample = (f"oracle {fmt} steps (M={list(ms)}), K={k}, {cols} of {n} columns, "
                   f"{done} steps in {dt:.1f} s")
+    elif fmt == "fp8_act":
+        # quantize the whole A with the oracle, then the GEMM against a column slice
+        cols = 512
+        a, b = wl.fp8_operands(mmax, n, k)
+        qb, sb = oracle.fp8_quantize(b[:, :cols])
+        unit, done, t0 = "GB/s", 0, time.perf_counter()
+        while True:
+            qa, sa = oracle.fp8_quantize(a)
+            oracle.gemm_fp8(qa, qb, sa, sb)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+        value = k * cols * done / dt / 1e9
+        sample = (f"oracle fp8 quantize of A [{mmax}, {k}] + GEMM against {cols} of {n} columns, "
+                  f"{done} runs in {dt:.1f} s")
     else:
         # bounded sample: 256 rows of X / A against the whole weight
         rows = 256
@@ -350,11 +408,16 @@ def cpu_baseline(name, budget_s=10.0):
             gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16
             x, w, s = gen(rows, k, n)
             run = lambda: gemm(x, w, s)  # noqa: E731
-        elif fmt == "mxfp4":
+        elif fmt in ("mxfp4", "mxfp4_act"):
             a, w = wl.mxfp4_operands(rows, n, k)
             ac, ae = oracle.mxfp4_quantize(a)
             wc, we = oracle.mxfp4_quantize(w)
-            run = lambda: oracle.gemm_mxfp4(ac, ae, wc, we)  # noqa: E731
+            if fmt == "mxfp4_act":   # the activation quantizer is part of each run
+                def run():
+                    c_, e_ = oracle.mxfp4_quantize(a)
+                    return oracle.gemm_mxfp4(c_, e_, wc, we)
+            else:
+                run = lambda: oracle.gemm_mxfp4(ac, ae, wc, we)  # noqa: E731
         else:
             a, b = wl.fp8_operands(rows, n, k)
             qa, sa = oracle.fp8_quantize(a)
@@ -461,6 +524,12 @@ def run(name, steps, warmup, with_cpu, use_graph):
 def kernel_name(setup, m):
     """Label of the kernel that runs a call with M rows (rocprofv3 lists the
     mangled template instance)."""
+    if setup.fmt == "fp8_act":
+        return (f"qgemm_fp8_act call: quantize kernels + decode_gemm_kernel[fp8, M={m}, "
+                f"N={setup.n}, K={setup.k}]")
+    if setup.fmt == "mxfp4_act":
+        return (f"qgemm_mxfp4_act call: quantize_mxfp4_kernel + pipe256_kernel[mxfp4, M={m}, "
+                f"N={setup.n}, K={setup.k}]")
     if setup.kind == "decode":
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     # same rules as the library's dispatch

@@ -46,6 +46,9 @@ _SIGNATURES = [
     ("qgemm_w4a16_grouped", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     ("qgemm_w8a16_grouped", ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     ("qgemm_nvfp4", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    ("qgemm_act_workspace_bytes", ctypes.c_int64, [ctypes.c_int, _I64, _I64]),
+    ("qgemm_mxfp4_act", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    ("qgemm_fp8_act", ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
 ]
 
 _lib = None
@@ -330,3 +333,61 @@ def qgemm_nvfp4(x, w_packed, global_scale, N, out=None):
     _check(lib().qgemm_nvfp4(_ptr(x), _ptr(w_packed), _ptr(global_scale), _ptr(out), M, N, K,
                              _stream(x)), "qgemm_nvfp4")
     return out
+
+
+def qgemm_act_workspace_bytes(fmt, M, K):
+    n = lib().qgemm_act_workspace_bytes(int(FORMATS.get(fmt, fmt)), int(M), int(K))
+    if n < 0:
+        raise QgemmError(int(n), "qgemm_act_workspace_bytes")
+    return int(n)
+
+
+def _act_workspace(fmt, a, workspace):
+    M, K = a.shape
+    need = qgemm_act_workspace_bytes(fmt, M, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    else:
+        _need(workspace, torch.uint8, 1, "workspace")
+        if workspace.numel() < need:
+            raise ValueError(f"workspace needs {need} bytes")
+    return workspace
+
+
+def qgemm_mxfp4_act(a, w_packed, N, workspace=None, out=None):
+    """fp32 A [M, K] -> MXFP4 on the device, then C = A_deq @ W_deq^T (bf16).
+    Returns (C, workspace); the workspace holds the quantized A."""
+    _need(a, torch.float32, 2, "a")
+    _need(w_packed, torch.uint8, 1, "w_packed")
+    M, K = a.shape
+    if w_packed.numel() < qgemm_prepack_bytes(QGEMM_MXFP4, K, N):
+        raise ValueError("w_packed is smaller than the packed size for this K, N")
+    workspace = _act_workspace(QGEMM_MXFP4, a, workspace)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    else:
+        _need(out, torch.bfloat16, 2, "out")
+    _check(lib().qgemm_mxfp4_act(_ptr(a), _ptr(w_packed), _ptr(out), _ptr(workspace), M, N, K,
+                                 _stream(a)), "qgemm_mxfp4_act")
+    return out, workspace
+
+
+def qgemm_fp8_act(a, b_packed, scale_b, N, workspace=None, out=None):
+    """fp32 A [M, K] -> per-tensor e4m3fn on the device, then C = (A_q @ B) *
+    s_a * s_b (bf16).  Returns (C, workspace); the workspace holds the codes
+    and, at round_up(M*K, 16), the fp32 scale."""
+    _need(a, torch.float32, 2, "a")
+    _need(b_packed, torch.uint8, 1, "b_packed")
+    if scale_b.dtype != torch.float32 or not scale_b.is_cuda or scale_b.numel() != 1:
+        raise TypeError("scale_b must be a one-element float32 device tensor")
+    M, K = a.shape
+    if b_packed.numel() < qgemm_prepack_bytes(QGEMM_FP8, K, N):
+        raise ValueError("b_packed is smaller than the packed size for this K, N")
+    workspace = _act_workspace(QGEMM_FP8, a, workspace)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    else:
+        _need(out, torch.bfloat16, 2, "out")
+    _check(lib().qgemm_fp8_act(_ptr(a), _ptr(b_packed), _ptr(scale_b), _ptr(out), _ptr(workspace),
+                               M, N, K, _stream(a)), "qgemm_fp8_act")
+    return out, workspace

@@ -276,4 +276,60 @@ int qgemm_fp8(const void* a, const void* b_packed, const float* scale_a, const f
                                           N, K, as_stream(stream)));
 }
 
+// ---- activation quantization enqueued before the GEMM ----------------------
+
+int64_t qgemm_act_workspace_bytes(int fmt, int64_t M, int64_t K) {
+  if (fmt != QGEMM_MXFP4 && fmt != QGEMM_FP8) return QGEMM_ERR_FORMAT;
+  if (M < 0 || K < 0 || !k_ok(fmt, K)) return QGEMM_ERR_SHAPE;
+  if (M >= kMaxIndex || K >= kMaxIndex || M * K >= kMaxIndex * 2) return QGEMM_ERR_SHAPE;
+  if (fmt == QGEMM_MXFP4) return qgemm::cdiv(M * K / 2, 16) * 16 + M * (K / 32);
+  return qgemm::cdiv(M * K, 16) * 16 + 16;
+}
+
+int qgemm_mxfp4_act(const float* a, const void* w_packed, void* c, void* workspace, int64_t M,
+                    int64_t N, int64_t K, void* stream) {
+  int st = check_sizes(QGEMM_MXFP4, M, N, K);
+  if (st != QGEMM_OK) return st;
+  if (!present(a, M * K) || !present(w_packed, K * N) || !present(c, M * N) ||
+      !present(workspace, M * K))
+    return QGEMM_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(c, 16) || !aligned(workspace, 16))
+    return QGEMM_ERR_ALIGN;
+  if (M == 0) return QGEMM_OK;
+  if ((st = check_device()) != QGEMM_OK) return st;
+  uint8_t* codes = static_cast<uint8_t*>(workspace);
+  uint8_t* e8m0 = codes + qgemm::cdiv(M * K / 2, 16) * 16;
+  if (K > 0) {
+    st = launched(qgemm::launch_quantize_mxfp4(a, M, K, codes, e8m0, as_stream(stream)));
+    if (st != QGEMM_OK) return st;
+  }
+  if (N == 0) return QGEMM_OK;
+  return launched(qgemm::launch_tile_gemm(QGEMM_MXFP4, codes, e8m0, w_packed, nullptr, nullptr, c,
+                                          M, N, K, as_stream(stream)));
+}
+
+int qgemm_fp8_act(const float* a, const void* b_packed, const float* scale_b, void* c,
+                  void* workspace, int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_sizes(QGEMM_FP8, M, N, K);
+  if (st != QGEMM_OK) return st;
+  if (!present(a, M * K) || !present(b_packed, K * N) || !present(c, M * N) || !scale_b ||
+      !workspace)
+    return QGEMM_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b_packed, 16) || !aligned(c, 16) || !aligned(workspace, 16) ||
+      !aligned(scale_b, 4))
+    return QGEMM_ERR_ALIGN;
+  if (M == 0) return QGEMM_OK;
+  if ((st = check_device()) != QGEMM_OK) return st;
+  uint8_t* codes = static_cast<uint8_t*>(workspace);
+  float* scale_a = reinterpret_cast<float*>(codes + qgemm::cdiv(M * K, 16) * 16);
+  // an empty A still gets its scale (1.0, the all-zero rule)
+  st = launched(qgemm::launch_quantize_fp8(a, M * K, codes, scale_a, as_stream(stream)));
+  if (st != QGEMM_OK || N == 0) return st;
+  if (M <= kDecodeMaxM)
+    return launched(qgemm::launch_decode_gemm(QGEMM_FP8, codes, b_packed, nullptr, scale_a,
+                                              scale_b, c, M, N, K, as_stream(stream)));
+  return launched(qgemm::launch_tile_gemm(QGEMM_FP8, codes, nullptr, b_packed, scale_a, scale_b,
+                                          c, M, N, K, as_stream(stream)));
+}
+
 }  // extern "C"

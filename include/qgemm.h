@@ -177,6 +177,34 @@ int qgemm_fp8(const void* a, const void* b_packed, const float* scale_a,
               void* stream);
 
 /*
+ * Activation quantization enqueued before the GEMM, on the same stream and
+ * without a host round trip (MXFP4 page, section 3: per-32 E8M0 quantization
+ * of A; FP8 page: per-tensor amax scaling and e4m3fn cast of A).  The caller
+ * passes fp32 activations and a device workspace of
+ * qgemm_act_workspace_bytes(fmt, M, K) bytes (16-byte aligned), which after
+ * the call (in stream order) holds the quantized A exactly as
+ * qgemm_quantize_mxfp4 / qgemm_quantize_fp8 produce it:
+ *   MXFP4: codes [M, K/2] at offset 0, E8M0 [M, K/32] at round_up(M*K/2, 16);
+ *   FP8:   e4m3fn codes [M, K] at offset 0, the fp32 scale at
+ *          round_up(M*K, 16).
+ * The result equals quantizing with those entry points and calling
+ * qgemm_mxfp4 / qgemm_fp8 on the quantized A (bit for bit).  The library
+ * allocates nothing.  Calls that share a workspace must not overlap.
+ *
+ * qgemm_act_workspace_bytes -- fmt QGEMM_MXFP4 or QGEMM_FP8; < 0 on bad
+ * arguments.  Host-only.
+ */
+int64_t qgemm_act_workspace_bytes(int fmt, int64_t M, int64_t K);
+
+/* C[M,N] bf16 = MXFP4(a)[M,K] * W_deq^T, a fp32 [M, K]; K % 32 == 0. */
+int qgemm_mxfp4_act(const float* a, const void* w_packed, void* c, void* workspace, int64_t M,
+                    int64_t N, int64_t K, void* stream);
+
+/* C[M,N] bf16 = (FP8(a) * B) * s_a * (*scale_b), a fp32 [M, K]; K % 16 == 0. */
+int qgemm_fp8_act(const float* a, const void* b_packed, const float* scale_b, void* c,
+                  void* workspace, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * qgemm_nvfp4 -- Y[M,N] fp16 = X[M,K] fp16 * W_deq^T with
  * W_deq[n,k] = e2m1(code[n,k]) * e4m3(scale[n, k/16]) * (*global_scale)
  * (W4A16 page, section 3: NVFP4's two-level block scaling; the second level

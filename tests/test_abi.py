@@ -40,7 +40,8 @@ def test_header_declares_the_expected_entry_points():
                  "qgemm_prepack_bytes", "qgemm_quantize_mxfp4", "qgemm_quantize_fp8",
                  "qgemm_status_string", "qgemm_abi_version", "qgemm_prepack_grouped",
                  "qgemm_prepack_grouped_bytes", "qgemm_w4a16_grouped", "qgemm_w8a16_grouped",
-                 "qgemm_nvfp4"):
+                 "qgemm_nvfp4", "qgemm_act_workspace_bytes", "qgemm_mxfp4_act",
+                 "qgemm_fp8_act"):
         assert want in names
 
 
@@ -140,6 +141,24 @@ def test_nvfp4_sizes_and_argument_errors(lib):
     assert lib.qgemm_nvfp4(GOOD, GOOD, P(0x10002), GOOD, 4, 16, 64, s) == ERR_ALIGN
     assert lib.qgemm_nvfp4(GOOD, ODD, GOOD, GOOD, 4, 16, 64, s) == ERR_ALIGN
     assert lib.qgemm_nvfp4(GOOD, GOOD, GOOD, GOOD, 0, 16, 64, s) == OK
+
+
+def test_act_workspace_and_argument_errors(lib):
+    s = P(0)
+    assert lib.qgemm_act_workspace_bytes(3, 16, 8192) == 16 * 8192 // 2 + 16 * 256
+    assert lib.qgemm_act_workspace_bytes(3, 3, 96) == 144 + 9      # codes rounded to 16
+    assert lib.qgemm_act_workspace_bytes(4, 16, 8192) == 16 * 8192 + 16
+    assert lib.qgemm_act_workspace_bytes(4, 3, 16) == 48 + 16
+    assert lib.qgemm_act_workspace_bytes(1, 16, 64) == ERR_FORMAT
+    assert lib.qgemm_act_workspace_bytes(3, 16, 48) == ERR_SHAPE
+    assert lib.qgemm_mxfp4_act(GOOD, GOOD, GOOD, None, 4, 16, 64, s) == ERR_NULL
+    assert lib.qgemm_mxfp4_act(GOOD, GOOD, GOOD, ODD, 4, 16, 64, s) == ERR_ALIGN
+    assert lib.qgemm_mxfp4_act(GOOD, GOOD, GOOD, GOOD, 4, 16, 48, s) == ERR_SHAPE
+    assert lib.qgemm_mxfp4_act(GOOD, GOOD, GOOD, GOOD, 0, 16, 64, s) == OK
+    assert lib.qgemm_fp8_act(GOOD, GOOD, None, GOOD, GOOD, 4, 16, 64, s) == ERR_NULL
+    assert lib.qgemm_fp8_act(GOOD, GOOD, GOOD, GOOD, None, 4, 16, 64, s) == ERR_NULL
+    assert lib.qgemm_fp8_act(GOOD, GOOD, GOOD, GOOD, GOOD, 4, 16, 40, s) == ERR_SHAPE
+    assert lib.qgemm_fp8_act(GOOD, GOOD, GOOD, GOOD, GOOD, 0, 16, 64, s) == OK
 
 
 def test_grouped_prepack_bytes(lib):
