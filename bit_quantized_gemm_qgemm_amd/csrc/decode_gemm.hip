@@ -297,24 +297,20 @@ struct DecodeConfig {
   int d;   // K tiles in flight per wave
 };
 
-// Launch shape by format and M (per 16-row slab), from measurements on
-// MI355X at the decode workloads (W8A16 K=4096 N=11008, W4A16 K=8192
-// N=28672, FP8 K=N=8192): with one or a few rows, more workgroups (small G)
-// stream the weight fastest; with 16 rows each X fragment is worth reusing
-// across more columns (large G), which cuts X traffic from L2 (it scales as
-// X bytes * N / (16 G)).  G then shrinks until at least 128 workgroups exist,
-// and short K uses four waves.
+// Launch shape: about one workgroup per CU.  Measured on MI355X at the decode
+// workloads (W8A16 K=4096 N=11008, W4A16 K=8192 N=28672, FP8 K=N=8192, M = 1
+// .. 16): the weight streams fastest when the grid has close to 256
+// workgroups, each owning G = ceil(column groups / 256) column groups; more,
+// smaller workgroups leave the CUs unevenly loaded and fewer leave CUs idle.
+// G is capped by the register budget (8 for INT4, 4 for the byte formats);
+// INT8 keeps three K tiles in flight, the others two; short K uses four
+// waves.
 DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
-  const int64_t rows = M < 16 ? M : 16;
-  DecodeConfig c{2, 8, 2};
-  if (fmt == 1) {
-    c = rows <= 4 ? DecodeConfig{2, 8, 2} : rows <= 8 ? DecodeConfig{4, 4, 2} : DecodeConfig{8, 8, 3};
-  } else if (fmt == 2) {
-    c = rows <= 4 ? DecodeConfig{1, 8, 2} : DecodeConfig{4, 8, 3};
-  } else {
-    c = DecodeConfig{2, 8, 2};
-  }
-  while (c.g > 1 && cdiv(CG, c.g) < 128) c.g /= 2;
+  (void)M;
+  const int64_t gmax = fmt == 1 ? 8 : 4;
+  int64_t g = cdiv(CG, 256);
+  g = g < 1 ? 1 : (g > gmax ? gmax : g);
+  DecodeConfig c{(int)g, 8, fmt == 2 ? 3 : 2};
   if (KT < 16) c.nw = 4;
   return c;
 }
@@ -342,15 +338,12 @@ hipError_t launch_fmt_cfg(const DecodeConfig& c, const void* x, const void* w, c
 #define QG_CASE(GG, WW, DD)                                                                 \
   if (c.g == GG && c.nw == WW && c.d == DD)                                                 \
     return launch_cfg<FMT, GG, WW, DD, false>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream);
-#define QG_G(GG) QG_CASE(GG, 4, 2) QG_CASE(GG, 8, 2) QG_CASE(GG, 4, 3) QG_CASE(GG, 8, 3)
-  QG_G(1) QG_G(2) QG_G(4)
-  if constexpr (FMT == 1) {   // eight groups only pay off (and fit in registers) for INT4
-    QG_G(8)
+#define QG_G(GG) QG_CASE(GG, 8, DEPTH) QG_CASE(GG, 4, DEPTH)
+  constexpr int DEPTH = FMT == 2 ? 3 : 2;
+  QG_G(1) QG_G(2) QG_G(3) QG_G(4)
+  if constexpr (FMT == 1) {   // up to eight INT4 column groups fit in registers
+    QG_G(5) QG_G(6) QG_G(7) QG_G(8)
   }
-#ifdef QGEMM_DECODE_SWEEP
-  QG_CASE(1, 4, 4) QG_CASE(1, 8, 4) QG_CASE(2, 4, 4) QG_CASE(2, 8, 4) QG_CASE(4, 4, 4)
-  QG_CASE(4, 8, 4) QG_CASE(1, 16, 2) QG_CASE(2, 16, 2) QG_CASE(1, 16, 3) QG_CASE(2, 16, 3)
-#endif
 #undef QG_G
 #undef QG_CASE
   return hipErrorInvalidValue;
@@ -363,6 +356,17 @@ hipError_t launch_fmt(const void* x, const void* w, const void* s, const float* 
   const PackGeom pg = pack_geom(FMT, K, N);
   const DecodeConfig c = pick_decode_config(FMT, M, pg.cg, pg.kt);
   return launch_fmt_cfg<FMT>(c, x, w, s, sa, sb, y, M, N, K, pg.kt, pg.cg, stream);
+}
+
+// Column groups per workgroup for the grouped and NVFP4 launches: the same
+// one-workgroup-per-CU rule, rounded down to an instantiated value (1, 2, 3,
+// 4, or 7 where gmax allows it); short K (four waves) uses 1 or 2.
+int slab_groups(int64_t CG, int gmax, int64_t KT) {
+  int64_t g = cdiv(CG, 256);
+  if (KT < 16) return g >= 2 ? 2 : 1;
+  if (g >= 7 && gmax >= 7) return 7;
+  g = g < 1 ? 1 : (g > 4 ? 4 : g);
+  return (int)g;
 }
 
 // Grouped formats: the same kernel with NGT metadata words per column and K
@@ -384,14 +388,15 @@ template <int FMT, int NGT>
 hipError_t launch_grouped_ngt(const void* x, const void* w, void* y, int64_t M, int64_t N,
                               int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
                               hipStream_t stream) {
-  const int64_t rows = M < 16 ? M : 16;
-  int g = rows <= 4 ? (FMT == 1 ? 2 : 1) : 4;
-  while (g > 1 && cdiv(CG, g) < 128) g /= 2;
+  const int g = slab_groups(CG, FMT == 1 ? 7 : 4, KT);
   const int nw = KT < 16 ? 4 : 8;
 #define QG_GCASE(GG, WW)                                                                   \
   if (g == GG && nw == WW)                                                                 \
     return launch_grouped_cfg<FMT, NGT, GG, WW>(x, w, y, M, N, K, KT, CG, meta_offset, stream);
-  QG_GCASE(1, 4) QG_GCASE(1, 8) QG_GCASE(2, 4) QG_GCASE(2, 8) QG_GCASE(4, 4) QG_GCASE(4, 8)
+  QG_GCASE(1, 4) QG_GCASE(1, 8) QG_GCASE(2, 4) QG_GCASE(2, 8) QG_GCASE(3, 8) QG_GCASE(4, 8)
+  if constexpr (FMT == 1) {
+    QG_GCASE(7, 8)
+  }
 #undef QG_GCASE
   return hipErrorInvalidValue;
 }
@@ -425,15 +430,14 @@ hipError_t launch_nvfp4_cfg(const void* x, const void* w, const float* gs, void*
 hipError_t launch_decode_nvfp4(const void* x, const void* w_packed, const float* global_scale,
                                void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const PackGeom pg = pack_geom(7, K, N);
-  const int64_t rows = M < 16 ? M : 16;
-  int g = rows <= 4 ? 2 : 4;
-  while (g > 1 && cdiv(pg.cg, g) < 128) g /= 2;
+  const int g = slab_groups(pg.cg, 7, pg.kt);
   const int nw = pg.kt < 16 ? 4 : 8;
 #define QG_NCASE(GG, WW)                                                                   \
   if (g == GG && nw == WW)                                                                 \
     return launch_nvfp4_cfg<GG, WW>(x, w_packed, global_scale, y, M, N, K, pg.kt, pg.cg,   \
                                     pg.scales, stream);
-  QG_NCASE(1, 4) QG_NCASE(1, 8) QG_NCASE(2, 4) QG_NCASE(2, 8) QG_NCASE(4, 4) QG_NCASE(4, 8)
+  QG_NCASE(1, 4) QG_NCASE(1, 8) QG_NCASE(2, 4) QG_NCASE(2, 8) QG_NCASE(3, 8) QG_NCASE(4, 8)
+  QG_NCASE(7, 8)
 #undef QG_NCASE
   return hipErrorInvalidValue;
 }
