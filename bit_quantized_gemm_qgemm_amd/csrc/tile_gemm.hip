@@ -365,27 +365,68 @@ __device__ __forceinline__ int a16_lane_offset(int wm, int lane, int swz) {
   return r * kStepBytes + 16 * ((lane >> 4) ^ swz);
 }
 
+// ---- epilogue: the 256 x 256 output tile goes through LDS -----------------
+// Each lane rounds its scaled accumulators (hardware RNE conversion) into a
+// row-major [256][512 B] tile in LDS; then the workgroup copies it out with
+// 16-byte row-contiguous stores.  16-byte chunk k of row r sits in slot
+// k ^ (((r >> 2) & 3) << 2): the rows that one 2-byte write instruction
+// touches (4 apart for 16 x 16 fragments, 4 apart for 32 x 32) land in
+// different banks.
+constexpr int kCTileBytes = kBig * kBig * 2;
+
+__device__ __forceinline__ int c_tile_offset(int row, int col) {
+  return row * (kBig * 2) + 16 * ((col >> 3) ^ (((row >> 2) & 3) << 2)) + 2 * (col & 7);
+}
+
+template <bool F16_OUT>
+__device__ __forceinline__ uint16_t round_out(float v) {
+  if constexpr (F16_OUT) return f32_to_f16_bits(v);
+  else return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
 // 16 x 16 accumulators: lane holds rows 4 (lane >> 4) + i, column lane & 15.
 template <bool F16_OUT>
-__device__ __forceinline__ void store16(const floatx4 (&acc)[8][8], const PipeOut& o, int m0,
+__device__ __forceinline__ void stage16(const floatx4 (&acc)[8][8], uint8_t* ct, const PipeOut& o,
                                         int n0, int wm, int wn, int lane) {
 #pragma unroll
   for (int fn = 0; fn < 8; ++fn) {
-    const int gn = n0 + wn * 128 + fn * 16 + (lane & 15);
+    const int col = wn * 128 + fn * 16 + (lane & 15);
     float s = o.s;
     if constexpr (F16_OUT) {
-      const int sn = gn < o.N ? gn : o.N - 1;
-      s = (float)__builtin_bit_cast(_Float16, o.col_scale[sn]);
+      const int gn = n0 + col;
+      s = (float)__builtin_bit_cast(_Float16, o.col_scale[gn < o.N ? gn : o.N - 1]);
     }
 #pragma unroll
     for (int fm = 0; fm < 8; ++fm)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int gm = m0 + wm * 128 + fm * 16 + 4 * (lane >> 4) + i;
-        if (gm < o.M && gn < o.N)
-          o.c[(int64_t)gm * o.N + gn] =
-              F16_OUT ? f32_to_f16_bits(acc[fm][fn][i] * s) : f32_to_bf16_rne(acc[fm][fn][i] * s);
+        const int row = wm * 128 + fm * 16 + 4 * (lane >> 4) + i;
+        *reinterpret_cast<uint16_t*>(ct + c_tile_offset(row, col)) =
+            round_out<F16_OUT>(acc[fm][fn][i] * s);
       }
+  }
+}
+
+// Copy the staged tile to C (rows past M and columns past N are dropped).
+__device__ __forceinline__ void pipe_copy_out(const uint8_t* ct, const PipeOut& o, int m0,
+                                              int n0) {
+  const bool vec = (o.N & 7) == 0;
+#pragma unroll 4
+  for (int j = 0; j < kCTileBytes / 16 / kThreads; ++j) {
+    const int q = (int)threadIdx.x + kThreads * j;
+    const int row = q >> 5, ch = q & 31;
+    const int gm = m0 + row, gn = n0 + 8 * ch;
+    if (gm >= o.M || gn >= o.N) continue;
+    const uintx4 v =
+        *reinterpret_cast<const uintx4*>(ct + row * (kBig * 2) + 16 * (ch ^ (((row >> 2) & 3) << 2)));
+    uint16_t* dst = o.c + (int64_t)gm * o.N + gn;
+    if (vec) {
+      *reinterpret_cast<uintx4*>(dst) = v;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (gn + t < o.N) dst[t] = (uint16_t)(v[t >> 1] >> (16 * (t & 1)));
+    }
   }
 }
 
@@ -469,9 +510,9 @@ struct Fp4Pipe {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  __device__ __forceinline__ static void store(const Acc& acc, const PipeOut& o, int m0, int n0,
-                                               int wm, int wn, int lane) {
-    store16<false>(acc, o, m0, n0, wm, wn, lane);
+  __device__ __forceinline__ static void stage(const Acc& acc, uint8_t* ct, const PipeOut& o,
+                                               int n0, int wm, int wn, int lane) {
+    stage16<false>(acc, ct, o, n0, wm, wn, lane);
   }
 };
 
@@ -549,18 +590,18 @@ struct Fp8Pipe {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   }
   // lane holds rows 8 (e >> 2) + 4 (lane >> 5) + (e & 3), column lane & 31
-  __device__ __forceinline__ static void store(const Acc& acc, const PipeOut& o, int m0, int n0,
-                                               int wm, int wn, int lane) {
+  __device__ __forceinline__ static void stage(const Acc& acc, uint8_t* ct, const PipeOut& o,
+                                               int, int wm, int wn, int lane) {
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
       for (int fn = 0; fn < 4; ++fn) {
-        const int gn = n0 + wn * 128 + fn * 32 + (lane & 31);
+        const int col = wn * 128 + fn * 32 + (lane & 31);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int gm = m0 + wm * 128 + fm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          if (gm < o.M && gn < o.N)
-            o.c[(int64_t)gm * o.N + gn] = f32_to_bf16_rne(acc[fm][fn][e] * o.s);
+          const int row = wm * 128 + fm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          *reinterpret_cast<uint16_t*>(ct + c_tile_offset(row, col)) =
+              round_out<false>(acc[fm][fn][e] * o.s);
         }
       }
   }
@@ -645,9 +686,9 @@ struct F16Pipe {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  __device__ __forceinline__ static void store(const Acc& acc, const PipeOut& o, int m0, int n0,
-                                               int wm, int wn, int lane) {
-    store16<true>(acc, o, m0, n0, wm, wn, lane);
+  __device__ __forceinline__ static void stage(const Acc& acc, uint8_t* ct, const PipeOut& o,
+                                               int n0, int wm, int wn, int lane) {
+    stage16<true>(acc, ct, o, n0, wm, wn, lane);
   }
 };
 
@@ -721,7 +762,8 @@ __global__ __launch_bounds__(kThreads) void pipe256_kernel(
     const uint16_t* __restrict__ col_scale, uint16_t* __restrict__ c, PipeArgs g) {
   constexpr int PER = Ops::DMA;
   static_assert(NST % 2 == 0 && NST >= 4, "stage ring");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * Ops::STAGE];
+  constexpr int LDS_BYTES = NST * Ops::STAGE > kCTileBytes ? NST * Ops::STAGE : kCTileBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1;
@@ -792,7 +834,10 @@ __global__ __launch_bounds__(kThreads) void pipe256_kernel(
   o.s = (Ops::FMT == 4) ? (*scale_a) * (*scale_b) : 1.0f;
   o.M = g.M;
   o.N = g.N;
-  Ops::store(acc, o, m0, cg0 * 16, wm, wn, lane);
+  __syncthreads();   // every wave has finished with the last stage
+  Ops::stage(acc, smem, o, cg0 * 16, wm, wn, lane);
+  __syncthreads();
+  pipe_copy_out(smem, o, m0, cg0 * 16);
 }
 
 // a_sc: MXFP4 activation scales; col_scale: W4A16/W8A16 column scales;
