@@ -430,29 +430,55 @@ __device__ __forceinline__ void pipe_copy_out(const uint8_t* ct, const PipeOut& 
   }
 }
 
-// MXFP4: 8 x 8 fragments of 16 x 16 per wave; one step = 128 K elements =
-// one v_mfma_scale_f32_16x16x128_f8f6f4 per fragment pair.
-// Stage: A | W 16 tiles x 1 KB (half h of each tile as is) | A scales
-// [256 rows][4 blocks] | W scales [wn 2][lane 64][tile 8].
+// 32 x 32 accumulator layout of v_mfma_*_32x32x*: lane holds rows
+// 8 (e >> 2) + 4 (lane >> 5) + (e & 3) of its fragment, column lane & 31.
+__device__ __forceinline__ void stage32(const floatx16 (&acc)[4][4], uint8_t* ct,
+                                        const PipeOut& o, int wm, int wn, int lane) {
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn) {
+      const int col = wn * 128 + fn * 32 + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = wm * 128 + fm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        *reinterpret_cast<uint16_t*>(ct + c_tile_offset(row, col)) =
+            round_out<false>(acc[fm][fn][e] * o.s);
+      }
+    }
+}
+
+// MXFP4: 4 x 4 fragments of 32 x 32 per wave; one step = 128 K elements =
+// two v_mfma_scale_f32_32x32x64_f8f6f4 per fragment pair (the 32 x 32 x 64
+// form keeps the matrix pipe fuller than 16 x 16 x 128 on FP4 operands).
+// Lane l feeds row (or column) l & 31 with the 32 contiguous bytes 32 j + [0,
+// 32) of the step (j = l >> 5), i.e. 32-element blocks 2j and 2j + 1; half h
+// of the pair multiplies block 2j + h.  Both operands use this K order, and
+// each lane's scale byte for half h is block 2j + h of its row or column: the
+// lane shifts its scale word so that one byte select serves all lanes.
+// Stage: A | W 16 tiles x 1 KB (half h of each tile as is: [kg 4][column
+// 16][16 B]) | A scales [256 rows][4 blocks] | W scales [wn 2][lane 64][tile
+// 8] (lane = column + 16 kg).
 struct Fp4Pipe {
   static constexpr int FMT = 3;
-  static constexpr int PARTS = 8;
+  static constexpr int PARTS = 4;
   static constexpr int STEPS_PER_TILE = 2;
   static constexpr int B = 16 * 1024, SA = kBig * 4, SB = 2 * 512;
   static constexpr int STAGE = kStageA + B + SA + SB;
   static constexpr int DMA = 10;
   static constexpr int NST = 4;                  // 4 x 34 KB of LDS
-  typedef floatx4 Acc[8][8];
+  typedef floatx16 Acc[4][4];
   struct Frags {
-    uintx4 a[8];
-    uintx4 b[8];
-    uint32_t sa[8];
-    uintx2 sb;
+    uintx4 alo[4], ahi[4];
+    uintx4 blo[4], bhi[4];
+    uint32_t sa[4];   // row scale words, shifted so byte h is block 2j + h
+    uintx2 sb[2];     // [h] column scale words of tiles 0-3 and 4-7, shifted
   };
   struct Lane {
-    int a, sa, b, sb;
+    int alo, ahi, sa, b, sb;
+    uint32_t sha, shb;
   };
-  __device__ __forceinline__ static int swizzle(int r) { return (r >> 1) & 3; }
+  __device__ __forceinline__ static int swizzle(int r) { return (r >> 2) & 3; }
   __device__ __forceinline__ static int row_bytes(int K) { return K / 2; }
   __device__ __forceinline__ static void issue_rest(uint8_t* st, int ks, int wave, int lane,
                                                     int m0, int cg0, const PipeArgs& g,
@@ -475,44 +501,60 @@ struct Fp4Pipe {
     dma4(rs.sw, st + kStageA + B + SA + 256 * wave, soff);
   }
   __device__ __forceinline__ static Lane lane_offsets(int wm, int wn, int lane) {
-    const int r = wm * 128 + (lane & 15);
+    const int r = wm * 128 + (lane & 31), j = lane >> 5, swz = swizzle(r);
+    const int par = (lane >> 4) & 1;   // column tile 2P + par of fragment P
     Lane L;
-    L.a = a16_lane_offset(wm, lane, swizzle(r));
-    L.sa = kStageA + B + r * 4 + (lane >> 4);
-    L.b = kStageA + wn * 8 * 1024 + 16 * lane;
-    L.sb = kStageA + B + SA + wn * 512 + 8 * lane;
+    L.alo = r * kStepBytes + 16 * ((2 * j) ^ swz);
+    L.ahi = r * kStepBytes + 16 * ((2 * j + 1) ^ swz);
+    L.sa = kStageA + B + 4 * r;
+    L.b = kStageA + (wn * 8 + par) * 1024 + 512 * j + 16 * (lane & 15);
+    L.sb = kStageA + B + SA + wn * 512 + 8 * ((lane & 15) + 32 * j);
+    L.sha = 16u * j;
+    L.shb = 8u * par;
     return L;
   }
   template <int P>
   __device__ __forceinline__ static void read(Frags& F, const uint8_t* st, const Lane& L) {
-    F.a[P] = *reinterpret_cast<const uintx4*>(st + L.a + P * 1024);
-    F.sa[P] = st[L.sa + P * 64];
-    F.b[P] = *reinterpret_cast<const uintx4*>(st + L.b + P * 1024);
-    if (P == 0) F.sb = *reinterpret_cast<const uintx2*>(st + L.sb);
+    F.alo[P] = *reinterpret_cast<const uintx4*>(st + L.alo + P * 2048);
+    F.ahi[P] = *reinterpret_cast<const uintx4*>(st + L.ahi + P * 2048);
+    F.sa[P] = *reinterpret_cast<const uint32_t*>(st + L.sa + P * 128) >> L.sha;
+    F.blo[P] = *reinterpret_cast<const uintx4*>(st + L.b + P * 2048);
+    F.bhi[P] = *reinterpret_cast<const uintx4*>(st + L.b + P * 2048 + 256);
+    if (P < 2) {
+      const uintx2 v = *reinterpret_cast<const uintx2*>(st + L.sb + 128 * P);
+      F.sb[P] = uintx2{v[0] >> L.shb, v[1] >> L.shb};
+    }
   }
-  // column fragment P against all 8 row fragments
+  template <int P, int H>
+  __device__ __forceinline__ static void mma_half(const Frags& F, Acc& acc) {
+    const uintx4& b = H ? F.bhi[P] : F.blo[P];
+    const intx8 bf = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+    // byte 2 (P & 1) of the shifted word is the scale of column tile 2P + par
+    const int sb = (int)F.sb[H][P >> 1];
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      const uintx4& a = H ? F.ahi[fm] : F.alo[fm];
+      const intx8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+      acc[fm][P] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          af, bf, acc[fm][P], kFmtFP4, kFmtFP4, H, (int)F.sa[fm], 2 * (P & 1), sb);
+    }
+  }
   template <int P>
   __device__ __forceinline__ static void mma(const Frags& F, const Lane&, Acc& acc) {
-    const intx8 bf = {(int)F.b[P][0], (int)F.b[P][1], (int)F.b[P][2], (int)F.b[P][3], 0, 0, 0, 0};
-    const int sb = (int)F.sb[P >> 2];
-#pragma unroll
-    for (int fm = 0; fm < 8; ++fm) {
-      const intx8 af = {(int)F.a[fm][0], (int)F.a[fm][1], (int)F.a[fm][2], (int)F.a[fm][3],
-                        0, 0, 0, 0};
-      // byte P & 3 of sb is the scale of column tile P
-      acc[fm][P] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          af, bf, acc[fm][P], kFmtFP4, kFmtFP4, 0, (int)F.sa[fm], P & 3, sb);
-    }
+    mma_half<P, 0>(F, acc);
+    mma_half<P, 1>(F, acc);
   }
   __device__ __forceinline__ static void zero(Acc& acc) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   }
   __device__ __forceinline__ static void stage(const Acc& acc, uint8_t* ct, const PipeOut& o,
-                                               int n0, int wm, int wn, int lane) {
-    stage16<false>(acc, ct, o, n0, wm, wn, lane);
+                                               int, int wm, int wn, int lane) {
+    stage32(acc, ct, o, wm, wn, lane);
   }
 };
 
@@ -589,21 +631,9 @@ struct Fp8Pipe {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   }
-  // lane holds rows 8 (e >> 2) + 4 (lane >> 5) + (e & 3), column lane & 31
   __device__ __forceinline__ static void stage(const Acc& acc, uint8_t* ct, const PipeOut& o,
                                                int, int wm, int wn, int lane) {
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < 4; ++fn) {
-        const int col = wn * 128 + fn * 32 + (lane & 31);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = wm * 128 + fm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          *reinterpret_cast<uint16_t*>(ct + c_tile_offset(row, col)) =
-              round_out<false>(acc[fm][fn][e] * o.s);
-        }
-      }
+    stage32(acc, ct, o, wm, wn, lane);
   }
 };
 
