@@ -467,6 +467,7 @@ struct Fp4Pipe {
   static constexpr int STAGE = kStageA + B + SA + SB;
   static constexpr int DMA = 10;
   static constexpr int NST = 4;                  // 4 x 34 KB of LDS
+  static constexpr int CP_PAIRS = 6;             // copies of parts 0 / 1: 4 / 6
   typedef floatx16 Acc[4][4];
   struct Frags {
     uintx4 alo[4], ahi[4];
@@ -572,6 +573,7 @@ struct Fp8Pipe {
   static constexpr int STAGE = kStageA + B;
   static constexpr int DMA = 8;
   static constexpr int NST = 4;                  // 4 x 32 KB
+  static constexpr int CP_PAIRS = 4;             // copies of parts 0 / 1: 4 / 4
   typedef floatx16 Acc[4][4];
   struct Frags {
     uintx4 alo[4], ahi[4];
@@ -656,6 +658,9 @@ struct F16Pipe {
   static constexpr int STAGE = kStageA + B;
   static constexpr int DMA = 4 + 4 * WV;
   static constexpr int NST = WFMT == 1 ? 8 : 6;  // 8 x 20 KB or 6 x 24 KB
+  // copies issued ahead of the step: pinning them between the matrix
+  // instructions makes these kernels spill
+  static constexpr int CP_PAIRS = 0;
   typedef floatx4 Acc[8][8];
   struct Frags {
     uintx4 a[8];
@@ -722,30 +727,47 @@ struct F16Pipe {
   }
 };
 
+// No copies in this step (the last steps, or copies issued before it).
+struct NoCopies {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
 // One part: read fragment P of the next step (RD), then the matrix work of
 // fragment P of the current step; the scheduler keeps the two together.
-template <class Ops, int P, bool RD>
+// With CP, parts 0 and 1 also issue the copies of a later step (cp(0): the A
+// slices, cp(1): the rest), pinned to alternate with the part's matrix
+// instructions: issuing them all ahead of the step kept the matrix pipe idle
+// after every barrier.
+template <class Ops, int P, bool RD, bool CP, class Copies>
 __device__ __forceinline__ void pipe_part(typename Ops::Frags& cur, typename Ops::Frags& nxt,
                                           const uint8_t* nx, const typename Ops::Lane& L,
-                                          typename Ops::Acc& acc) {
+                                          typename Ops::Acc& acc, const Copies& cp) {
   if (RD) Ops::template read<P>(nxt, nx, L);
   Ops::template mma<P>(cur, L, acc);
+  if constexpr (CP && P <= 1) {
+    cp(P);
+#pragma unroll
+    for (int i = 0; i < Ops::CP_PAIRS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one vector memory read
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class Ops, bool RD>
+template <class Ops, bool RD, bool CP = false, class Copies = NoCopies>
 __device__ __forceinline__ void pipe_step(typename Ops::Frags& cur, typename Ops::Frags& nxt,
                                           const uint8_t* nx, const typename Ops::Lane& L,
-                                          typename Ops::Acc& acc) {
-  pipe_part<Ops, 0, RD>(cur, nxt, nx, L, acc);
-  pipe_part<Ops, 1, RD>(cur, nxt, nx, L, acc);
-  pipe_part<Ops, 2, RD>(cur, nxt, nx, L, acc);
-  pipe_part<Ops, 3, RD>(cur, nxt, nx, L, acc);
+                                          typename Ops::Acc& acc, const Copies& cp = Copies{}) {
+  pipe_part<Ops, 0, RD, CP>(cur, nxt, nx, L, acc, cp);
+  pipe_part<Ops, 1, RD, CP>(cur, nxt, nx, L, acc, cp);
+  pipe_part<Ops, 2, RD, CP>(cur, nxt, nx, L, acc, cp);
+  pipe_part<Ops, 3, RD, CP>(cur, nxt, nx, L, acc, cp);
   if constexpr (Ops::PARTS == 8) {
-    pipe_part<Ops, 4, RD>(cur, nxt, nx, L, acc);
-    pipe_part<Ops, 5, RD>(cur, nxt, nx, L, acc);
-    pipe_part<Ops, 6, RD>(cur, nxt, nx, L, acc);
-    pipe_part<Ops, 7, RD>(cur, nxt, nx, L, acc);
+    pipe_part<Ops, 4, RD, CP>(cur, nxt, nx, L, acc, cp);
+    pipe_part<Ops, 5, RD, CP>(cur, nxt, nx, L, acc, cp);
+    pipe_part<Ops, 6, RD, CP>(cur, nxt, nx, L, acc, cp);
+    pipe_part<Ops, 7, RD, CP>(cur, nxt, nx, L, acc, cp);
   }
 }
 
@@ -845,13 +867,26 @@ __global__ __launch_bounds__(kThreads) void pipe256_kernel(
   // Two steps per iteration, F0 and F1 trading roles; every copy issued in
   // here is in range (ks + NST < KS).  At the end of step ks the copies of
   // step ks+2 must have landed (its fragments are read during step ks+1).
+  // step_issuing(cur, nxt, r, s): compute with cur, read step r into nxt,
+  // issue the copies of step s
+  auto step_issuing = [&](typename Ops::Frags& cur, typename Ops::Frags& nxt, int r, int s) {
+    if constexpr (Ops::CP_PAIRS > 0) {
+      uint8_t* st = stage(s);
+      auto cp = [&](int part) {
+        if (part == 0) pipe_issue_a<Ops>(st, s, wave, lane, m0, row_bytes, rs.a);
+        if (part == 1) Ops::issue_rest(st, s, wave, lane, m0, cg0, g, rs);
+      };
+      pipe_step<Ops, true, true>(cur, nxt, stage(r), L, acc, cp);
+    } else {
+      issue(s);
+      pipe_step<Ops, true>(cur, nxt, stage(r), L, acc);
+    }
+  };
   int ks = 0;
   for (; ks + NST < KS; ks += 2) {
-    issue(ks + NST - 1);
-    pipe_step<Ops, true>(F0, F1, stage(ks + 1), L, acc);
+    step_issuing(F0, F1, ks + 1, ks + NST - 1);
     QG_WAIT_VM_BARRIER((NST - 3) * PER);
-    issue(ks + NST);
-    pipe_step<Ops, true>(F1, F0, stage(ks + 2), L, acc);
+    step_issuing(F1, F0, ks + 2, ks + NST);
     QG_WAIT_VM_BARRIER((NST - 3) * PER);
   }
   // last NST steps (ks == KS - NST), copies issued up to step KS - 2
