@@ -472,8 +472,8 @@ struct Fp4Pipe {
   struct Frags {
     uintx4 alo[4], ahi[4];
     uintx4 blo[4], bhi[4];
-    uint32_t sa[4];   // row scale words, shifted so byte h is block 2j + h
-    uintx2 sb[2];     // [h] column scale words of tiles 0-3 and 4-7, shifted
+    uint32_t sa[4];   // row scale words (blocks 0-3 of the step)
+    uintx2 sb[2];     // [h] column scale words of tiles 0-3 and 4-7
   };
   struct Lane {
     int alo, ahi, sa, b, sb;
@@ -518,32 +518,34 @@ struct Fp4Pipe {
   __device__ __forceinline__ static void read(Frags& F, const uint8_t* st, const Lane& L) {
     F.alo[P] = *reinterpret_cast<const uintx4*>(st + L.alo + P * 2048);
     F.ahi[P] = *reinterpret_cast<const uintx4*>(st + L.ahi + P * 2048);
-    F.sa[P] = *reinterpret_cast<const uint32_t*>(st + L.sa + P * 128) >> L.sha;
+    F.sa[P] = *reinterpret_cast<const uint32_t*>(st + L.sa + P * 128);
     F.blo[P] = *reinterpret_cast<const uintx4*>(st + L.b + P * 2048);
     F.bhi[P] = *reinterpret_cast<const uintx4*>(st + L.b + P * 2048 + 256);
-    if (P < 2) {
-      const uintx2 v = *reinterpret_cast<const uintx2*>(st + L.sb + 128 * P);
-      F.sb[P] = uintx2{v[0] >> L.shb, v[1] >> L.shb};
-    }
+    if (P < 2) F.sb[P] = *reinterpret_cast<const uintx2*>(st + L.sb + 128 * P);
   }
+  // The lane's scale shifts run in the step that uses the words (read one
+  // step earlier): shifting right after the read would make the matrix
+  // instructions behind it wait for the LDS.
   template <int P, int H>
-  __device__ __forceinline__ static void mma_half(const Frags& F, Acc& acc) {
+  __device__ __forceinline__ static void mma_half(const Frags& F, const Lane& L, Acc& acc) {
     const uintx4& b = H ? F.bhi[P] : F.blo[P];
     const intx8 bf = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
     // byte 2 (P & 1) of the shifted word is the scale of column tile 2P + par
-    const int sb = (int)F.sb[H][P >> 1];
+    const int sb = (int)(F.sb[H][P >> 1] >> L.shb);
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) {
       const uintx4& a = H ? F.ahi[fm] : F.alo[fm];
       const intx8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+      // byte h of the shifted word is block 2j + h of the row
+      const int sa = (int)(F.sa[fm] >> L.sha);
       acc[fm][P] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          af, bf, acc[fm][P], kFmtFP4, kFmtFP4, H, (int)F.sa[fm], 2 * (P & 1), sb);
+          af, bf, acc[fm][P], kFmtFP4, kFmtFP4, H, sa, 2 * (P & 1), sb);
     }
   }
   template <int P>
-  __device__ __forceinline__ static void mma(const Frags& F, const Lane&, Acc& acc) {
-    mma_half<P, 0>(F, acc);
-    mma_half<P, 1>(F, acc);
+  __device__ __forceinline__ static void mma(const Frags& F, const Lane& L, Acc& acc) {
+    mma_half<P, 0>(F, L, acc);
+    mma_half<P, 1>(F, L, acc);
   }
   __device__ __forceinline__ static void zero(Acc& acc) {
 #pragma unroll
