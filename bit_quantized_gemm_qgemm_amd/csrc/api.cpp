@@ -139,7 +139,7 @@ const char* qgemm_status_string(int status) {
   }
 }
 
-int qgemm_abi_version(void) { return 101; }
+int qgemm_abi_version(void) { return 102; }
 
 int64_t qgemm_prepack_bytes(int fmt, int64_t K, int64_t N) {
   if (!valid_format(fmt)) return QGEMM_ERR_FORMAT;
@@ -283,7 +283,7 @@ int64_t qgemm_act_workspace_bytes(int fmt, int64_t M, int64_t K) {
   if (M < 0 || K < 0 || !k_ok(fmt, K)) return QGEMM_ERR_SHAPE;
   if (M >= kMaxIndex || K >= kMaxIndex || M * K >= kMaxIndex * 2) return QGEMM_ERR_SHAPE;
   if (fmt == QGEMM_MXFP4) return qgemm::cdiv(M * K / 2, 16) * 16 + M * (K / 32);
-  return qgemm::cdiv(M * K, 16) * 16 + 16;
+  return qgemm::cdiv(M * K, 16) * 16 + 16 + 4 * qgemm::kFp8Partials;
 }
 
 int qgemm_mxfp4_act(const float* a, const void* w_packed, void* c, void* workspace, int64_t M,
@@ -322,8 +322,11 @@ int qgemm_fp8_act(const float* a, const void* b_packed, const float* scale_b, vo
   if ((st = check_device()) != QGEMM_OK) return st;
   uint8_t* codes = static_cast<uint8_t*>(workspace);
   float* scale_a = reinterpret_cast<float*>(codes + qgemm::cdiv(M * K, 16) * 16);
-  // an empty A still gets its scale (1.0, the all-zero rule)
-  st = launched(qgemm::launch_quantize_fp8(a, M * K, codes, scale_a, as_stream(stream)));
+  float* partials = scale_a + 4;
+  // an empty A still gets its scale (1.0, the all-zero rule); K % 16 == 0,
+  // so A is whole 16-byte pieces
+  st = launched(
+      qgemm::launch_quantize_fp8_ws(a, M * K, codes, scale_a, partials, as_stream(stream)));
   if (st != QGEMM_OK || N == 0) return st;
   if (M <= kDecodeMaxM)
     return launched(qgemm::launch_decode_gemm(QGEMM_FP8, codes, b_packed, nullptr, scale_a,

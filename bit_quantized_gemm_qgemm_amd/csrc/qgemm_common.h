@@ -145,6 +145,11 @@ hipError_t launch_quantize_mxfp4(const float* x, int64_t rows, int64_t K, uint8_
                                  uint8_t* e8m0, hipStream_t stream);
 hipError_t launch_quantize_fp8(const float* x, int64_t count, uint8_t* codes, float* scale,
                                hipStream_t stream);
+// Per-block partial maxima of the two-launch FP8 quantizer (workspace form).
+constexpr int kFp8Partials = 256;
+// count % 4 == 0, x 16-byte aligned; partials holds kFp8Partials floats.
+hipError_t launch_quantize_fp8_ws(const float* x, int64_t count, uint8_t* codes, float* scale,
+                                  float* partials, hipStream_t stream);
 
 // Small-M path (M rows handled in 16-row slabs) for W4A16 / W8A16 / FP8.
 hipError_t launch_decode_gemm(int fmt, const void* x, const void* w_packed, const void* scales,

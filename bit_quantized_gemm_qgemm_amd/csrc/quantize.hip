@@ -118,7 +118,71 @@ __global__ void fp8_finish_kernel(float* __restrict__ scale) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *scale = fp8_scale_of(*scale);
 }
 
+// With a workspace: the same scale and codes in two launches and no
+// atomics.  Pass 1 writes one partial max |x| per block; in pass 2 every
+// block reduces all partials itself (at most kFp8Partials floats), forms the
+// scale and casts its share, four elements per thread; block 0 stores the
+// scale.  count % 4 == 0 and x 16-byte aligned.
+__global__ __launch_bounds__(256) void fp8_partial_amax_kernel(const float* __restrict__ x,
+                                                               int64_t n4,
+                                                               float* __restrict__ partials) {
+  float m = 0.f;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const floatx4* x4 = reinterpret_cast<const floatx4*>(x);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const floatx4 v = x4[i];
+    m = fmaxf(fmaxf(m, fmaxf(fabsf(v[0]), fabsf(v[1]))), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    partials[blockIdx.x] = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+}
+
+__global__ __launch_bounds__(256) void fp8_cast_partials_kernel(
+    const float* __restrict__ x, int64_t n4, const float* __restrict__ partials, int np,
+    uint32_t* __restrict__ codes4, float* __restrict__ scale) {
+  float m = (int)threadIdx.x < np ? partials[threadIdx.x] : 0.f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float s = fp8_scale_of(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3])));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+  const double sd = (double)s;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const floatx4* x4 = reinterpret_cast<const floatx4*>(x);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const floatx4 v = x4[i];
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w |= e4m3fn_rne((float)((double)v[j] / sd)) << (8 * j);
+    codes4[i] = w;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_fp8_ws(const float* x, int64_t count, uint8_t* codes, float* scale,
+                                  float* partials, hipStream_t stream) {
+  const int64_t n4 = count / 4;
+  const int64_t want = cdiv(n4, 256);
+  const int np = (int)(want < kFp8Partials ? want : kFp8Partials);
+  if (np > 0) {
+    hipLaunchKernelGGL(fp8_partial_amax_kernel, dim3((unsigned)np), dim3(256), 0, stream, x, n4,
+                       partials);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t grid = want < 1 ? 1 : (want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(fp8_cast_partials_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, n4,
+                     (const float*)partials, np, reinterpret_cast<uint32_t*>(codes), scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_mxfp4(const float* x, int64_t rows, int64_t K, uint8_t* codes,
                                  uint8_t* e8m0, hipStream_t stream) {

@@ -186,7 +186,8 @@ int qgemm_fp8(const void* a, const void* b_packed, const float* scale_a,
  * qgemm_quantize_mxfp4 / qgemm_quantize_fp8 produce it:
  *   MXFP4: codes [M, K/2] at offset 0, E8M0 [M, K/32] at round_up(M*K/2, 16);
  *   FP8:   e4m3fn codes [M, K] at offset 0, the fp32 scale at
- *          round_up(M*K, 16).
+ *          round_up(M*K, 16); 1 KB of per-block partial maxima follows at
+ *          round_up(M*K, 16) + 16 (scratch of the quantizer).
  * The result equals quantizing with those entry points and calling
  * qgemm_mxfp4 / qgemm_fp8 on the quantized A (bit for bit).  The library
  * allocates nothing.  Calls that share a workspace must not overlap.

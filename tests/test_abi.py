@@ -58,7 +58,7 @@ def test_status_strings(lib):
         s = qg.status_string(st)
         assert s and s != "unknown status"
     assert qg.status_string(12345) == "unknown status"
-    assert lib.qgemm_abi_version() == 101
+    assert lib.qgemm_abi_version() == 102
 
 
 def test_prepack_bytes(lib):
@@ -147,8 +147,8 @@ def test_act_workspace_and_argument_errors(lib):
     s = P(0)
     assert lib.qgemm_act_workspace_bytes(3, 16, 8192) == 16 * 8192 // 2 + 16 * 256
     assert lib.qgemm_act_workspace_bytes(3, 3, 96) == 144 + 9      # codes rounded to 16
-    assert lib.qgemm_act_workspace_bytes(4, 16, 8192) == 16 * 8192 + 16
-    assert lib.qgemm_act_workspace_bytes(4, 3, 16) == 48 + 16
+    assert lib.qgemm_act_workspace_bytes(4, 16, 8192) == 16 * 8192 + 16 + 1024   # + partial maxima
+    assert lib.qgemm_act_workspace_bytes(4, 3, 16) == 48 + 16 + 1024
     assert lib.qgemm_act_workspace_bytes(1, 16, 64) == ERR_FORMAT
     assert lib.qgemm_act_workspace_bytes(3, 16, 48) == ERR_SHAPE
     assert lib.qgemm_mxfp4_act(GOOD, GOOD, GOOD, None, 4, 16, 64, s) == ERR_NULL
