@@ -58,6 +58,9 @@ WORKLOADS = {
     # group-wise scales along K (128) with zero points, at the decode shapes
     "w4a16_g128_decode": ("w4a16_grouped", (1, 8, 16), 28672, 8192),
     "w8a16_g128_decode": ("w8a16_grouped", (1, 4, 16), 11008, 4096),
+    # ... and at the large-M comparison shape (the tiled kernel)
+    "w4a16_g128_square": ("w4a16_grouped", (4096,), 4096, 4096),
+    "w8a16_g128_square": ("w8a16_grouped", (4096,), 4096, 4096),
     # NVFP4-style weights (e4m3 scale per 16 elements, fp32 per tensor), fp16 X
     "nvfp4_decode": ("nvfp4", (1, 8, 16), 28672, 8192),
     # fp32 activations quantized on the device inside the call, then the GEMM
@@ -347,7 +350,7 @@ def cpu_baseline(name, budget_s=10.0):
 
     fmt, ms, n, k = WORKLOADS[name]
     mmax = max(ms)
-    if fmt in ("w4a16_grouped", "w8a16_grouped"):
+    if fmt in ("w4a16_grouped", "w8a16_grouped") and mmax <= 16:
         w4 = fmt == "w4a16_grouped"
         gen = wl.w4a16_grouped if w4 else wl.w8a16_grouped
         ggemm = oracle.gemm_w4a16_grouped if w4 else oracle.gemm_w8a16_grouped
@@ -408,6 +411,12 @@ def cpu_baseline(name, budget_s=10.0):
             gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16
             x, w, s = gen(rows, k, n)
             run = lambda: gemm(x, w, s)  # noqa: E731
+        elif fmt in ("w4a16_grouped", "w8a16_grouped"):
+            w4 = fmt == "w4a16_grouped"
+            gen = wl.w4a16_grouped if w4 else wl.w8a16_grouped
+            ggemm = oracle.gemm_w4a16_grouped if w4 else oracle.gemm_w8a16_grouped
+            x, w, s, z = gen(rows, k, n, GROUP_K)
+            run = lambda: ggemm(x, w, s, z, GROUP_K)  # noqa: E731
         elif fmt in ("mxfp4", "mxfp4_act"):
             a, w = wl.mxfp4_operands(rows, n, k)
             ac, ae = oracle.mxfp4_quantize(a)
@@ -533,7 +542,7 @@ def kernel_name(setup, m):
     if setup.kind == "decode":
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     # same rules as the library's dispatch
-    if setup.fmt in ("w4a16", "w8a16"):
+    if setup.fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped"):
         big = m >= 256 and setup.n > 128 and setup.k % 8 == 0
         name = "pipe256_kernel" if big else "decode_gemm_kernel"
         return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"

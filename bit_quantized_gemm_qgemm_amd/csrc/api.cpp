@@ -117,6 +117,10 @@ int grouped_gemm(int fmt, const void* x, const void* w_packed, void* y, int64_t 
   if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 16)) return QGEMM_ERR_ALIGN;
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
+  // K % 32 == 0 here, so fp16 X rows are 16-byte aligned
+  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0)
+    return launched(qgemm::launch_weight_only_tile_grouped(fmt, x, w_packed, y, M, N, K, group_k,
+                                                           as_stream(stream)));
   return launched(qgemm::launch_decode_grouped(fmt, x, w_packed, y, M, N, K, group_k,
                                                as_stream(stream)));
 }

@@ -385,14 +385,14 @@ __device__ __forceinline__ uint16_t round_out(float v) {
 }
 
 // 16 x 16 accumulators: lane holds rows 4 (lane >> 4) + i, column lane & 15.
-template <bool F16_OUT>
+template <bool F16_OUT, bool COL_SCALE = F16_OUT>
 __device__ __forceinline__ void stage16(const floatx4 (&acc)[8][8], uint8_t* ct, const PipeOut& o,
                                         int n0, int wm, int wn, int lane) {
 #pragma unroll
   for (int fn = 0; fn < 8; ++fn) {
     const int col = wn * 128 + fn * 16 + (lane & 15);
     float s = o.s;
-    if constexpr (F16_OUT) {
+    if constexpr (COL_SCALE) {
       const int gn = n0 + col;
       s = (float)__builtin_bit_cast(_Float16, o.col_scale[gn < o.N ? gn : o.N - 1]);
     }
@@ -461,6 +461,7 @@ __device__ __forceinline__ void stage32(const floatx16 (&acc)[4][4], uint8_t* ct
 // 8] (lane = column + 16 kg).
 struct Fp4Pipe {
   static constexpr int FMT = 3;
+  static constexpr int GROUP_WORDS = 0;
   static constexpr int PARTS = 4;
   static constexpr int STEPS_PER_TILE = 2;
   static constexpr int B = 16 * 1024, SA = kBig * 4, SB = 2 * 512;
@@ -569,6 +570,7 @@ struct Fp4Pipe {
 // 2s, 2s + 1 (s = step within the tile) from both 1 KB halves h.
 struct Fp8Pipe {
   static constexpr int FMT = 4;
+  static constexpr int GROUP_WORDS = 0;
   static constexpr int PARTS = 4;
   static constexpr int STEPS_PER_TILE = 2;
   static constexpr int B = 16 * 1024;
@@ -649,17 +651,26 @@ struct Fp8Pipe {
 // before the matrix instructions that use them (W4A16 page section 2, W8A16
 // page Steps 1-2: the dequantized weight never leaves the registers).  The
 // per-column scale multiplies the fp32 sum in the epilogue.
-// Stage: A (fp16 X) | W: [tile 16][part WV][lane 64][4 B].
-template <int WFMT>
+// Grouped formats (NGT > 0 metadata words per column and 128-wide tile, the
+// layout of the grouped prepack): each step also gathers the lane's word
+// {fp16 1024 + z (1152 + z for INT8), fp16 s} of its column and the step's K
+// group, and the dequant forms fp16((w - z) * s) with one rounding, as the
+// small-M kernel does; the epilogue then rounds the fp32 sum alone.
+// Stage: A (fp16 X) | W: [tile 16][part WV][lane 64][4 B] | metadata (grouped):
+// [tile 16][lane 64][4 B].
+template <int WFMT, int NGT = 0>
 struct F16Pipe {
   static constexpr int FMT = WFMT;
+  static constexpr int GROUP_WORDS = NGT;
   static constexpr int WV = WFMT == 1 ? 1 : 2;        // weight words per lane per step
   static constexpr int PARTS = 8;
   static constexpr int STEPS_PER_TILE = 4;
   static constexpr int B = 16 * WV * 256;
-  static constexpr int STAGE = kStageA + B;
-  static constexpr int DMA = 4 + 4 * WV;
-  static constexpr int NST = WFMT == 1 ? 8 : 6;  // 8 x 20 KB or 6 x 24 KB
+  static constexpr int MB = NGT > 0 ? 16 * 256 : 0;
+  static constexpr int STAGE = kStageA + B + MB;
+  static constexpr int DMA = 4 + 4 * WV + (NGT > 0 ? 4 : 0);
+  // 8 x 20 KB or 6 x 24 KB; grouped: 6 x 24 KB or 4 x 28 KB
+  static constexpr int NST = NGT > 0 ? (WFMT == 1 ? 6 : 4) : (WFMT == 1 ? 8 : 6);
   // copies issued ahead of the step: pinning them between the matrix
   // instructions makes these kernels spill
   static constexpr int CP_PAIRS = 0;
@@ -669,7 +680,7 @@ struct F16Pipe {
     half8_t b[8];   // dequantized right after the LDS read
   };
   struct Lane {
-    int a, b;
+    int a, b, m;
   };
   __device__ __forceinline__ static int swizzle(int r) { return (r >> 1) & 3; }
   __device__ __forceinline__ static int row_bytes(int K) { return 2 * K; }
@@ -691,19 +702,39 @@ struct F16Pipe {
         dma4(rs.w, st + kStageA + (t * WV + p) * 256, off);
       }
     }
+    if constexpr (NGT > 0) {
+      // the word of the lane's column (lane & 15) for the step's K group
+      const int j = (s * NGT) >> 2;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int t = 4 * wave + jj;
+        const uint32_t off =
+            ((((uint32_t)(cg0 + t) * g.KT + kt) * 16u + (uint32_t)(lane & 15)) * NGT + j) * 4u;
+        dma4(rs.sw, st + kStageA + B + t * 256, off);
+      }
+    }
   }
   __device__ __forceinline__ static Lane lane_offsets(int wm, int wn, int lane) {
     const int r = wm * 128 + (lane & 15);
     Lane L;
     L.a = a16_lane_offset(wm, lane, swizzle(r));
     L.b = kStageA + wn * 8 * WV * 256 + 4 * lane;
+    L.m = kStageA + B + wn * 8 * 256 + 4 * lane;
     return L;
   }
   template <int P>
   __device__ __forceinline__ static void read(Frags& F, const uint8_t* st, const Lane& L) {
     F.a[P] = *reinterpret_cast<const uintx4*>(st + L.a + P * 1024);
     const uint32_t w0 = *reinterpret_cast<const uint32_t*>(st + L.b + P * WV * 256);
-    if constexpr (WFMT == 1) {
+    if constexpr (NGT > 0) {
+      const uint32_t e = *reinterpret_cast<const uint32_t*>(st + L.m + P * 256);
+      if constexpr (WFMT == 1) {
+        F.b[P] = dequant_w4_group(w0, e);
+      } else {
+        const uint32_t w1 = *reinterpret_cast<const uint32_t*>(st + L.b + (P * WV + 1) * 256);
+        F.b[P] = dequant_w8_group(w0, w1, e);
+      }
+    } else if constexpr (WFMT == 1) {
       F.b[P] = dequant_w4_shift(w0);
     } else {
       const uint32_t w1 = *reinterpret_cast<const uint32_t*>(st + L.b + (P * WV + 1) * 256);
@@ -725,7 +756,7 @@ struct F16Pipe {
   }
   __device__ __forceinline__ static void stage(const Acc& acc, uint8_t* ct, const PipeOut& o,
                                                int n0, int wm, int wn, int lane) {
-    stage16<true>(acc, ct, o, n0, wm, wn, lane);
+    stage16<true, NGT == 0>(acc, ct, o, n0, wm, wn, lane);
   }
 };
 
@@ -920,10 +951,12 @@ hipError_t launch_pipe_nst(const PipeArgs& g, const void* a, const void* a_sc, c
   return hipGetLastError();
 }
 
+// group_k: grouped weight-only formats (their metadata segment is the second
+// weight buffer); 0 otherwise.
 template <class Ops>
 hipError_t launch_pipe(const void* a, const void* a_sc, const void* wp, const float* sa,
                        const float* sb, const void* col_scale, void* c, int64_t M, int64_t N,
-                       int64_t K, hipStream_t stream) {
+                       int64_t K, hipStream_t stream, int64_t group_k = 0) {
   constexpr int FMT = Ops::FMT;
   const PackGeom pg = pack_geom(FMT, K, N);
   PipeArgs g;
@@ -941,6 +974,11 @@ hipError_t launch_pipe(const void* a, const void* a_sc, const void* wp, const fl
   g.asc_bytes = FMT == 3 ? (uint32_t)(M * (K / 32)) : 0u;
   g.wsc_bytes = FMT == 3 ? (uint32_t)(pg.total - pg.scales) : 0u;
   const uint8_t* w_sc = FMT == 3 ? static_cast<const uint8_t*>(wp) + pg.scales : nullptr;
+  if constexpr (Ops::GROUP_WORDS > 0) {
+    const PackGeom gg = grouped_geom(FMT == 1 ? 5 : 6, K, N, group_k);
+    g.wsc_bytes = (uint32_t)(gg.total - gg.scales);
+    w_sc = static_cast<const uint8_t*>(wp) + gg.scales;
+  }
   // the deepest ring that fits in LDS, when K has at least that many steps
   if (Ops::NST > 4 && g.KS >= Ops::NST)
     return launch_pipe_nst<Ops, Ops::NST>(g, a, a_sc, wp, w_sc, sa, sb, col_scale, c, stream);
@@ -975,6 +1013,27 @@ hipError_t launch_weight_only_tile(int fmt, const void* x, const void* w_packed,
   if (fmt == 2)
     return launch_pipe<F16Pipe<2>>(x, nullptr, w_packed, nullptr, nullptr, scales, y, M, N, K,
                                    stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_weight_only_tile_grouped(int fmt, const void* x, const void* w_packed, void* y,
+                                          int64_t M, int64_t N, int64_t K, int64_t group_k,
+                                          hipStream_t stream) {
+#define QG_GROUPED(W, NG)                                                                   \
+  return launch_pipe<F16Pipe<W, NG>>(x, nullptr, w_packed, nullptr, nullptr, nullptr, y, M, N, \
+                                     K, stream, group_k);
+  const int ngt = grouped_ngt(group_k);
+  if (fmt == 5) {
+    if (ngt == 1) QG_GROUPED(1, 1)
+    if (ngt == 2) QG_GROUPED(1, 2)
+    QG_GROUPED(1, 4)
+  }
+  if (fmt == 6) {
+    if (ngt == 1) QG_GROUPED(2, 1)
+    if (ngt == 2) QG_GROUPED(2, 2)
+    QG_GROUPED(2, 4)
+  }
+#undef QG_GROUPED
   return hipErrorInvalidValue;
 }
 

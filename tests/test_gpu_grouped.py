@@ -116,3 +116,51 @@ def test_grouped_full_size_sampled(fmt, m):
     gemm = oracle.gemm_w4a16_grouped if fmt == "w4a16" else oracle.gemm_w8a16_grouped
     y_ref, bound = gemm(x, w[:, cols], s[:, cols], z[:, cols], gk, 1)
     assert_within(y[:, cols], y_ref, bound, f"{fmt} grouped full M={m}")
+
+
+# M >= 256 and N > 128 take the LDS-tiled matrix-core kernel (256 x 256 output
+# tiles): every metadata density (NGT = 1, 2, 4 words per column and tile),
+# ragged M and N, K not a multiple of 128, K shorter than the stage ring.
+TILE_CASES = [
+    # (m, k, n, group_k, group_n, zero points)
+    (256, 256, 200, 128, 1, True),    # one entry per tile, ragged N
+    (300, 640, 520, 64, 1, True),     # two entries per tile, ragged M and N
+    (257, 384, 136, 32, 3, True),     # per-step entries, column groups of 3
+    (512, 1056, 384, 96, 1, False),   # groups across tiles, K = 8.25 tiles, symmetric
+    (260, 160, 2100, 32, 5, True),    # short K: two tiles
+    (256, 96, 300, 32, 1, True),      # K < 128: one partial tile, 4-stage ring
+]
+
+
+@pytest.mark.parametrize("m,k,n,gk,gn,zp", TILE_CASES)
+def test_w4a16_grouped_tile_matches_oracle(m, k, n, gk, gn, zp):
+    case_id("w4a16 grouped tile", m, k, n, gk, gn, zp)
+    x, packed, s, z = wl.w4a16_grouped(m, k, n, gk, gn, zeros=zp, seed=m + k + n + gk)
+    y_ref, bound = oracle.gemm_w4a16_grouped(x, packed, s, z, gk, gn)
+    assert_within(run("w4a16", x, packed, s, z, k, n, gk, gn), y_ref, bound,
+                  f"w4a16 grouped tile {m}x{k}x{n} g{gk}/{gn}")
+
+
+@pytest.mark.parametrize("m,k,n,gk,gn,zp", TILE_CASES)
+def test_w8a16_grouped_tile_matches_oracle(m, k, n, gk, gn, zp):
+    case_id("w8a16 grouped tile", m, k, n, gk, gn, zp)
+    x, w, s, z = wl.w8a16_grouped(m, k, n, gk, gn, zeros=zp, seed=m + k + n + gk + 1)
+    y_ref, bound = oracle.gemm_w8a16_grouped(x, w, s, z, gk, gn)
+    assert_within(run("w8a16", x, w, s, z, k, n, gk, gn), y_ref, bound,
+                  f"w8a16 grouped tile {m}x{k}x{n} g{gk}/{gn}")
+
+
+@pytest.mark.parametrize("fmt", ["w4a16", "w8a16"])
+def test_grouped_tile_full_size_sampled(fmt):
+    """M = N = K = 4096 with group_k = 128 and zero points (the tiled kernel),
+    on sampled output columns."""
+    m = k = n = 4096
+    gk = 128
+    case_id(f"{fmt} grouped tile full", m, k, n, gk)
+    gen = wl.w4a16_grouped if fmt == "w4a16" else wl.w8a16_grouped
+    x, w, s, z = gen(m, k, n, gk, 1, seed=7)
+    y = run(fmt, x, w, s, z, k, n, gk, 1)
+    cols = np.unique(np.concatenate([np.random.default_rng(5).integers(0, n, 48), [0, n - 1]]))
+    gemm = oracle.gemm_w4a16_grouped if fmt == "w4a16" else oracle.gemm_w8a16_grouped
+    y_ref, bound = gemm(x, w[:, cols], s[:, cols], z[:, cols], gk, 1)
+    assert_within(y[:, cols], y_ref, bound, f"{fmt} grouped tile full")
