@@ -63,6 +63,7 @@ WORKLOADS = {
     "w8a16_g128_square": ("w8a16_grouped", (4096,), 4096, 4096),
     # NVFP4-style weights (e4m3 scale per 16 elements, fp32 per tensor), fp16 X
     "nvfp4_decode": ("nvfp4", (1, 8, 16), 28672, 8192),
+    "nvfp4_square": ("nvfp4", (4096,), 4096, 4096),
     # fp32 activations quantized on the device inside the call, then the GEMM
     "fp8_act_decode": ("fp8_act", (16,), 8192, 8192),
     "mxfp4_act_square": ("mxfp4_act", (8192,), 8192, 8192),
@@ -359,7 +360,7 @@ def cpu_baseline(name, budget_s=10.0):
         w, s, z = np.ascontiguousarray(w[:, :cols]), s[:, :cols], z[:, :cols]
         gemm = lambda xm, w, s: ggemm(xm, w, s, z, GROUP_K)  # noqa: E731
         w_bytes_per_step = sum(((k * cols // 2) if w4 else k * cols) + 3 * s.size for _ in ms)
-    if fmt == "nvfp4":
+    if fmt == "nvfp4" and mmax <= 16:
         cols = n if k * n <= 50_000_000 else max(16, int(50_000_000 // k))
         x, codes, scales, g = wl.nvfp4_weight(mmax, k, n)
         w, s = np.ascontiguousarray(codes[:cols]), np.ascontiguousarray(scales[:cols])
@@ -417,6 +418,9 @@ def cpu_baseline(name, budget_s=10.0):
             ggemm = oracle.gemm_w4a16_grouped if w4 else oracle.gemm_w8a16_grouped
             x, w, s, z = gen(rows, k, n, GROUP_K)
             run = lambda: ggemm(x, w, s, z, GROUP_K)  # noqa: E731
+        elif fmt == "nvfp4":
+            x, codes, scales, g = wl.nvfp4_weight(rows, k, n)
+            run = lambda: oracle.gemm_nvfp4(x, codes, scales, g)  # noqa: E731
         elif fmt in ("mxfp4", "mxfp4_act"):
             a, w = wl.mxfp4_operands(rows, n, k)
             ac, ae = oracle.mxfp4_quantize(a)
@@ -542,7 +546,7 @@ def kernel_name(setup, m):
     if setup.kind == "decode":
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     # same rules as the library's dispatch
-    if setup.fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped"):
+    if setup.fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped", "nvfp4"):
         big = m >= 256 and setup.n > 128 and setup.k % 8 == 0
         name = "pipe256_kernel" if big else "decode_gemm_kernel"
         return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"

@@ -200,6 +200,10 @@ int qgemm_nvfp4(const void* x, const void* w_packed, const float* global_scale, 
     return QGEMM_ERR_ALIGN;
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
+  // K % 16 == 0 here, so fp16 X rows are 16-byte aligned
+  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0)
+    return launched(qgemm::launch_weight_only_tile_nvfp4(x, w_packed, global_scale, y, M, N, K,
+                                                         as_stream(stream)));
   return launched(qgemm::launch_decode_nvfp4(x, w_packed, global_scale, y, M, N, K,
                                              as_stream(stream)));
 }

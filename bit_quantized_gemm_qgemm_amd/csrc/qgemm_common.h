@@ -171,6 +171,10 @@ hipError_t launch_decode_grouped(int fmt, const void* x, const void* w_packed, v
 hipError_t launch_weight_only_tile(int fmt, const void* x, const void* w_packed,
                                   const void* scales, void* y, int64_t M, int64_t N, int64_t K,
                                   hipStream_t stream);
+// NVFP4 weights with fp16 X (format 7) through the same tiled kernel.
+hipError_t launch_weight_only_tile_nvfp4(const void* x, const void* w_packed,
+                                        const float* global_scale, void* y, int64_t M, int64_t N,
+                                        int64_t K, hipStream_t stream);
 // Grouped W4A16 / W8A16 (formats 5, 6) through the same tiled kernel.
 hipError_t launch_weight_only_tile_grouped(int fmt, const void* x, const void* w_packed, void* y,
                                           int64_t M, int64_t N, int64_t K, int64_t group_k,

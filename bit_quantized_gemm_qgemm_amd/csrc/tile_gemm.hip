@@ -461,6 +461,8 @@ __device__ __forceinline__ void stage32(const floatx16 (&acc)[4][4], uint8_t* ct
 // 8] (lane = column + 16 kg).
 struct Fp4Pipe {
   static constexpr int FMT = 3;
+  template <class F>
+  __device__ __forceinline__ static void init(F&, F&) {}
   static constexpr int GROUP_WORDS = 0;
   static constexpr int PARTS = 4;
   static constexpr int STEPS_PER_TILE = 2;
@@ -570,6 +572,8 @@ struct Fp4Pipe {
 // 2s, 2s + 1 (s = step within the tile) from both 1 KB halves h.
 struct Fp8Pipe {
   static constexpr int FMT = 4;
+  template <class F>
+  __device__ __forceinline__ static void init(F&, F&) {}
   static constexpr int GROUP_WORDS = 0;
   static constexpr int PARTS = 4;
   static constexpr int STEPS_PER_TILE = 2;
@@ -656,21 +660,28 @@ struct Fp8Pipe {
 // {fp16 1024 + z (1152 + z for INT8), fp16 s} of its column and the step's K
 // group, and the dequant forms fp16((w - z) * s) with one rounding, as the
 // small-M kernel does; the epilogue then rounds the fp32 sum alone.
-// Stage: A (fp16 X) | W: [tile 16][part WV][lane 64][4 B] | metadata (grouped):
-// [tile 16][lane 64][4 B].
+// NVFP4 weights (WFMT 7: E2M1 codes in the INT4 tile geometry, natural
+// nibble order): each step also gathers the dword of the lane's column that
+// holds its 16-element block's e4m3 scale for all four steps of the tile
+// (byte s for step s; the register set counts its steps to pick the byte);
+// each weight is formed exactly in fp16 (E2M1 value times e4m3 scale) and
+// the per-tensor scale multiplies the fp32 sum in the epilogue.
+// Stage: A (fp16 X) | W: [tile 16][part WV][lane 64][4 B] | metadata (grouped
+// or NVFP4): [tile 16][lane 64][4 B].
 template <int WFMT, int NGT = 0>
 struct F16Pipe {
   static constexpr int FMT = WFMT;
   static constexpr int GROUP_WORDS = NGT;
-  static constexpr int WV = WFMT == 1 ? 1 : 2;        // weight words per lane per step
+  static constexpr bool META = NGT > 0 || WFMT == 7;
+  static constexpr int WV = WFMT == 2 ? 2 : 1;        // weight words per lane per step
   static constexpr int PARTS = 8;
   static constexpr int STEPS_PER_TILE = 4;
   static constexpr int B = 16 * WV * 256;
-  static constexpr int MB = NGT > 0 ? 16 * 256 : 0;
+  static constexpr int MB = META ? 16 * 256 : 0;
   static constexpr int STAGE = kStageA + B + MB;
-  static constexpr int DMA = 4 + 4 * WV + (NGT > 0 ? 4 : 0);
-  // 8 x 20 KB or 6 x 24 KB; grouped: 6 x 24 KB or 4 x 28 KB
-  static constexpr int NST = NGT > 0 ? (WFMT == 1 ? 6 : 4) : (WFMT == 1 ? 8 : 6);
+  static constexpr int DMA = 4 + 4 * WV + (META ? 4 : 0);
+  // 8 x 20 KB or 6 x 24 KB; with metadata: 6 x 24 KB or 4 x 28 KB
+  static constexpr int NST = META ? (WV == 1 ? 6 : 4) : (WV == 1 ? 8 : 6);
   // copies issued ahead of the step: pinning them between the matrix
   // instructions makes these kernels spill
   static constexpr int CP_PAIRS = 0;
@@ -678,10 +689,16 @@ struct F16Pipe {
   struct Frags {
     uintx4 a[8];
     half8_t b[8];   // dequantized right after the LDS read
+    int step;       // NVFP4: the step these registers are read for next
   };
   struct Lane {
     int a, b, m;
   };
+  // the two register sets take the even and the odd steps
+  __device__ __forceinline__ static void init(Frags& F0, Frags& F1) {
+    F0.step = 0;
+    F1.step = 1;
+  }
   __device__ __forceinline__ static int swizzle(int r) { return (r >> 1) & 3; }
   __device__ __forceinline__ static int row_bytes(int K) { return 2 * K; }
   __device__ __forceinline__ static void issue_rest(uint8_t* st, int ks, int wave, int lane,
@@ -695,11 +712,22 @@ struct F16Pipe {
       for (int p = 0; p < WV; ++p) {
         // W4: word s of the lane's 16 bytes.  W8: bytes 8 (s & 1) + 4p of
         // the lane's 16 bytes in half s >> 1.
-        const uint32_t off = WFMT == 1
+        const uint32_t off = WV == 1
             ? ((uint32_t)(cg0 + t) * g.KT + kt) * kTileBytesW4 + 16u * lane + 4u * s
             : ((uint32_t)(cg0 + t) * g.KT + kt) * kTileBytes + 1024u * (s >> 1) + 16u * lane +
                   8u * (s & 1) + 4u * p;
         dma4(rs.w, st + kStageA + (t * WV + p) * 256, off);
+      }
+    }
+    if constexpr (WFMT == 7) {
+      // the scale dword of the lane's column (lane & 15) and 16-element
+      // block pair (lane >> 5): bytes c*8 + 4(g >> 1) + s of the tile
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int t = 4 * wave + jj;
+        const uint32_t off = ((uint32_t)(cg0 + t) * g.KT + kt) * (uint32_t)kScaleTileBytes +
+                             8u * (uint32_t)(lane & 15) + 4u * (uint32_t)(lane >> 5);
+        dma4(rs.sw, st + kStageA + B + t * 256, off);
       }
     }
     if constexpr (NGT > 0) {
@@ -726,7 +754,11 @@ struct F16Pipe {
   __device__ __forceinline__ static void read(Frags& F, const uint8_t* st, const Lane& L) {
     F.a[P] = *reinterpret_cast<const uintx4*>(st + L.a + P * 1024);
     const uint32_t w0 = *reinterpret_cast<const uint32_t*>(st + L.b + P * WV * 256);
-    if constexpr (NGT > 0) {
+    if constexpr (WFMT == 7) {
+      const uint32_t e = *reinterpret_cast<const uint32_t*>(st + L.m + P * 256);
+      F.b[P] = dequant_nvfp4(w0, e >> (8 * (F.step & 3)));
+      if constexpr (P == PARTS - 1) F.step += 2;
+    } else if constexpr (NGT > 0) {
       const uint32_t e = *reinterpret_cast<const uint32_t*>(st + L.m + P * 256);
       if constexpr (WFMT == 1) {
         F.b[P] = dequant_w4_group(w0, e);
@@ -756,7 +788,7 @@ struct F16Pipe {
   }
   __device__ __forceinline__ static void stage(const Acc& acc, uint8_t* ct, const PipeOut& o,
                                                int n0, int wm, int wn, int lane) {
-    stage16<true, NGT == 0>(acc, ct, o, n0, wm, wn, lane);
+    stage16<true, NGT == 0 && WFMT != 7>(acc, ct, o, n0, wm, wn, lane);
   }
 };
 
@@ -895,6 +927,7 @@ __global__ __launch_bounds__(kThreads) void pipe256_kernel(
   for (int s = 0; s < NST - 1; ++s) issue(s);
   QG_WAIT_VM_BARRIER((NST - 3) * PER);   // steps 0 and 1 landed
   typename Ops::Frags F0, F1;
+  Ops::init(F0, F1);
   pipe_read_all<Ops>(F0, stage(0), L);
 
   // Two steps per iteration, F0 and F1 trading roles; every copy issued in
@@ -929,7 +962,7 @@ __global__ __launch_bounds__(kThreads) void pipe256_kernel(
   PipeOut o;
   o.c = c;
   o.col_scale = col_scale;
-  o.s = (Ops::FMT == 4) ? (*scale_a) * (*scale_b) : 1.0f;
+  o.s = (Ops::FMT == 4) ? (*scale_a) * (*scale_b) : (Ops::FMT == 7) ? *scale_a : 1.0f;
   o.M = g.M;
   o.N = g.N;
   __syncthreads();   // every wave has finished with the last stage
@@ -972,8 +1005,9 @@ hipError_t launch_pipe(const void* a, const void* a_sc, const void* wp, const fl
   g.a_bytes = (uint32_t)(M * a_row);
   g.w_bytes = (uint32_t)pg.codes;
   g.asc_bytes = FMT == 3 ? (uint32_t)(M * (K / 32)) : 0u;
-  g.wsc_bytes = FMT == 3 ? (uint32_t)(pg.total - pg.scales) : 0u;
-  const uint8_t* w_sc = FMT == 3 ? static_cast<const uint8_t*>(wp) + pg.scales : nullptr;
+  g.wsc_bytes = FMT == 3 || FMT == 7 ? (uint32_t)(pg.total - pg.scales) : 0u;
+  const uint8_t* w_sc =
+      FMT == 3 || FMT == 7 ? static_cast<const uint8_t*>(wp) + pg.scales : nullptr;
   if constexpr (Ops::GROUP_WORDS > 0) {
     const PackGeom gg = grouped_geom(FMT == 1 ? 5 : 6, K, N, group_k);
     g.wsc_bytes = (uint32_t)(gg.total - gg.scales);
@@ -1035,6 +1069,13 @@ hipError_t launch_weight_only_tile_grouped(int fmt, const void* x, const void* w
   }
 #undef QG_GROUPED
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_weight_only_tile_nvfp4(const void* x, const void* w_packed,
+                                        const float* global_scale, void* y, int64_t M, int64_t N,
+                                        int64_t K, hipStream_t stream) {
+  return launch_pipe<F16Pipe<7>>(x, nullptr, w_packed, global_scale, nullptr, nullptr, y, M, N, K,
+                                 stream);
 }
 
 hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const void* w_packed,

@@ -88,3 +88,38 @@ def test_nvfp4_decode_full_size_sampled(m):
     y_ref, bound = oracle.gemm_nvfp4(x, codes[cols], scales[cols], g)
     ok = oracle.within_tolerance(y[:, cols], y_ref, bound)
     assert ok.all(), f"{int((~ok).sum())} outside tolerance"
+
+
+# M >= 256 and N > 128 take the LDS-tiled matrix-core kernel.
+TILE_CASES = [
+    (256, 256, 200),      # two K tiles, ragged N
+    (300, 1056, 520),     # ragged M and N, K = 8.25 tiles
+    (257, 48, 136),       # K below one tile (four-stage ring)
+    (512, 2048, 384),
+]
+
+
+@pytest.mark.parametrize("m,k,n", TILE_CASES)
+def test_nvfp4_tile_matches_oracle(m, k, n):
+    case_id("nvfp4 tile", m, k, n)
+    x, codes, scales, g = wl.nvfp4_weight(m, k, n, seed=m + k + n)
+    y_ref, bound = oracle.gemm_nvfp4(x, codes, scales, g)
+    y = run(x, codes, scales, g, k, n)
+    ok = oracle.within_tolerance(y, y_ref, bound)
+    assert ok.all(), f"{int((~ok).sum())} outside tolerance"
+
+
+def test_nvfp4_tile_one_hot_reads_back_every_weight():
+    """The tiled kernel (M = K = 384 > 256, N = 200): X = identity, global
+    scale 1, Y = fp16(e2m1 * e4m3) for every weight, bit-exact; every step
+    of a tile picks its own scale byte."""
+    k, n = 384, 200
+    case_id("nvfp4 tile one-hot", k, n)
+    rng = np.random.default_rng(21)
+    codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(n, k // 16), dtype=np.uint8)
+    scales[0, :] = np.arange(k // 16, dtype=np.uint8)
+    scales[1, :] = 0x7E
+    wdeq = oracle.round_fp16(oracle.dequant_nvfp4(codes, scales, 1.0))
+    y = run(np.eye(k, dtype=np.float16), codes, scales, np.float32(1.0), k, n)
+    assert np.array_equal(y, wdeq.T)
