@@ -15,43 +15,56 @@ namespace {
 // An element's grid index is the number of midpoints {0.25, 0.75, 1.25, 1.75,
 // 2.5, 3.5, 5} * 2^e that |x| exceeds strictly -- nearest grid point, with an
 // exact tie going to the smaller magnitude.  Every threshold is exact in fp32.
-__global__ void quantize_mxfp4_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
-                                      uint8_t* __restrict__ e8m0, int64_t rows, int64_t K) {
-  const int64_t nblk = K / 32;
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= rows * nblk) return;
-  const int64_t row = b / nblk;
-  const int64_t kb = b - row * nblk;
-  const floatx4* src = reinterpret_cast<const floatx4*>(x + row * K + 32 * kb);
-  float v[32];
+// Blocks are consecutive in memory (row-major [rows, K], K % 32 == 0), so
+// the input is a flat array of 128-byte blocks.  Eight lanes share a block,
+// each reading 16 bytes (a wave reads 1 KB of whole cache lines per load);
+// a workgroup takes kQBlocksPerLane rounds of 32 blocks and issues all its
+// loads first.  The block max is reduced over the eight lanes; each lane
+// forms the codes of its 4 elements (2 bytes of the block's 16) and lane
+// pairs store 4 bytes.
+constexpr int kQBlocksPerLane = 4;
+
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const float* __restrict__ x,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ e8m0,
+                                                             int64_t nblocks) {
+  const int part = (int)(threadIdx.x & 7);   // elements 4 part .. 4 part + 3 of a block
+  const int64_t b0 = (int64_t)blockIdx.x * (32 * kQBlocksPerLane) + (threadIdx.x >> 3);
+  floatx4 v[kQBlocksPerLane];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const floatx4 t = src[i];
-    v[4 * i + 0] = t[0];
-    v[4 * i + 1] = t[1];
-    v[4 * i + 2] = t[2];
-    v[4 * i + 3] = t[3];
+  for (int j = 0; j < kQBlocksPerLane; ++j) {
+    const int64_t b = b0 + 32 * j;   // uniform over the 8 lanes of a block
+    v[j] = b < nblocks ? __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(x) + 8 * b + part)
+                       : floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  amax = fmaxf(amax, 1e-8f);
-  const uint32_t bits = __builtin_bit_cast(uint32_t, amax);
-  const int e0 = (int)(bits >> 23) - 127;
-  const int e = e0 - 2 + ((bits & 0x7fffffu) > 0x400000u ? 1 : 0);
-  const float p2 = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);  // 2^e, normal
-  const float t0 = 0.25f * p2, t1 = 0.75f * p2, t2 = 1.25f * p2, t3 = 1.75f * p2;
-  const float t4 = 2.5f * p2, t5 = 3.5f * p2, t6 = 5.0f * p2;
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int j = 0; j < kQBlocksPerLane; ++j) {
+    const int64_t b = b0 + 32 * j;
+    float amax = fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    amax = fmaxf(amax, 1e-8f);
+    const uint32_t bits = __builtin_bit_cast(uint32_t, amax);
+    const int e0 = (int)(bits >> 23) - 127;
+    const int e = e0 - 2 + ((bits & 0x7fffffu) > 0x400000u ? 1 : 0);
+    const float p2 = __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);  // 2^e, normal
+    const float t0 = 0.25f * p2, t1 = 0.75f * p2, t2 = 1.25f * p2, t3 = 1.75f * p2;
+    const float t4 = 2.5f * p2, t5 = 3.5f * p2, t6 = 5.0f * p2;
+    uint32_t w = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float a = fabsf(v[i]);
-    uint32_t idx = (a > t0) + (a > t1) + (a > t2) + (a > t3) + (a > t4) + (a > t5) + (a > t6);
-    const uint32_t code = idx | (v[i] < 0.f ? 8u : 0u);
-    w[i >> 3] |= code << (4 * (i & 7));  // element 2j -> low nibble of byte j
+    for (int i = 0; i < 4; ++i) {
+      const float a = fabsf(v[j][i]);
+      const uint32_t idx =
+          (a > t0) + (a > t1) + (a > t2) + (a > t3) + (a > t4) + (a > t5) + (a > t6);
+      w |= (idx | (v[j][i] < 0.f ? 8u : 0u)) << (4 * i);   // element 2j -> low nibble of byte j
+    }
+    // lanes 2q and 2q + 1 hold bytes 4q .. 4q + 3 of the block's codes
+    const uint32_t pair = w | (__shfl_xor(w, 1, 64) << 16);
+    if (b < nblocks && (part & 1) == 0)
+      __builtin_nontemporal_store(pair, reinterpret_cast<uint32_t*>(codes + 16 * b + 2 * part));
+    if (b < nblocks && part == 0) e8m0[b] = (uint8_t)(e + 127);
   }
-  *reinterpret_cast<uintx4*>(codes + row * (K / 2) + 16 * kb) = uintx4{w[0], w[1], w[2], w[3]};
-  e8m0[row * nblk + kb] = (uint8_t)(e + 127);
 }
 
 // ---------------------------------------------------------------------------
@@ -188,9 +201,8 @@ hipError_t launch_quantize_mxfp4(const float* x, int64_t rows, int64_t K, uint8_
                                  uint8_t* e8m0, hipStream_t stream) {
   const int64_t blocks = rows * (K / 32);
   if (blocks == 0) return hipSuccess;
-  const int threads = 256;
-  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3((unsigned)cdiv(blocks, threads)),
-                     dim3(threads), 0, stream, x, codes, e8m0, rows, K);
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3((unsigned)cdiv(blocks, 32 * kQBlocksPerLane)),
+                     dim3(256), 0, stream, x, codes, e8m0, blocks);
   return hipGetLastError();
 }
 
