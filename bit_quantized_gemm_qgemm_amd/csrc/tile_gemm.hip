@@ -470,7 +470,8 @@ struct Fp4Pipe {
   static constexpr int STAGE = kStageA + B + SA + SB;
   static constexpr int DMA = 10;
   static constexpr int NST = 4;                  // 4 x 34 KB of LDS
-  static constexpr int CP_PAIRS = 6;             // copies of parts 0 / 1: 4 / 6
+  static constexpr bool CP_INTERLEAVE = true;
+  static constexpr int CP_PIN_PAIRS = 6;         // copies of parts 0 / 1: 4 / 6
   typedef floatx16 Acc[4][4];
   struct Frags {
     uintx4 alo[4], ahi[4];
@@ -581,7 +582,8 @@ struct Fp8Pipe {
   static constexpr int STAGE = kStageA + B;
   static constexpr int DMA = 8;
   static constexpr int NST = 4;                  // 4 x 32 KB
-  static constexpr int CP_PAIRS = 4;             // copies of parts 0 / 1: 4 / 4
+  static constexpr bool CP_INTERLEAVE = true;
+  static constexpr int CP_PIN_PAIRS = 4;         // copies of parts 0 / 1: 4 / 4
   typedef floatx16 Acc[4][4];
   struct Frags {
     uintx4 alo[4], ahi[4];
@@ -682,9 +684,11 @@ struct F16Pipe {
   static constexpr int DMA = 4 + 4 * WV + (META ? 4 : 0);
   // 8 x 20 KB or 6 x 24 KB; with metadata: 6 x 24 KB or 4 x 28 KB
   static constexpr int NST = META ? (WV == 1 ? 6 : 4) : (WV == 1 ? 8 : 6);
-  // copies issued ahead of the step: pinning them between the matrix
-  // instructions makes these kernels spill
-  static constexpr int CP_PAIRS = 0;
+  // copies issued inside parts 0 and 1 but not pinned between the matrix
+  // instructions (pinning made the register allocator spill); 2-5% faster
+  // than issuing them ahead of the step
+  static constexpr bool CP_INTERLEAVE = true;
+  static constexpr int CP_PIN_PAIRS = 0;
   typedef floatx4 Acc[8][8];
   struct Frags {
     uintx4 a[8];
@@ -800,9 +804,10 @@ struct NoCopies {
 // One part: read fragment P of the next step (RD), then the matrix work of
 // fragment P of the current step; the scheduler keeps the two together.
 // With CP, parts 0 and 1 also issue the copies of a later step (cp(0): the A
-// slices, cp(1): the rest), pinned to alternate with the part's matrix
-// instructions: issuing them all ahead of the step kept the matrix pipe idle
-// after every barrier.
+// slices, cp(1): the rest), after the part's matrix instructions in program
+// order and, where the policy asks (CP_PIN_PAIRS), pinned to alternate with
+// them: issuing them all ahead of the step kept the matrix pipe idle after
+// every barrier.
 template <class Ops, int P, bool RD, bool CP, class Copies>
 __device__ __forceinline__ void pipe_part(typename Ops::Frags& cur, typename Ops::Frags& nxt,
                                           const uint8_t* nx, const typename Ops::Lane& L,
@@ -812,7 +817,7 @@ __device__ __forceinline__ void pipe_part(typename Ops::Frags& cur, typename Ops
   if constexpr (CP && P <= 1) {
     cp(P);
 #pragma unroll
-    for (int i = 0; i < Ops::CP_PAIRS; ++i) {
+    for (int i = 0; i < Ops::CP_PIN_PAIRS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one vector memory read
     }
@@ -936,7 +941,9 @@ __global__ __launch_bounds__(kThreads) void pipe256_kernel(
   // step_issuing(cur, nxt, r, s): compute with cur, read step r into nxt,
   // issue the copies of step s
   auto step_issuing = [&](typename Ops::Frags& cur, typename Ops::Frags& nxt, int r, int s) {
-    if constexpr (Ops::CP_PAIRS > 0) {
+    // the 4-stage fallback ring of the unpinned (weight-only) kernels keeps
+    // its copies ahead of the step: interleaving them made one spill
+    if constexpr (Ops::CP_INTERLEAVE && !(Ops::CP_PIN_PAIRS == 0 && NST == 4)) {
       uint8_t* st = stage(s);
       auto cp = [&](int part) {
         if (part == 0) pipe_issue_a<Ops>(st, s, wave, lane, m0, row_bytes, rs.a);
