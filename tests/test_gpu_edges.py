@@ -1,0 +1,111 @@
+"""Degenerate shapes on the device, for every GEMM entry point: M = 0 or
+N = 0 leave nothing to compute and must succeed with an empty result; K = 0
+makes every output the empty sum, exactly 0 (on both the small-M and the
+tiled dispatch); an empty tensor quantizes to no codes and the all-zero
+scale rule (1.0)."""
+
+import numpy as np
+import pytest
+import torch
+
+import qgemm_workloads as wl
+import bit_quantized_gemm_qgemm_amd as qg
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    qg.lib()
+    return torch.device("cuda:0")
+
+
+def z(shape, dtype):
+    return torch.zeros(shape, dtype=dtype, device="cuda")
+
+
+def empty_packed():
+    return z((0,), torch.uint8)
+
+
+def case_id(*a):
+    print("case", *a, flush=True)
+
+
+def assert_zero(t, shape):
+    torch.cuda.synchronize()
+    assert tuple(t.shape) == shape
+    assert torch.count_nonzero(t.float()) == 0
+
+
+def test_mxfp4_degenerate():
+    case_id("mxfp4 degenerate")
+    w = torch.from_numpy(wl.mxfp4_operands(1, 32, 64)[1]).cuda()
+    wc, we = qg.qgemm_quantize_mxfp4(w)
+    wp = qg.qgemm_prepack("mxfp4", wc, 64, 32, w_scales=we)
+    assert qg.qgemm_mxfp4(z((0, 32), torch.uint8), z((0, 2), torch.uint8), wp, 32).shape == (0, 32)
+    assert qg.qgemm_mxfp4(z((4, 32), torch.uint8), z((4, 2), torch.uint8), empty_packed(),
+                          0).shape == (4, 0)
+    for m, n in ((20, 24), (200, 136)):
+        assert_zero(qg.qgemm_mxfp4(z((m, 0), torch.uint8), z((m, 0), torch.uint8),
+                                   empty_packed(), n), (m, n))
+
+
+def test_fp8_degenerate():
+    case_id("fp8 degenerate")
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    bp = qg.qgemm_prepack("fp8", z((64, 32), torch.uint8), 64, 32)
+    assert qg.qgemm_fp8(z((0, 64), torch.uint8), bp, one, one, 32).shape == (0, 32)
+    assert qg.qgemm_fp8(z((4, 64), torch.uint8), empty_packed(), one, one, 0).shape == (4, 0)
+    for m, n in ((4, 24), (200, 136)):   # small-M kernel, tiled kernel
+        assert_zero(qg.qgemm_fp8(z((m, 0), torch.uint8), empty_packed(), one, one, n), (m, n))
+
+
+@pytest.mark.parametrize("fmt", ["w4a16_grouped", "w8a16_grouped"])
+def test_grouped_degenerate(fmt):
+    case_id(fmt, "degenerate")
+    fn = qg.qgemm_w4a16_grouped if fmt == "w4a16_grouped" else qg.qgemm_w8a16_grouped
+    gen = wl.w4a16_grouped if fmt == "w4a16_grouped" else wl.w8a16_grouped
+    _, w, s, zp = gen(1, 64, 32, 32)
+    wp = qg.qgemm_prepack_grouped(fmt, torch.from_numpy(w).cuda(), 64, 32,
+                                  torch.from_numpy(s).cuda(), torch.from_numpy(zp).cuda(), 32)
+    assert fn(z((0, 64), torch.float16), wp, 32, 32).shape == (0, 32)
+    assert fn(z((4, 64), torch.float16), empty_packed(), 0, 32).shape == (4, 0)
+    for m, n in ((4, 24), (300, 136)):
+        assert_zero(fn(z((m, 0), torch.float16), empty_packed(), n, 32), (m, n))
+
+
+def test_nvfp4_degenerate():
+    case_id("nvfp4 degenerate")
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+    wp = qg.qgemm_prepack("nvfp4", z((32, 32), torch.uint8), 64, 32, w_scales=z((32, 4), torch.uint8))
+    assert qg.qgemm_nvfp4(z((0, 64), torch.float16), wp, g, 32).shape == (0, 32)
+    assert qg.qgemm_nvfp4(z((4, 64), torch.float16), empty_packed(), g, 0).shape == (4, 0)
+    for m, n in ((4, 24), (300, 136)):
+        assert_zero(qg.qgemm_nvfp4(z((m, 0), torch.float16), empty_packed(), g, n), (m, n))
+
+
+def test_act_degenerate():
+    case_id("act degenerate")
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    bp = qg.qgemm_prepack("fp8", z((64, 32), torch.uint8), 64, 32)
+    c, _ = qg.qgemm_fp8_act(z((0, 64), torch.float32), bp, one, 32)
+    assert c.shape == (0, 32)
+    for m, n in ((4, 24), (200, 136)):
+        c, ws = qg.qgemm_fp8_act(z((m, 0), torch.float32), empty_packed(), one, n)
+        assert_zero(c, (m, n))
+        # the all-zero scale rule applies to an empty A as well
+        assert ws[:4].view(torch.float32).item() == 1.0
+        c, _ = qg.qgemm_mxfp4_act(z((m, 0), torch.float32), empty_packed(), n)
+        assert_zero(c, (m, n))
+
+
+def test_quantizers_empty():
+    case_id("quantizers empty")
+    codes, scale = qg.qgemm_quantize_fp8(z((0,), torch.float32))
+    torch.cuda.synchronize()
+    assert codes.numel() == 0 and scale.item() == 1.0
+    c, e = qg.qgemm_quantize_mxfp4(z((0, 64), torch.float32))
+    assert c.shape == (0, 32) and e.shape == (0, 2)
