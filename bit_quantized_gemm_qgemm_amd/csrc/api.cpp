@@ -92,7 +92,8 @@ int weight_only(int fmt, const void* x, const void* w_packed, const void* scales
   // Large M: LDS-tiled matrix-core kernel (each weight byte is read once per
   // 256 rows).  Otherwise the register-dequant kernel in 16-row slabs, the
   // bandwidth path of decode.
-  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0 && K % 8 == 0)
+  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0 && K % 8 == 0 &&
+      qgemm::pipe_fits(fmt, M, N, K, 0))
     return launched(qgemm::launch_weight_only_tile(fmt, x, w_packed, scales, y, M, N, K,
                                                    as_stream(stream)));
   return launched(qgemm::launch_decode_gemm(fmt, x, w_packed, scales, nullptr, nullptr, y, M, N,
@@ -118,7 +119,7 @@ int grouped_gemm(int fmt, const void* x, const void* w_packed, void* y, int64_t 
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
   // K % 32 == 0 here, so fp16 X rows are 16-byte aligned
-  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0)
+  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0 && qgemm::pipe_fits(fmt, M, N, K, group_k))
     return launched(qgemm::launch_weight_only_tile_grouped(fmt, x, w_packed, y, M, N, K, group_k,
                                                            as_stream(stream)));
   return launched(qgemm::launch_decode_grouped(fmt, x, w_packed, y, M, N, K, group_k,
@@ -201,7 +202,7 @@ int qgemm_nvfp4(const void* x, const void* w_packed, const float* global_scale, 
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
   // K % 16 == 0 here, so fp16 X rows are 16-byte aligned
-  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0)
+  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0 && qgemm::pipe_fits(QGEMM_NVFP4, M, N, K, 0))
     return launched(qgemm::launch_weight_only_tile_nvfp4(x, w_packed, global_scale, y, M, N, K,
                                                          as_stream(stream)));
   return launched(qgemm::launch_decode_nvfp4(x, w_packed, global_scale, y, M, N, K,

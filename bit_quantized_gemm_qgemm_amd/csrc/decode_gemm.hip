@@ -1,4 +1,5 @@
-// Small-M GEMM with in-register dequantization (W4A16, W8A16, FP8).
+// Small-M GEMM with in-register dequantization (W4A16 and W8A16 with per-column
+// or group-wise scales, NVFP4 weights, FP8).
 //
 // The bandwidth-bound shape of the W4A16 page (section 1: every decode step
 // streams the whole weight) and of the W8A16 page (Steps 1-2: load the low-bit
@@ -14,8 +15,9 @@
 // of loads in flight in a register ring and its fp32 partial sums in
 // registers; the workgroup reduces them through LDS in a fixed order
 // (deterministic, no atomics, no workspace) and the epilogue applies the
-// per-column scale (or the per-tensor FP8 scales) once to the fp32 sum before
-// rounding to the output type.
+// per-column scale (or the per-tensor FP8 / NVFP4 scales) once to the fp32
+// sum before rounding to the output type; the grouped formats apply their
+// scales in the dequant, before the matrix instruction.
 //
 // K order inside a 128-wide tile (fp16 formats): matrix step s (0..3) of lane
 // group g = lane >> 4 covers k = 32 s + 8 g + [0, 8).  Both operands use the

@@ -79,7 +79,7 @@ struct PackGeom {
   int64_t kt;      // K tiles
   int64_t tile;    // bytes per code tile
   int64_t codes;   // bytes of the code segment
-  int64_t scales;  // offset of the scale segment (MXFP4) or 0
+  int64_t scales;  // offset of the scale (MXFP4, NVFP4) or metadata (grouped) segment, or 0
   int64_t total;   // total bytes
 };
 
@@ -165,6 +165,12 @@ hipError_t launch_decode_nvfp4(const void* x, const void* w_packed, const float*
 hipError_t launch_decode_grouped(int fmt, const void* x, const void* w_packed, void* y,
                                  int64_t M, int64_t N, int64_t K, int64_t group_k,
                                  hipStream_t stream);
+
+// Whether the operands of a format-`fmt` GEMM (group_k for formats 5 and 6)
+// fit the 256 x 256 kernels, whose buffer descriptors take 32-bit offsets
+// (every operand below 2^31 bytes).  Larger ones take the kernels that
+// address with 64 bits (the 128 x 128 tile kernel, the small-M kernel).
+bool pipe_fits(int fmt, int64_t M, int64_t N, int64_t K, int64_t group_k);
 
 // LDS-tiled matrix-core path for W4A16 / W8A16 at large M (fp16 X with K a
 // positive multiple of 8; 256 x 256 output tiles).

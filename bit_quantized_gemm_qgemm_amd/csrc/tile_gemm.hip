@@ -1,16 +1,20 @@
-// LDS-tiled matrix-core GEMM for MXFP4 x MXFP4 and FP8 e4m3fn (any M).
+// LDS-tiled matrix-core GEMMs: MXFP4 x MXFP4 and FP8 e4m3fn at any M, and the
+// weight-only formats (INT4 / INT8 per column or grouped, NVFP4 weights; fp16
+// X) at large M.
 //
 // The MXFP4 page (section 2) tiles C into B_M x B_N blocks per workgroup and
 // sums, per 32-element micro-block, S_A * S_W * dot(A, W) (eq. 1) with the
 // scale product done as an exponent add (eq. 2).  On gfx950 that whole step is
-// one instruction: v_mfma_scale_f32_16x16x128_f8f6f4 takes 128 K-elements of
-// FP4 (or FP8) codes per lane group and one E8M0 byte per lane, applies
-// 2^(E_A-127) * 2^(E_W-127) to each 32-element block product in hardware and
-// accumulates in fp32.  FP8 (FP8 page) uses the same instruction with e4m3
-// operands and unit scales; its per-tensor scales multiply the fp32 result
-// once in the epilogue.
+// one instruction: v_mfma_scale_f32_16x16x128_f8f6f4 (here in the 128 x 128
+// kernel; the 256 x 256 kernels below use its 32 x 32 x 64 form) takes FP4
+// (or FP8) codes and one E8M0 byte per lane, applies 2^(E_A-127) *
+// 2^(E_W-127) to each 32-element block product in hardware and accumulates in
+// fp32.  FP8 (FP8 page) uses the same instruction with e4m3 operands and unit
+// scales; its per-tensor scales multiply the fp32 result once in the
+// epilogue.
 //
-// Data flow per K step (128 bytes of K per row: 256 FP4 or 128 FP8 elements):
+// 128 x 128 kernel, data flow per K step (128 bytes of K per row: 256 FP4 or
+// 128 FP8 elements):
 //   A (row-major activations) -> LDS, 16-byte chunks XOR-swizzled by row so
 //     that both the row-wise stores and the fragment reads are bank-conflict
 //     free;
@@ -275,10 +279,11 @@ __global__ __launch_bounds__(kThreads) void tile_gemm_kernel(
 // and K chunks past K read as zero without predication.
 //
 // Schedule per step ks (one barrier per step):
-//   - issue the global->LDS copies of step ks+3;
 //   - run the step's matrix instructions from registers, and in between read
 //     the fragments of step ks+1 from LDS into a second register set, so the
 //     LDS latency hides behind matrix work;
+//   - in the step's first two parts, issue the global->LDS copies of step
+//     ks+3 (into the stage whose fragments were read one step earlier);
 //   - wait until this wave's copies of step ks+2 have landed (those of ks+3
 //     stay in flight) and meet at the barrier.
 // The barrier is issued without the full memory drain that __syncthreads()
@@ -1045,6 +1050,15 @@ hipError_t launch_tiles(const void* a, const void* a_sc, const void* wp, const f
 
 }  // namespace
 
+bool pipe_fits(int fmt, int64_t M, int64_t N, int64_t K, int64_t group_k) {
+  const int64_t lim = kOutOfRange;
+  const int64_t a_row = fmt == 3 ? K / 2 : fmt == 4 ? K : 2 * K;
+  if (M * a_row >= lim || (fmt == 3 && M * (K / 32) >= lim)) return false;
+  const PackGeom g =
+      fmt == 5 || fmt == 6 ? grouped_geom(fmt, K, N, group_k) : pack_geom(fmt, K, N);
+  return g.total < lim;   // the code segment and any scale or metadata segment
+}
+
 hipError_t launch_weight_only_tile(int fmt, const void* x, const void* w_packed,
                                   const void* scales, void* y, int64_t M, int64_t N, int64_t K,
                                   hipStream_t stream) {
@@ -1092,7 +1106,7 @@ hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const vo
   // two 256-element tiles; the 128 x 128 kernel covers the rest (and MXFP4 K
   // that is not a multiple of 128, whose scale rows the 4-byte copies of the
   // large kernel cannot split)
-  const bool big = M > 128 && N > 128 && cdiv(K, kTileK8) >= 2;
+  const bool big = M > 128 && N > 128 && cdiv(K, kTileK8) >= 2 && pipe_fits(fmt, M, N, K, 0);
   if (fmt == 3) {
     if (big && K % 128 == 0 && cdiv(K, kTileK4) >= 2)
       return launch_pipe<Fp4Pipe>(a, a_e8m0, w_packed, scale_a, scale_b, nullptr, c, M, N, K,

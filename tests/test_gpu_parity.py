@@ -521,3 +521,25 @@ def test_fp8_full_size_sampled(m):
     ci = np.searchsorted(uc, cols)
     got = host(c[torch.from_numpy(rows), torch.from_numpy(cols)])
     assert np.all(oracle.within_tolerance(got, c_ref[ri, ci], bound[ri, ci]))
+
+
+def test_weight_only_activations_over_2gib():
+    """X of 2.7 GB (M = 40960, K = 32776 with a ragged last K tile, fp16):
+    too large for the 32-bit buffer offsets of the 256 x 256 kernels, so the
+    call takes a kernel that addresses with 64 bits; rows on both sides of
+    the 2^31-byte mark (row 32760) match the oracle."""
+    m, k = 40960, 32776
+    n = 256
+    case_id("w8a16 X over 2 GiB", m, k, n)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn((m, k), generator=g, device="cuda", dtype=torch.float32).half()
+    _, w, s = wl.w8a16(1, k, n, seed=11)
+    y = qg.qgemm_w8a16(x, qg.qgemm_prepack("w8a16", dev(w), k, n), dev(s), n)
+    mark = (1 << 31) // (2 * k)
+    rows = np.array([0, 1, mark - 1, mark, mark + 1, m - 1])
+    xr = x[torch.from_numpy(rows).cuda()].cpu().numpy()
+    y_ref, bound = oracle.gemm_w8a16(xr, w, s)
+    assert_within(y[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64), y_ref, bound,
+                  "w8a16 X over 2 GiB")
+    del x, y
+    torch.cuda.empty_cache()
