@@ -8,6 +8,11 @@
  *   MXFP4  C[M,N] = A[M,K] * W[N,K]^T              E2M1 codes, one E8M0
  *                                                  exponent per 32 K-elements
  *   FP8    C[M,N] = (A[M,K] * B[K,N]) * sa * sb    e4m3fn, per-tensor scales
+ * and their extensions: W4A16 / W8A16 with group-wise scales and zero points
+ * (qgemm_w4a16_grouped, qgemm_w8a16_grouped), NVFP4 weights with fp16
+ * activations (qgemm_nvfp4), and MXFP4 / FP8 GEMMs that quantize fp32
+ * activations on the device inside the call (qgemm_mxfp4_act,
+ * qgemm_fp8_act).
  *
  * Sources (short names):
  *   W4A16 page -- "Triton W4A16 blocked GEMM and Blackwell NVFP4"
@@ -32,8 +37,9 @@
  *   - Arguments are checked on the host before anything is launched.  A
  *     status < 0 means nothing was enqueued (except QGEMM_ERR_LAUNCH, which
  *     reports a failed launch).  No entry point prints or throws.
- *   - M == 0 or N == 0 is a valid no-op.  Results are deterministic: the same
- *     inputs give bit-identical outputs (no atomics in any GEMM).
+ *   - M == 0 or N == 0 is a valid no-op; K == 0 writes the empty sum, an
+ *     all-zero output.  Results are deterministic: the same inputs give
+ *     bit-identical outputs (no atomics in any GEMM).
  *   - Accumulation is fp32; the output is rounded to nearest-even once.
  */
 #ifndef QGEMM_H
