@@ -54,9 +54,11 @@ template <> struct DecodeTraits<4> {
 
 // NGT > 0: grouped formats, NGT metadata words {1024 + z (+128), s} per
 // column and K tile (layout in qgemm_common.h).
-template <int FMT, int G, int NGT = 0>
+// S: 16-row slabs of X per workgroup (each weight tile, loaded and
+// dequantized once, multiplies the rows of all S slabs).
+template <int FMT, int G, int NGT = 0, int S = 1>
 struct Chunk {
-  uintx4 x[DecodeTraits<FMT>::XV];
+  uintx4 x[S][DecodeTraits<FMT>::XV];
   uintx4 w[G][DecodeTraits<FMT>::WV];
   uint32_t meta[G][NGT > 0 ? NGT : 1];
 };
@@ -65,7 +67,7 @@ struct Chunk {
 // parts stay in SGPRs; each lane adds a 32-bit offset.
 struct DecodeAddr {
   const uint8_t* x;       // activations
-  uint32_t xlane;         // byte offset of this lane's row and first K piece
+  uint32_t xlane[4];      // per slab: byte offset of this lane's row and first K piece
   const uint8_t* w;       // first weight tile of this workgroup
   int64_t cg_stride;      // bytes between column groups
   int cg_last;            // last valid group index relative to this workgroup
@@ -89,8 +91,9 @@ __device__ __forceinline__ int piece_k(int kt, int g, int p) {
 // weight tiles.  X pieces past K read as zero.  Rows past M load row M-1
 // instead (their outputs are never stored); groups past the last column load
 // the last group (likewise discarded).
-template <int FMT, int G, bool X_ELEMENTWISE, int NGT = 0>
-__device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT>& ch, const DecodeAddr& ad, int kt) {
+template <int FMT, int G, bool X_ELEMENTWISE, int NGT = 0, int S = 1>
+__device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const DecodeAddr& ad,
+                                           int kt) {
   constexpr int XV = DecodeTraits<FMT>::XV;
   constexpr int TB = DecodeTraits<FMT>::TB;
   constexpr int XB = (FMT == 4) ? 1 : 2;           // bytes per activation element
@@ -100,20 +103,26 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT>& ch, const DecodeA
   if constexpr (!X_ELEMENTWISE) {
     if (full) {
 #pragma unroll
-      for (int p = 0; p < XV; ++p)
-        ch.x[p] = *reinterpret_cast<const uintx4*>(xk + ad.xlane + PSTRIDE * p);
+      for (int q = 0; q < S; ++q)
+#pragma unroll
+        for (int p = 0; p < XV; ++p)
+          ch.x[q][p] = *reinterpret_cast<const uintx4*>(xk + ad.xlane[q] + PSTRIDE * p);
     } else {
       // K % 8 == 0 (fp16) or K % 16 == 0 (e4m3): a piece is wholly in or out
 #pragma unroll
-      for (int p = 0; p < XV; ++p) {
-        const int k = piece_k<FMT>(kt, ad.g, p);
-        ch.x[p] = (k < ad.K) ? *reinterpret_cast<const uintx4*>(xk + ad.xlane + PSTRIDE * p)
-                             : uintx4{0, 0, 0, 0};
-      }
+      for (int q = 0; q < S; ++q)
+#pragma unroll
+        for (int p = 0; p < XV; ++p) {
+          const int k = piece_k<FMT>(kt, ad.g, p);
+          ch.x[q][p] = (k < ad.K)
+                           ? *reinterpret_cast<const uintx4*>(xk + ad.xlane[q] + PSTRIDE * p)
+                           : uintx4{0, 0, 0, 0};
+        }
     }
   } else {
     // K % 8 != 0 (fp16 only): rows are not 16-byte aligned; go element-wise
-    const uint16_t* xr = reinterpret_cast<const uint16_t*>(xk + ad.xlane);
+    static_assert(S == 1, "the element-wise X path takes one slab");
+    const uint16_t* xr = reinterpret_cast<const uint16_t*>(xk + ad.xlane[0]);
 #pragma unroll
     for (int p = 0; p < XV; ++p) {
       uint32_t d[4];
@@ -125,7 +134,7 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT>& ch, const DecodeA
         const uint32_t hi = (k + 1 < ad.K) ? xr[e + 1] : 0u;
         d[j] = lo | (hi << 16);
       }
-      ch.x[p] = uintx4{d[0], d[1], d[2], d[3]};
+      ch.x[0][p] = uintx4{d[0], d[1], d[2], d[3]};
     }
   }
 #pragma unroll
@@ -153,24 +162,27 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT>& ch, const DecodeA
   }
 }
 
-template <int FMT, int G, int NGT = 0>
-__device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT>& ch, floatx4 (&acc)[G],
-                                              W4Masks mk) {
+template <int FMT, int G, int NGT = 0, int S = 1>
+__device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
+                                              floatx4 (&acc)[S][G], W4Masks mk) {
   if constexpr (FMT == 4) {
-    const intx8 a = {(int)ch.x[0][0], (int)ch.x[0][1], (int)ch.x[0][2], (int)ch.x[0][3],
-                     (int)ch.x[1][0], (int)ch.x[1][1], (int)ch.x[1][2], (int)ch.x[1][3]};
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const intx8 b = {(int)ch.w[g][0][0], (int)ch.w[g][0][1], (int)ch.w[g][0][2],
                        (int)ch.w[g][0][3], (int)ch.w[g][1][0], (int)ch.w[g][1][1],
                        (int)ch.w[g][1][2], (int)ch.w[g][1][3]};
-      acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          a, b, acc[g], kFmtFP8, kFmtFP8, 0, kE8M0One, 0, kE8M0One);
+#pragma unroll
+      for (int q = 0; q < S; ++q) {
+        const intx8 a = {(int)ch.x[q][0][0], (int)ch.x[q][0][1], (int)ch.x[q][0][2],
+                         (int)ch.x[q][0][3], (int)ch.x[q][1][0], (int)ch.x[q][1][1],
+                         (int)ch.x[q][1][2], (int)ch.x[q][1][3]};
+        acc[q][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            a, b, acc[q][g], kFmtFP8, kFmtFP8, 0, kE8M0One, 0, kE8M0One);
+      }
     }
   } else {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const half8_t a = __builtin_bit_cast(half8_t, ch.x[s]);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         half8_t b;
@@ -191,7 +203,10 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT>& ch, floa
           const uintx4& h = ch.w[g][s >> 1];
           b = dequant_w8(h[2 * (s & 1)], h[2 * (s & 1) + 1]);
         }
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[g], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < S; ++q)
+          acc[q][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(half8_t, ch.x[q][s]), b, acc[q][g], 0, 0, 0);
       }
     }
   }
@@ -199,7 +214,8 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT>& ch, floa
 
 // NGT > 0: grouped W4A16 / W8A16 (scales and zero points in the metadata
 // segment at wp + meta_offset; `scales` unused).
-template <int FMT, int G, int NW, int D, bool X_ELEMENTWISE, int NGT = 0>
+// S: 16-row slabs per workgroup (rows m0 .. m0 + 16 S - 1).
+template <int FMT, int G, int NW, int D, bool X_ELEMENTWISE, int NGT = 0, int S = 1>
 __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ wp,
     const _Float16* __restrict__ scales, const float* __restrict__ scale_a,
@@ -207,6 +223,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
     int CG, int64_t meta_offset) {
   static_assert(NW >= 2, "the K split needs at least two waves");
   static_assert(D >= 2 && D <= 4, "prefetch depth 2..4");
+  static_assert(S == 1 || S == 2 || S == 4, "1, 2 or 4 slabs");
   constexpr int TB = DecodeTraits<FMT>::TB;
   constexpr int XB = (FMT == 4) ? 1 : 2;
   __shared__ floatx4 red[NW][G][kWave];
@@ -214,13 +231,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int cg0 = blockIdx.x * G;
-  const int m0 = blockIdx.y * 16;
-  const int row = min(m0 + (lane & 15), M - 1);
+  const int m0 = blockIdx.y * 16 * S;
 
   DecodeAddr ad;
   ad.g = lane >> 4;
   ad.x = x;
-  ad.xlane = (uint32_t)(((int64_t)row * K + (FMT == 4 ? 32 : 8) * ad.g) * XB);
+  // rows past M load row M - 1 (their outputs are never stored)
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    const int row = min(m0 + 16 * q + (lane & 15), M - 1);
+    ad.xlane[q] = (uint32_t)(((int64_t)row * K + (FMT == 4 ? 32 : 8) * ad.g) * XB);
+  }
   ad.cg_stride = (int64_t)KT * TB;
   ad.w = wp + (int64_t)cg0 * ad.cg_stride;
   ad.cg_last = CG - 1 - cg0;
@@ -237,57 +258,66 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   W4Masks mk{};
   if constexpr (FMT == 1) mk = W4Masks{vgpr_const(0x000f000fu), vgpr_const(0x00f000f0u)};
 
-  floatx4 acc[G];
+  floatx4 acc[S][G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) acc[g] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < S; ++q)
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[q][g] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // K tiles wave, wave + NW, ...; a ring of D register buffers keeps D tiles
   // of loads in flight per wave
-  Chunk<FMT, G, NGT> ring[D];
+  Chunk<FMT, G, NGT, S> ring[D];
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (wave + d * NW < KT) load_chunk<FMT, G, X_ELEMENTWISE, NGT>(ring[d], ad, wave + d * NW);
+    if (wave + d * NW < KT)
+      load_chunk<FMT, G, X_ELEMENTWISE, NGT, S>(ring[d], ad, wave + d * NW);
   for (int base = wave; base < KT; base += D * NW) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int kt = base + d * NW;
       if (kt < KT) {
-        compute_chunk<FMT, G, NGT>(ring[d], acc, mk);
-        if (kt + D * NW < KT) load_chunk<FMT, G, X_ELEMENTWISE, NGT>(ring[d], ad, kt + D * NW);
+        compute_chunk<FMT, G, NGT, S>(ring[d], acc, mk);
+        if (kt + D * NW < KT)
+          load_chunk<FMT, G, X_ELEMENTWISE, NGT, S>(ring[d], ad, kt + D * NW);
       }
     }
   }
 
-  // ---- reduce the NW partial tiles in a fixed order
-#pragma unroll
-  for (int g = 0; g < G; ++g) red[wave][g][lane] = acc[g];
-  __syncthreads();
+  // ---- reduce the NW partial tiles in a fixed order, one slab at a time
   const float fp8_scale = (FMT == 4) ? (*scale_a) * (*scale_b) : (FMT == 7) ? *scale_a : 1.0f;
   const float* redf = reinterpret_cast<const float*>(&red[0][0][0]);
   constexpr int OUT = 16 * 16 * G;
-  // consecutive threads take consecutive columns of one row (coalesced store);
-  // the 16x16 accumulator of a wave holds row 4*(lane>>4)+i, column lane&15
-  for (int o = threadIdx.x; o < OUT; o += NW * kWave) {
-    const int m = o / (16 * G);
-    const int nl = o - m * (16 * G);
-    const int g = nl >> 4;
-    const int c = nl & 15;
-    const int src_lane = 16 * (m >> 2) + c;
-    const int i = m & 3;
-    float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) sum += redf[((w * G + g) * kWave + src_lane) * 4 + i];
-    const int gm = m0 + m;
-    const int gn = (cg0 + g) * 16 + c;
-    if (gm < M && gn < N) {
-      if constexpr (FMT == 4) {
-        y[(int64_t)gm * N + gn] = f32_to_bf16_rne(sum * fp8_scale);
-      } else if constexpr (FMT == 7) {
-        y[(int64_t)gm * N + gn] = f32_to_f16_bits(sum * fp8_scale);   // per-tensor scale
-      } else if constexpr (NGT > 0) {
-        y[(int64_t)gm * N + gn] = f32_to_f16_bits(sum);   // scales already applied
-      } else {
-        y[(int64_t)gm * N + gn] = f32_to_f16_bits((float)scales[gn] * sum);
+  for (int q = 0; q < S; ++q) {
+    if (q > 0) __syncthreads();   // every thread has read the previous slab's partials
+#pragma unroll
+    for (int g = 0; g < G; ++g) red[wave][g][lane] = acc[q][g];
+    __syncthreads();
+    // consecutive threads take consecutive columns of one row (coalesced
+    // store); the 16x16 accumulator of a wave holds row 4*(lane>>4)+i,
+    // column lane&15
+    for (int o = threadIdx.x; o < OUT; o += NW * kWave) {
+      const int m = o / (16 * G);
+      const int nl = o - m * (16 * G);
+      const int g = nl >> 4;
+      const int c = nl & 15;
+      const int src_lane = 16 * (m >> 2) + c;
+      const int i = m & 3;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += redf[((w * G + g) * kWave + src_lane) * 4 + i];
+      const int gm = m0 + 16 * q + m;
+      const int gn = (cg0 + g) * 16 + c;
+      if (gm < M && gn < N) {
+        if constexpr (FMT == 4) {
+          y[(int64_t)gm * N + gn] = f32_to_bf16_rne(sum * fp8_scale);
+        } else if constexpr (FMT == 7) {
+          y[(int64_t)gm * N + gn] = f32_to_f16_bits(sum * fp8_scale);   // per-tensor scale
+        } else if constexpr (NGT > 0) {
+          y[(int64_t)gm * N + gn] = f32_to_f16_bits(sum);   // scales already applied
+        } else {
+          y[(int64_t)gm * N + gn] = f32_to_f16_bits((float)scales[gn] * sum);
+        }
       }
     }
   }
@@ -297,6 +327,7 @@ struct DecodeConfig {
   int g;   // column groups (of 16) per workgroup
   int nw;  // waves per workgroup (K split)
   int d;   // K tiles in flight per wave
+  int s;   // 16-row slabs per workgroup
 };
 
 // Launch shape: about one workgroup per CU.  Measured on MI355X at the decode
@@ -306,24 +337,30 @@ struct DecodeConfig {
 // smaller workgroups leave the CUs unevenly loaded and fewer leave CUs idle.
 // G is capped by the register budget (8 for INT4, 4 for the byte formats);
 // INT8 keeps three K tiles in flight, the others two; short K uses four
-// waves.
+// waves.  Above 16 rows a workgroup takes 2 (M <= 32) or 4 slabs, so each
+// weight tile is streamed and dequantized once for up to 64 rows instead of
+// once per 16; the activations of all slabs then share the register ring,
+// which caps G and the ring at two tiles.  INT4 keeps 2 slabs at every M:
+// with 4 slabs G could not exceed 3 and the grid of its wide weights grew to
+// 2.3 workgroups per CU (K = 8192, N = 28672, M = 64: 106 us against 68 us).
 DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
-  (void)M;
-  const int64_t gmax = fmt == 1 ? 8 : 4;
+  const int s = M <= 16 ? 1 : (M <= 32 || fmt == 1) ? 2 : 4;
+  const int64_t gmax = s == 1 ? (fmt == 1 ? 8 : 4) : s == 2 ? (fmt == 1 ? 7 : 4) : 3;
   int64_t g = cdiv(CG, 256);
   g = g < 1 ? 1 : (g > gmax ? gmax : g);
-  DecodeConfig c{(int)g, 8, fmt == 2 ? 3 : 2};
+  DecodeConfig c{(int)g, 8, s == 1 && fmt == 2 ? 3 : 2, s};
   if (KT < 16) c.nw = 4;
   return c;
 }
 
-template <int FMT, int G, int NW, int D, bool ELEMENTWISE>
+template <int FMT, int G, int NW, int D, bool ELEMENTWISE, int S = 1>
 hipError_t launch_cfg(const void* x, const void* w, const void* s, const float* sa,
                       const float* sb, void* y, int64_t M, int64_t N, int64_t K, int64_t KT,
                       int64_t CG, hipStream_t stream) {
-  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16));
+  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16 * S));
   dim3 block(NW * kWave);
-  hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, D, ELEMENTWISE>), grid, block, 0, stream,
+  hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, D, ELEMENTWISE, 0, S>), grid, block, 0,
+                     stream,
                      (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)s, sa, sb,
                      (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG, (int64_t)0);
   return hipGetLastError();
@@ -337,15 +374,22 @@ hipError_t launch_fmt_cfg(const DecodeConfig& c, const void* x, const void* w, c
   // element-wise configuration
   if (FMT != 4 && K % 8 != 0)
     return launch_cfg<FMT, 1, 4, 2, true>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream);
-#define QG_CASE(GG, WW, DD)                                                                 \
-  if (c.g == GG && c.nw == WW && c.d == DD)                                                 \
-    return launch_cfg<FMT, GG, WW, DD, false>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream);
-#define QG_G(GG) QG_CASE(GG, 8, DEPTH) QG_CASE(GG, 4, DEPTH)
+#define QG_CASE(GG, WW, DD, SS)                                                             \
+  if (c.g == GG && c.nw == WW && c.d == DD && c.s == SS)                                    \
+    return launch_cfg<FMT, GG, WW, DD, false, SS>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream);
+#define QG_G(GG) QG_CASE(GG, 8, DEPTH, 1) QG_CASE(GG, 4, DEPTH, 1)
+#define QG_GS(GG, SS) QG_CASE(GG, 8, 2, SS) QG_CASE(GG, 4, 2, SS)
   constexpr int DEPTH = FMT == 2 ? 3 : 2;
   QG_G(1) QG_G(2) QG_G(3) QG_G(4)
   if constexpr (FMT == 1) {   // up to eight INT4 column groups fit in registers
     QG_G(5) QG_G(6) QG_G(7) QG_G(8)
   }
+  QG_GS(1, 2) QG_GS(2, 2) QG_GS(3, 2) QG_GS(4, 2)
+  if constexpr (FMT == 1) {   // two INT4 slabs leave room for seven groups
+    QG_GS(5, 2) QG_GS(6, 2) QG_GS(7, 2)
+  }
+  QG_GS(1, 4) QG_GS(2, 4) QG_GS(3, 4)
+#undef QG_GS
 #undef QG_G
 #undef QG_CASE
   return hipErrorInvalidValue;

@@ -76,6 +76,10 @@ W4_CASES = [
     (300, 1000, 520),   # ragged M, K tail inside the last 128-wide tile
     (513, 136, 384),    # three row tiles, eight 32-wide K steps
     (260, 100, 300),    # K % 8 != 0 at large M: 16-row slabs instead
+    (32, 2048, 16400),  # two 16-row slabs per workgroup, seven column groups
+    (64, 1024, 1000),   # four slabs per workgroup
+    (100, 768, 3000),   # four slabs, two workgroup rows, ragged last slab
+    (255, 256, 600),    # four workgroup rows of four slabs
 ]
 
 
@@ -107,11 +111,11 @@ def test_w4a16_one_hot_reads_back_dequantized_weights(k, n):
         assert np.array_equal(y, wdeq[rows]), f"rows {rows[0]}..{rows[-1]}"
 
 
-@pytest.mark.parametrize("m", [1, 8, 16])
+@pytest.mark.parametrize("m", [1, 8, 16, 48])
 def test_w4a16_decode_full_size_sampled(m):
     k, n = 8192, 28672
     case_id("w4a16 decode full", m, k, n)
-    x, packed, s = wl.w4a16(16, k, n)
+    x, packed, s = wl.w4a16(max(m, 16), k, n)
     x = x[:m]
     wp = qg.qgemm_prepack("w4a16", dev(packed), k, n)
     y = host(qg.qgemm_w4a16(dev(x), wp, dev(s), n))
@@ -137,6 +141,9 @@ W8_CASES = [
     (300, 1000, 520),   # ragged M, N and K
     (260, 64, 1000),    # one K tile: the four-step pipeline tail only
     (257, 333, 200),    # K % 8 != 0 at large M: 16-row slabs instead
+    (32, 512, 640),     # two 16-row slabs per workgroup
+    (129, 640, 2100),   # four slabs, three workgroup rows, ragged
+    (64, 4096, 520),    # four slabs, long K
 ]
 
 
@@ -177,11 +184,11 @@ def test_w8a16_one_hot_full_byte_range():
         assert np.array_equal(y, wdeq[k0:k0 + 16])
 
 
-@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("m", [1, 4, 16, 64])
 def test_w8a16_decode_full_size_sampled(m):
     k, n = 4096, 11008
     case_id("w8a16 decode full", m, k, n)
-    x, w, s = wl.w8a16(16, k, n)
+    x, w, s = wl.w8a16(max(m, 16), k, n)
     x = x[:m]
     wp = qg.qgemm_prepack("w8a16", dev(w), k, n)
     y = host(qg.qgemm_w8a16(dev(x), wp, dev(s), n))
@@ -448,6 +455,10 @@ FP8_CASES = [
     (129, 1000, 256),
     (257, 300, 384),    # 256 x 256 tiles, six 64-wide steps
     (136, 200, 2064),   # 256 x 256 tiles, K tail of 16 in the last step
+    (32, 256, 512),     # small-M kernel, two 16-row slabs per workgroup
+    (64, 1024, 2048),   # four slabs
+    (100, 512, 384),    # four slabs, two workgroup rows, ragged
+    (128, 2048, 256),   # the largest M the small-M kernel takes
 ]
 
 
@@ -501,7 +512,7 @@ def test_fp8_one_hot_through_large_tiles():
     assert np.array_equal(c, oracle.round_bf16(bdeq[ks]))
 
 
-@pytest.mark.parametrize("m", [16, 8192])
+@pytest.mark.parametrize("m", [16, 64, 8192])
 def test_fp8_full_size_sampled(m):
     n = k = 8192
     case_id("fp8 full", m, n, k)
