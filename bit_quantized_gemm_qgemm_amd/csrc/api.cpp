@@ -16,8 +16,16 @@ using qgemm::pack_geom;
 using qgemm::grouped_geom;
 
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;   // kernels index with 32-bit ints
-// Smallest M for which the weight-only GEMMs take the tiled kernel.
+// The weight-only GEMMs take the 256 x 256 tiled kernel from M = 256 on, once
+// its grid has at least 64 workgroups; a smaller grid leaves most CUs idle,
+// and the small-M kernel (several 16-row slabs per workgroup, one pass over
+// the weight per 32 or 64 rows) is faster there.
 constexpr int64_t kWeightOnlyTileMinM = 256;
+constexpr int64_t kWeightOnlyTileMinTiles = 64;
+bool weight_only_tiled(int64_t M, int64_t N) {
+  return M >= kWeightOnlyTileMinM && N > 128 &&
+         qgemm::cdiv(M, 256) * qgemm::cdiv(N, 256) >= kWeightOnlyTileMinTiles;
+}
 // FP8 GEMMs with M up to this take the small-M kernel (16-row slabs, up to
 // four per workgroup); above it the tile kernels.  Measured on MI355X at
 // K = N = 8192: M = 32 / 64 / 128 in 15.7 / 24.0 / 43.5 us against 71-76 us
@@ -96,8 +104,7 @@ int weight_only(int fmt, const void* x, const void* w_packed, const void* scales
   // Large M: LDS-tiled matrix-core kernel (each weight byte is read once per
   // 256 rows).  Otherwise the register-dequant kernel in 16-row slabs, the
   // bandwidth path of decode.
-  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0 && K % 8 == 0 &&
-      qgemm::pipe_fits(fmt, M, N, K, 0))
+  if (weight_only_tiled(M, N) && K > 0 && K % 8 == 0 && qgemm::pipe_fits(fmt, M, N, K, 0))
     return launched(qgemm::launch_weight_only_tile(fmt, x, w_packed, scales, y, M, N, K,
                                                    as_stream(stream)));
   return launched(qgemm::launch_decode_gemm(fmt, x, w_packed, scales, nullptr, nullptr, y, M, N,
@@ -123,7 +130,7 @@ int grouped_gemm(int fmt, const void* x, const void* w_packed, void* y, int64_t 
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
   // K % 32 == 0 here, so fp16 X rows are 16-byte aligned
-  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0 && qgemm::pipe_fits(fmt, M, N, K, group_k))
+  if (weight_only_tiled(M, N) && K > 0 && qgemm::pipe_fits(fmt, M, N, K, group_k))
     return launched(qgemm::launch_weight_only_tile_grouped(fmt, x, w_packed, y, M, N, K, group_k,
                                                            as_stream(stream)));
   return launched(qgemm::launch_decode_grouped(fmt, x, w_packed, y, M, N, K, group_k,
@@ -206,7 +213,7 @@ int qgemm_nvfp4(const void* x, const void* w_packed, const float* global_scale, 
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
   // K % 16 == 0 here, so fp16 X rows are 16-byte aligned
-  if (M >= kWeightOnlyTileMinM && N > 128 && K > 0 && qgemm::pipe_fits(QGEMM_NVFP4, M, N, K, 0))
+  if (weight_only_tiled(M, N) && K > 0 && qgemm::pipe_fits(QGEMM_NVFP4, M, N, K, 0))
     return launched(qgemm::launch_weight_only_tile_nvfp4(x, w_packed, global_scale, y, M, N, K,
                                                          as_stream(stream)));
   return launched(qgemm::launch_decode_nvfp4(x, w_packed, global_scale, y, M, N, K,

@@ -404,6 +404,11 @@ hipError_t launch_fmt(const void* x, const void* w, const void* s, const float* 
   return launch_fmt_cfg<FMT>(c, x, w, s, sa, sb, y, M, N, K, pg.kt, pg.cg, stream);
 }
 
+// Slabs per workgroup for the grouped and NVFP4 launches: two above 16 rows
+// (as for INT4: each weight tile dequantized once for 32 rows), one with
+// short K (four waves).
+int slab_count(int64_t M, int nw) { return M > 16 && nw == 8 ? 2 : 1; }
+
 // Column groups per workgroup for the grouped and NVFP4 launches: the same
 // one-workgroup-per-CU rule, rounded down to an instantiated value (1, 2, 3,
 // 4, or 7 where gmax allows it); short K (four waves) uses 1 or 2.
@@ -417,13 +422,13 @@ int slab_groups(int64_t CG, int gmax, int64_t KT) {
 
 // Grouped formats: the same kernel with NGT metadata words per column and K
 // tile, D = 2; G and NW as for the per-column formats with fewer rows.
-template <int FMT, int NGT, int G, int NW>
+template <int FMT, int NGT, int G, int NW, int S>
 hipError_t launch_grouped_cfg(const void* x, const void* w, void* y, int64_t M, int64_t N,
                               int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
                               hipStream_t stream) {
-  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16));
+  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16 * S));
   dim3 block(NW * kWave);
-  hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, 2, false, NGT>), grid, block, 0, stream,
+  hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, 2, false, NGT, S>), grid, block, 0, stream,
                      (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)nullptr,
                      (const float*)nullptr, (const float*)nullptr, (uint16_t*)y, (int)M, (int)N,
                      (int)K, (int)KT, (int)CG, meta_offset);
@@ -434,14 +439,23 @@ template <int FMT, int NGT>
 hipError_t launch_grouped_ngt(const void* x, const void* w, void* y, int64_t M, int64_t N,
                               int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
                               hipStream_t stream) {
-  const int g = slab_groups(CG, FMT == 1 ? 7 : 4, KT);
   const int nw = KT < 16 ? 4 : 8;
-#define QG_GCASE(GG, WW)                                                                   \
-  if (g == GG && nw == WW)                                                                 \
-    return launch_grouped_cfg<FMT, NGT, GG, WW>(x, w, y, M, N, K, KT, CG, meta_offset, stream);
-  QG_GCASE(1, 4) QG_GCASE(1, 8) QG_GCASE(2, 4) QG_GCASE(2, 8) QG_GCASE(3, 8) QG_GCASE(4, 8)
+  const int s = slab_count(M, nw);
+  // two slabs with four metadata words per tile leave room for four INT4
+  // groups (seven spill)
+  const int g = slab_groups(CG, FMT == 1 && !(s == 2 && NGT == 4) ? 7 : 4, KT);
+#define QG_GCASE(GG, WW, SS)                                                               \
+  if (g == GG && nw == WW && s == SS)                                                      \
+    return launch_grouped_cfg<FMT, NGT, GG, WW, SS>(x, w, y, M, N, K, KT, CG, meta_offset,  \
+                                                    stream);
+  QG_GCASE(1, 4, 1) QG_GCASE(1, 8, 1) QG_GCASE(2, 4, 1) QG_GCASE(2, 8, 1) QG_GCASE(3, 8, 1)
+  QG_GCASE(4, 8, 1)
+  QG_GCASE(1, 8, 2) QG_GCASE(2, 8, 2) QG_GCASE(3, 8, 2) QG_GCASE(4, 8, 2)
   if constexpr (FMT == 1) {
-    QG_GCASE(7, 8)
+    QG_GCASE(7, 8, 1)
+  }
+  if constexpr (FMT == 1 && NGT < 4) {
+    QG_GCASE(7, 8, 2)
   }
 #undef QG_GCASE
   return hipErrorInvalidValue;
@@ -458,13 +472,13 @@ hipError_t launch_grouped_fmt(const void* x, const void* w, void* y, int64_t M, 
   }
 }
 
-template <int G, int NW>
+template <int G, int NW, int S>
 hipError_t launch_nvfp4_cfg(const void* x, const void* w, const float* gs, void* y, int64_t M,
                             int64_t N, int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
                             hipStream_t stream) {
-  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16));
+  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16 * S));
   dim3 block(NW * kWave);
-  hipLaunchKernelGGL((decode_gemm_kernel<7, G, NW, 2, false, 1>), grid, block, 0, stream,
+  hipLaunchKernelGGL((decode_gemm_kernel<7, G, NW, 2, false, 1, S>), grid, block, 0, stream,
                      (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)nullptr, gs,
                      (const float*)nullptr, (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT,
                      (int)CG, meta_offset);
@@ -478,12 +492,14 @@ hipError_t launch_decode_nvfp4(const void* x, const void* w_packed, const float*
   const PackGeom pg = pack_geom(7, K, N);
   const int g = slab_groups(pg.cg, 7, pg.kt);
   const int nw = pg.kt < 16 ? 4 : 8;
-#define QG_NCASE(GG, WW)                                                                   \
-  if (g == GG && nw == WW)                                                                 \
-    return launch_nvfp4_cfg<GG, WW>(x, w_packed, global_scale, y, M, N, K, pg.kt, pg.cg,   \
-                                    pg.scales, stream);
-  QG_NCASE(1, 4) QG_NCASE(1, 8) QG_NCASE(2, 4) QG_NCASE(2, 8) QG_NCASE(3, 8) QG_NCASE(4, 8)
-  QG_NCASE(7, 8)
+  const int s = slab_count(M, nw);
+#define QG_NCASE(GG, WW, SS)                                                               \
+  if (g == GG && nw == WW && s == SS)                                                      \
+    return launch_nvfp4_cfg<GG, WW, SS>(x, w_packed, global_scale, y, M, N, K, pg.kt,      \
+                                        pg.cg, pg.scales, stream);
+  QG_NCASE(1, 4, 1) QG_NCASE(1, 8, 1) QG_NCASE(2, 4, 1) QG_NCASE(2, 8, 1) QG_NCASE(3, 8, 1)
+  QG_NCASE(4, 8, 1) QG_NCASE(7, 8, 1)
+  QG_NCASE(1, 8, 2) QG_NCASE(2, 8, 2) QG_NCASE(3, 8, 2) QG_NCASE(4, 8, 2) QG_NCASE(7, 8, 2)
 #undef QG_NCASE
   return hipErrorInvalidValue;
 }

@@ -118,9 +118,9 @@ def test_grouped_full_size_sampled(fmt, m):
     assert_within(y[:, cols], y_ref, bound, f"{fmt} grouped full M={m}")
 
 
-# M >= 256 and N > 128 take the LDS-tiled matrix-core kernel (256 x 256 output
-# tiles): every metadata density (NGT = 1, 2, 4 words per column and tile),
-# ragged M and N, K not a multiple of 128, K shorter than the stage ring.
+# M >= 256 with fewer than 64 tiles of 256 x 256: the small-M kernel with two
+# 16-row slabs per workgroup: every metadata density (NGT = 1, 2, 4 words per
+# column and tile), ragged M and N, K not a multiple of 128, short K.
 TILE_CASES = [
     # (m, k, n, group_k, group_n, zero points)
     (256, 256, 200, 128, 1, True),    # one entry per tile, ragged N
@@ -164,3 +164,31 @@ def test_grouped_tile_full_size_sampled(fmt):
     gemm = oracle.gemm_w4a16_grouped if fmt == "w4a16" else oracle.gemm_w8a16_grouped
     y_ref, bound = gemm(x, w[:, cols], s[:, cols], z[:, cols], gk, 1)
     assert_within(y[:, cols], y_ref, bound, f"{fmt} grouped tile full")
+
+
+# At least 64 tiles of 256 x 256: the tiled kernel, on sampled outputs (every
+# metadata density, K tail, K below one tile; each sampled column gets its own
+# group entries).
+TILED_CASES = [
+    (2048, 256, 2048, 128, 1, True),
+    (2048, 640, 2080, 64, 1, True),
+    (2304, 384, 2048, 32, 3, True),
+    (2048, 1056, 2304, 96, 1, False),
+    (2048, 96, 2048, 32, 1, True),
+]
+
+
+@pytest.mark.parametrize("fmt", ["w4a16", "w8a16"])
+@pytest.mark.parametrize("m,k,n,gk,gn,zp", TILED_CASES)
+def test_grouped_tiled_sampled(fmt, m, k, n, gk, gn, zp):
+    case_id(f"{fmt} grouped tiled", m, k, n, gk, gn, zp)
+    gen = wl.w4a16_grouped if fmt == "w4a16" else wl.w8a16_grouped
+    x, w, s, z = gen(m, k, n, gk, gn, zeros=zp, seed=m + k + n + gk)
+    y = run(fmt, x, w, s, z, k, n, gk, gn)
+    rng = np.random.default_rng(gk)
+    rows = np.unique(np.concatenate([rng.integers(0, m, 64), [0, 255, 256, m - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(0, n, 64), [0, 255, 256, n - 1]]))
+    gemm = oracle.gemm_w4a16_grouped if fmt == "w4a16" else oracle.gemm_w8a16_grouped
+    zc = None if z is None else z[:, cols // gn]
+    y_ref, bound = gemm(x[rows], w[:, cols], s[:, cols // gn], zc, gk, 1)
+    assert_within(y[np.ix_(rows, cols)], y_ref, bound, f"{fmt} grouped tiled sampled")

@@ -90,7 +90,8 @@ def test_nvfp4_decode_full_size_sampled(m):
     assert ok.all(), f"{int((~ok).sum())} outside tolerance"
 
 
-# M >= 256 and N > 128 take the LDS-tiled matrix-core kernel.
+# M >= 256 with fewer than 64 tiles of 256 x 256: the small-M kernel, two
+# 16-row slabs per workgroup.
 TILE_CASES = [
     (256, 256, 200),      # two K tiles, ragged N
     (300, 1056, 520),     # ragged M and N, K = 8.25 tiles
@@ -110,16 +111,30 @@ def test_nvfp4_tile_matches_oracle(m, k, n):
 
 
 def test_nvfp4_tile_one_hot_reads_back_every_weight():
-    """The tiled kernel (M = K = 384 > 256, N = 200): X = identity, global
-    scale 1, Y = fp16(e2m1 * e4m3) for every weight, bit-exact; every step
-    of a tile picks its own scale byte."""
-    k, n = 384, 200
+    """The tiled kernel (M = K = 2048, N = 2080: 72 tiles of 256 x 256):
+    X = identity, global scale 1, Y = fp16(e2m1 * e4m3) for every weight,
+    bit-exact; every step of a tile picks its own scale byte."""
+    k, n = 2048, 2080
     case_id("nvfp4 tile one-hot", k, n)
     rng = np.random.default_rng(21)
     codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
     scales = rng.integers(0, 0x7F, size=(n, k // 16), dtype=np.uint8)
-    scales[0, :] = np.arange(k // 16, dtype=np.uint8)
+    scales[0, :] = (np.arange(k // 16) % 0x7F).astype(np.uint8)   # every non-NaN code
     scales[1, :] = 0x7E
     wdeq = oracle.round_fp16(oracle.dequant_nvfp4(codes, scales, 1.0))
     y = run(np.eye(k, dtype=np.float16), codes, scales, np.float32(1.0), k, n)
     assert np.array_equal(y, wdeq.T)
+
+
+@pytest.mark.parametrize("m,k,n", [(2048, 1056, 2080), (2304, 48, 2048), (2048, 2048, 2048)])
+def test_nvfp4_tiled_sampled(m, k, n):
+    """At least 64 tiles of 256 x 256: the tiled kernel, on sampled outputs."""
+    case_id("nvfp4 tiled", m, k, n)
+    x, codes, scales, g = wl.nvfp4_weight(m, k, n, seed=m + k + n)
+    y = run(x, codes, scales, g, k, n)
+    rng = np.random.default_rng(k)
+    rows = np.unique(np.concatenate([rng.integers(0, m, 64), [0, 255, 256, m - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(0, n, 64), [0, 255, 256, n - 1]]))
+    y_ref, bound = oracle.gemm_nvfp4(x[rows], codes[cols], scales[cols], g)
+    ok = oracle.within_tolerance(y[np.ix_(rows, cols)], y_ref, bound)
+    assert ok.all(), f"{int((~ok).sum())} outside tolerance"

@@ -72,10 +72,10 @@ W4_CASES = [
     (8, 2048, 700),
     (16, 256, 16400),   # eight column groups per workgroup, ragged last workgroup
     (6, 384, 9000),     # four groups per workgroup (M in 5..8)
-    (256, 1024, 272),   # M >= 256: 256 x 256 matrix-core tiles, ragged N
+    (256, 1024, 272),   # M >= 256 with few 256 x 256 tiles: the small-M kernel, slabs
     (300, 1000, 520),   # ragged M, K tail inside the last 128-wide tile
-    (513, 136, 384),    # three row tiles, eight 32-wide K steps
-    (260, 100, 300),    # K % 8 != 0 at large M: 16-row slabs instead
+    (513, 136, 384),    # seventeen 32-row slab pairs
+    (260, 100, 300),    # K % 8 != 0 at large M: element-wise activation loads
     (32, 2048, 16400),  # two 16-row slabs per workgroup, seven column groups
     (64, 1024, 1000),   # four slabs per workgroup
     (100, 768, 3000),   # four slabs, two workgroup rows, ragged last slab
@@ -137,10 +137,10 @@ W8_CASES = [
     (2, 64, 1),
     (9, 200, 9000),     # four groups, three tiles in flight, short K, ragged N
     (16, 520, 2100),
-    (256, 2048, 300),   # M >= 256: 256 x 256 matrix-core tiles
+    (256, 2048, 300),   # M >= 256 with few 256 x 256 tiles: the small-M kernel, slabs
     (300, 1000, 520),   # ragged M, N and K
-    (260, 64, 1000),    # one K tile: the four-step pipeline tail only
-    (257, 333, 200),    # K % 8 != 0 at large M: 16-row slabs instead
+    (260, 64, 1000),    # one K tile
+    (257, 333, 200),    # K % 8 != 0 at large M: element-wise activation loads
     (32, 512, 640),     # two 16-row slabs per workgroup
     (129, 640, 2100),   # four slabs, three workgroup rows, ragged
     (64, 4096, 520),    # four slabs, long K
@@ -199,9 +199,10 @@ def test_w8a16_decode_full_size_sampled(m):
 
 @pytest.mark.parametrize("fmt", ["w4a16", "w8a16"])
 def test_weight_only_one_hot_through_large_tiles(fmt):
-    """X = the identity (M = K = 512 rows, the 256 x 256 tile path):
-    Y = fp16(W_deq) exactly, every weight of every tile and K step."""
-    k, n = 512, 272
+    """X = the identity (M = K = 2048, N = 2080: 8 x 9 tiles of 256 x 256, the
+    tiled kernel): Y = fp16(W_deq) exactly, every weight of every tile and K
+    step."""
+    k, n = 2048, 2080
     case_id(f"{fmt} one-hot large tiles", k, n)
     rng = np.random.default_rng(11)
     s = (rng.uniform(0.002, 0.02, n) * np.where(np.arange(n) % 3 == 0, -1, 1)).astype(np.float16)
@@ -217,6 +218,27 @@ def test_weight_only_one_hot_through_large_tiles(fmt):
     x = np.eye(k, dtype=np.float16)
     y = host(fn(dev(x), wp, dev(s), n))
     assert np.array_equal(y, wdeq)
+
+
+# At least 64 tiles of 256 x 256: the tiled kernel (K tail, short K, one K tile).
+TILED_CASES = [(2048, 1000, 2100), (2304, 136, 2048), (2050, 64, 2304)]
+
+
+@pytest.mark.parametrize("fmt", ["w4a16", "w8a16"])
+@pytest.mark.parametrize("m,k,n", TILED_CASES)
+def test_weight_only_tiled_sampled(fmt, m, k, n):
+    case_id(f"{fmt} tiled", m, k, n)
+    gen = wl.w4a16 if fmt == "w4a16" else wl.w8a16
+    x, w, s = gen(m, k, n, seed=m + k + n)
+    wp = qg.qgemm_prepack(fmt, dev(w), k, n)
+    fn = qg.qgemm_w4a16 if fmt == "w4a16" else qg.qgemm_w8a16
+    y = host(fn(dev(x), wp, dev(s), n))
+    rng = np.random.default_rng(k)
+    rows = np.unique(np.concatenate([rng.integers(0, m, 64), [0, 255, 256, m - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(0, n, 64), [0, 255, 256, n - 1]]))
+    gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16
+    y_ref, bound = gemm(x[rows], w[:, cols], s[cols])
+    assert_within(y[np.ix_(rows, cols)], y_ref, bound, f"{fmt} tiled sampled")
 
 
 @pytest.mark.parametrize("fmt", ["w4a16", "w8a16"])
