@@ -26,8 +26,8 @@ bool weight_only_tiled(int64_t M, int64_t N) {
   return M >= kWeightOnlyTileMinM && N > 128 &&
          qgemm::cdiv(M, 256) * qgemm::cdiv(N, 256) >= kWeightOnlyTileMinTiles;
 }
-// FP8 GEMMs with M up to this take the small-M kernel (16-row slabs, up to
-// four per workgroup); above it the tile kernels.  Measured on MI355X at
+// FP8 and MXFP4 GEMMs with M up to this take the small-M kernel (16-row
+// slabs, up to four per workgroup); above it the tile kernels.  Measured on MI355X at
 // K = N = 8192: M = 32 / 64 / 128 in 15.7 / 24.0 / 43.5 us against 71-76 us
 // through the 128 x 128 tiles, and a tie at M = 256.
 constexpr int kDecodeMaxM = 128;
@@ -274,6 +274,9 @@ int qgemm_mxfp4(const void* a_codes, const void* a_e8m0, const void* w_packed, v
   if (!aligned(a_codes, 16) || !aligned(w_packed, 16) || !aligned(c, 16)) return QGEMM_ERR_ALIGN;
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
+  if (M <= kDecodeMaxM)
+    return launched(qgemm::launch_decode_gemm(QGEMM_MXFP4, a_codes, w_packed, a_e8m0, nullptr,
+                                              nullptr, c, M, N, K, as_stream(stream)));
   return launched(qgemm::launch_tile_gemm(QGEMM_MXFP4, a_codes, a_e8m0, w_packed, nullptr,
                                           nullptr, c, M, N, K, as_stream(stream)));
 }
@@ -324,6 +327,9 @@ int qgemm_mxfp4_act(const float* a, const void* w_packed, void* c, void* workspa
     if (st != QGEMM_OK) return st;
   }
   if (N == 0) return QGEMM_OK;
+  if (M <= kDecodeMaxM)
+    return launched(qgemm::launch_decode_gemm(QGEMM_MXFP4, codes, w_packed, e8m0, nullptr,
+                                              nullptr, c, M, N, K, as_stream(stream)));
   return launched(qgemm::launch_tile_gemm(QGEMM_MXFP4, codes, e8m0, w_packed, nullptr, nullptr, c,
                                           M, N, K, as_stream(stream)));
 }

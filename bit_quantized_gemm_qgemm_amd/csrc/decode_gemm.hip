@@ -51,6 +51,16 @@ template <> struct DecodeTraits<7> {
 template <> struct DecodeTraits<4> {
   static constexpr int WV = 2, XV = 2, TB = kTileBytes;
 };
+// MXFP4: a 256-wide tile = two 128-element blocks h; per lane 16 B of W codes
+// and 16 B of A codes per block (k = 128 h + 32 g + [0, 32)), plus one E8M0
+// byte of each operand per block.
+template <> struct DecodeTraits<3> {
+  static constexpr int WV = 2, XV = 2, TB = kTileBytes;
+};
+
+// K elements per tile and activation bytes per row and tile.
+template <int FMT> constexpr int tile_k() { return FMT == 3 ? kTileK4 : kTileK8; }
+template <int FMT> constexpr int tile_x_bytes() { return FMT == 3 ? 128 : FMT == 4 ? 128 : 256; }
 
 // NGT > 0: grouped formats, NGT metadata words {1024 + z (+128), s} per
 // column and K tile (layout in qgemm_common.h).
@@ -60,7 +70,8 @@ template <int FMT, int G, int NGT = 0, int S = 1>
 struct Chunk {
   uintx4 x[S][DecodeTraits<FMT>::XV];
   uintx4 w[G][DecodeTraits<FMT>::WV];
-  uint32_t meta[G][NGT > 0 ? NGT : 1];
+  uint32_t meta[G][NGT > 0 ? NGT : (FMT == 3 ? 2 : 1)];   // MXFP4: W scale word per block
+  uint32_t asc[FMT == 3 ? S : 1][2];                        // MXFP4: A scale byte per block
 };
 
 // Per-lane and per-workgroup addressing of one launch.  Scalar (wave-uniform)
@@ -74,7 +85,12 @@ struct DecodeAddr {
   uint32_t wlane;         // 16 * lane
   int K;
   int g;                  // lane group, lane >> 4
-  const uint8_t* meta;    // grouped / NVFP4: first metadata tile of this workgroup
+  const uint8_t* meta;    // grouped / NVFP4: first metadata tile of this workgroup;
+                          // MXFP4: the W scale segment
+  const uint8_t* asc;     // MXFP4: A scales, E8M0 [M, K/32]
+  uint32_t alane[4];      // MXFP4, per slab: this lane's row and block g in asc
+  int cg0, KT;            // MXFP4: first column group, K tiles
+  uint32_t wsh[8];        // MXFP4, per group: bit shift of its tile's scale byte
   int64_t meta_cg_stride; // bytes between column groups of metadata
   int meta_kt_stride;     // bytes of metadata per K tile
   uint32_t mlane;         // this lane's entries within a tile
@@ -84,6 +100,7 @@ struct DecodeAddr {
 template <int FMT>
 __device__ __forceinline__ int piece_k(int kt, int g, int p) {
   if constexpr (FMT == 4) return kt * kTileK8 + 32 * g + 16 * p;   // e4m3: contiguous 32
+  else if constexpr (FMT == 3) return kt * kTileK4 + 128 * p + 32 * g;   // FP4: block p
   else return kt * kTileK8 + 32 * p + 8 * g;                        // fp16: step p
 }
 
@@ -96,10 +113,9 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const Deco
                                            int kt) {
   constexpr int XV = DecodeTraits<FMT>::XV;
   constexpr int TB = DecodeTraits<FMT>::TB;
-  constexpr int XB = (FMT == 4) ? 1 : 2;           // bytes per activation element
   constexpr int PSTRIDE = (FMT == 4) ? 16 : 64;    // bytes between a lane's pieces
-  const uint8_t* xk = ad.x + (int64_t)kt * kTileK8 * XB;   // uniform
-  const bool full = (kt + 1) * kTileK8 <= ad.K;            // uniform
+  const uint8_t* xk = ad.x + (int64_t)kt * tile_x_bytes<FMT>();   // uniform
+  const bool full = (kt + 1) * tile_k<FMT>() <= ad.K;             // uniform
   if constexpr (!X_ELEMENTWISE) {
     if (full) {
 #pragma unroll
@@ -121,7 +137,8 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const Deco
     }
   } else {
     // K % 8 != 0 (fp16 only): rows are not 16-byte aligned; go element-wise
-    static_assert(S == 1, "the element-wise X path takes one slab");
+    static_assert(S == 1 && FMT != 3 && FMT != 4, "the element-wise path: fp16 X, one slab");
+    constexpr int XB = 2;
     const uint16_t* xr = reinterpret_cast<const uint16_t*>(xk + ad.xlane[0]);
 #pragma unroll
     for (int p = 0; p < XV; ++p) {
@@ -137,6 +154,18 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const Deco
       ch.x[0][p] = uintx4{d[0], d[1], d[2], d[3]};
     }
   }
+  if constexpr (FMT == 3) {
+    // the E8M0 byte of block 8 kt + 4 h + g of each slab row; blocks past K
+    // take the unit scale (their codes read as zero)
+    const int nblk = ad.K / 32;
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int blk = 8 * kt + 4 * h + ad.g;
+        ch.asc[q][h] = blk < nblk ? (uint32_t)ad.asc[ad.alane[q] + 8 * kt + 4 * h] : kE8M0One;
+      }
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int gg = g < ad.cg_last ? g : ad.cg_last;                      // uniform
@@ -145,6 +174,16 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const Deco
     if constexpr (DecodeTraits<FMT>::WV == 2)
       ch.w[g][1] =
           __builtin_nontemporal_load(reinterpret_cast<const uintx4*>(t + 1024 + ad.wlane));
+    if constexpr (FMT == 3) {
+      // the scale entries of this group's column for blocks 8 kt + 4 h + g:
+      // 512 B per (8 column tiles, 128-element block), [lane][tile]
+      const int cg = ad.cg0 + gg;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint8_t* e = ad.meta + ((int64_t)(cg >> 3) * (2 * ad.KT) + 2 * kt + h) * 512;
+        ch.meta[g][h] = *reinterpret_cast<const uint32_t*>(e + ad.wlane / 2 + 4 * ((cg >> 2) & 1));
+      }
+    }
     if constexpr (NGT > 0) {
       const uint8_t* mt = ad.meta + gg * ad.meta_cg_stride + (int64_t)kt * ad.meta_kt_stride;
       if constexpr (FMT == 7) {
@@ -164,8 +203,28 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const Deco
 
 template <int FMT, int G, int NGT = 0, int S = 1>
 __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
-                                              floatx4 (&acc)[S][G], W4Masks mk) {
-  if constexpr (FMT == 4) {
+                                              floatx4 (&acc)[S][G], W4Masks mk,
+                                              const DecodeAddr& ad) {
+  if constexpr (FMT == 3) {
+    // two scaled FP4 instructions per group (blocks h = 0, 1); the lane's
+    // scale bytes sit in the low byte (A) and at byte (cg & 3) of the loaded
+    // word (W)
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uintx4& wb = ch.w[g][h];
+        const intx8 b = {(int)wb[0], (int)wb[1], (int)wb[2], (int)wb[3], 0, 0, 0, 0};
+        const int sb = (int)(ch.meta[g][h] >> ad.wsh[g]);
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          const uintx4& xa = ch.x[q][h];
+          const intx8 a = {(int)xa[0], (int)xa[1], (int)xa[2], (int)xa[3], 0, 0, 0, 0};
+          acc[q][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a, b, acc[q][g], kFmtFP4, kFmtFP4, 0, (int)ch.asc[q][h], 0, sb);
+        }
+      }
+  } else if constexpr (FMT == 4) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const intx8 b = {(int)ch.w[g][0][0], (int)ch.w[g][0][1], (int)ch.w[g][0][2],
@@ -225,7 +284,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   static_assert(D >= 2 && D <= 4, "prefetch depth 2..4");
   static_assert(S == 1 || S == 2 || S == 4, "1, 2 or 4 slabs");
   constexpr int TB = DecodeTraits<FMT>::TB;
-  constexpr int XB = (FMT == 4) ? 1 : 2;
   __shared__ floatx4 red[NW][G][kWave];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -240,7 +298,24 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
 #pragma unroll
   for (int q = 0; q < S; ++q) {
     const int row = min(m0 + 16 * q + (lane & 15), M - 1);
-    ad.xlane[q] = (uint32_t)(((int64_t)row * K + (FMT == 4 ? 32 : 8) * ad.g) * XB);
+    if constexpr (FMT == 3) {   // 16 B of codes at k = 32 g of a block
+      ad.xlane[q] = (uint32_t)((int64_t)row * (K / 2) + 16 * ad.g);
+      ad.alane[q] = (uint32_t)((int64_t)row * (K / 32) + ad.g);
+    } else {
+      const int xb = FMT == 4 ? 1 : 2;
+      ad.xlane[q] = (uint32_t)(((int64_t)row * K + (FMT == 4 ? 32 : 8) * ad.g) * xb);
+    }
+  }
+  if constexpr (FMT == 3) {
+    // `scales` carries the A E8M0 bytes; meta_offset locates the W scales
+    ad.asc = reinterpret_cast<const uint8_t*>(scales);
+    ad.cg0 = cg0;
+    ad.KT = KT;
+#pragma unroll
+    for (int g = 0; g < G && g < 8; ++g) {
+      const int cg = cg0 + min(g, CG - 1 - cg0);
+      ad.wsh[g] = 8u * (uint32_t)(cg & 3);
+    }
   }
   ad.cg_stride = (int64_t)KT * TB;
   ad.w = wp + (int64_t)cg0 * ad.cg_stride;
@@ -251,7 +326,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   // and tile, the lanes of group g reading the dword of blocks 2s + (g >> 1)
   ad.meta_kt_stride = FMT == 7 ? kScaleTileBytes : 16 * (NGT > 0 ? NGT : 1) * 4;
   ad.meta_cg_stride = (int64_t)KT * ad.meta_kt_stride;
-  ad.meta = wp + meta_offset + (int64_t)cg0 * ad.meta_cg_stride;
+  ad.meta = FMT == 3 ? wp + meta_offset : wp + meta_offset + (int64_t)cg0 * ad.meta_cg_stride;
   ad.mlane = FMT == 7 ? (uint32_t)((lane & 15) * 8 + 4 * (ad.g >> 1))
                       : (uint32_t)((lane & 15) * (NGT > 0 ? NGT : 1) * 4);
 
@@ -276,7 +351,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
     for (int d = 0; d < D; ++d) {
       const int kt = base + d * NW;
       if (kt < KT) {
-        compute_chunk<FMT, G, NGT, S>(ring[d], acc, mk);
+        compute_chunk<FMT, G, NGT, S>(ring[d], acc, mk, ad);
         if (kt + D * NW < KT)
           load_chunk<FMT, G, X_ELEMENTWISE, NGT, S>(ring[d], ad, kt + D * NW);
       }
@@ -309,7 +384,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
       const int gm = m0 + 16 * q + m;
       const int gn = (cg0 + g) * 16 + c;
       if (gm < M && gn < N) {
-        if constexpr (FMT == 4) {
+        if constexpr (FMT == 3) {
+          y[(int64_t)gm * N + gn] = f32_to_bf16_rne(sum);   // scales applied in the MFMA
+        } else if constexpr (FMT == 4) {
           y[(int64_t)gm * N + gn] = f32_to_bf16_rne(sum * fp8_scale);
         } else if constexpr (FMT == 7) {
           y[(int64_t)gm * N + gn] = f32_to_f16_bits(sum * fp8_scale);   // per-tensor scale
@@ -345,7 +422,8 @@ struct DecodeConfig {
 // 2.3 workgroups per CU (K = 8192, N = 28672, M = 64: 106 us against 68 us).
 DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
   const int s = M <= 16 ? 1 : (M <= 32 || fmt == 1) ? 2 : 4;
-  const int64_t gmax = s == 1 ? (fmt == 1 ? 8 : 4) : s == 2 ? (fmt == 1 ? 7 : 4) : 3;
+  // MXFP4 carries its scale words in the ring too: 2 groups with 4 slabs
+  const int64_t gmax = s == 1 ? (fmt == 1 ? 8 : 4) : s == 2 ? (fmt == 1 ? 7 : 4) : fmt == 3 ? 2 : 3;
   int64_t g = cdiv(CG, 256);
   g = g < 1 ? 1 : (g > gmax ? gmax : g);
   DecodeConfig c{(int)g, 8, s == 1 && fmt == 2 ? 3 : 2, s};
@@ -353,30 +431,36 @@ DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
   return c;
 }
 
+// MXFP4 (FMT 3): `s` is the A E8M0 array and meta_offset the offset of the W
+// scale segment in the packed weight.
 template <int FMT, int G, int NW, int D, bool ELEMENTWISE, int S = 1>
 hipError_t launch_cfg(const void* x, const void* w, const void* s, const float* sa,
                       const float* sb, void* y, int64_t M, int64_t N, int64_t K, int64_t KT,
-                      int64_t CG, hipStream_t stream) {
+                      int64_t CG, hipStream_t stream, int64_t meta_offset = 0) {
   dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16 * S));
   dim3 block(NW * kWave);
   hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, D, ELEMENTWISE, 0, S>), grid, block, 0,
                      stream,
                      (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)s, sa, sb,
-                     (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG, (int64_t)0);
+                     (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG, meta_offset);
   return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t launch_fmt_cfg(const DecodeConfig& c, const void* x, const void* w, const void* s,
                           const float* sa, const float* sb, void* y, int64_t M, int64_t N,
-                          int64_t K, int64_t KT, int64_t CG, hipStream_t stream) {
+                          int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
+                          hipStream_t stream) {
   // fp16 X rows that are not 16-byte aligned (K % 8 != 0) take one
   // element-wise configuration
-  if (FMT != 4 && K % 8 != 0)
-    return launch_cfg<FMT, 1, 4, 2, true>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream);
+  if constexpr (FMT == 1 || FMT == 2) {
+    if (K % 8 != 0)
+      return launch_cfg<FMT, 1, 4, 2, true>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream);
+  }
 #define QG_CASE(GG, WW, DD, SS)                                                             \
   if (c.g == GG && c.nw == WW && c.d == DD && c.s == SS)                                    \
-    return launch_cfg<FMT, GG, WW, DD, false, SS>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream);
+    return launch_cfg<FMT, GG, WW, DD, false, SS>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream, \
+                                                  meta_offset);
 #define QG_G(GG) QG_CASE(GG, 8, DEPTH, 1) QG_CASE(GG, 4, DEPTH, 1)
 #define QG_GS(GG, SS) QG_CASE(GG, 8, 2, SS) QG_CASE(GG, 4, 2, SS)
   constexpr int DEPTH = FMT == 2 ? 3 : 2;
@@ -388,7 +472,10 @@ hipError_t launch_fmt_cfg(const DecodeConfig& c, const void* x, const void* w, c
   if constexpr (FMT == 1) {   // two INT4 slabs leave room for seven groups
     QG_GS(5, 2) QG_GS(6, 2) QG_GS(7, 2)
   }
-  QG_GS(1, 4) QG_GS(2, 4) QG_GS(3, 4)
+  QG_GS(1, 4) QG_GS(2, 4)
+  if constexpr (FMT != 3) {
+    QG_GS(3, 4)
+  }
 #undef QG_GS
 #undef QG_G
 #undef QG_CASE
@@ -401,7 +488,7 @@ hipError_t launch_fmt(const void* x, const void* w, const void* s, const float* 
                       hipStream_t stream) {
   const PackGeom pg = pack_geom(FMT, K, N);
   const DecodeConfig c = pick_decode_config(FMT, M, pg.cg, pg.kt);
-  return launch_fmt_cfg<FMT>(c, x, w, s, sa, sb, y, M, N, K, pg.kt, pg.cg, stream);
+  return launch_fmt_cfg<FMT>(c, x, w, s, sa, sb, y, M, N, K, pg.kt, pg.cg, pg.scales, stream);
 }
 
 // Slabs per workgroup for the grouped and NVFP4 launches: two above 16 rows
@@ -518,6 +605,7 @@ hipError_t launch_decode_gemm(int fmt, const void* x, const void* w_packed, cons
   switch (fmt) {
     case 1: return launch_fmt<1>(x, w_packed, scales, scale_a, scale_b, y, M, N, K, stream);
     case 2: return launch_fmt<2>(x, w_packed, scales, scale_a, scale_b, y, M, N, K, stream);
+    case 3: return launch_fmt<3>(x, w_packed, scales, scale_a, scale_b, y, M, N, K, stream);
     case 4: return launch_fmt<4>(x, w_packed, scales, scale_a, scale_b, y, M, N, K, stream);
     default: return hipErrorInvalidValue;
   }

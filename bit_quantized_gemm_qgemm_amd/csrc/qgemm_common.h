@@ -151,7 +151,8 @@ constexpr int kFp8Partials = 256;
 hipError_t launch_quantize_fp8_ws(const float* x, int64_t count, uint8_t* codes, float* scale,
                                   float* partials, hipStream_t stream);
 
-// Small-M path (M rows handled in 16-row slabs) for W4A16 / W8A16 / FP8.
+// Small-M path (M rows handled in 16-row slabs) for W4A16 / W8A16 / FP8 /
+// MXFP4; for MXFP4 `scales` is the A E8M0 array [M, K/32].
 hipError_t launch_decode_gemm(int fmt, const void* x, const void* w_packed, const void* scales,
                               const float* scale_a, const float* scale_b, void* y,
                               int64_t M, int64_t N, int64_t K, hipStream_t stream);

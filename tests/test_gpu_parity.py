@@ -344,6 +344,9 @@ MX_CASES = [
     (129, 1000, 384),   # K = 384: a half 256-wide step at the end
     (257, 384, 1280),   # 256 x 256 tiles, several pipeline iterations
     (160, 136, 896),    # last 128-wide step all padding; 9 column tiles
+    (100, 520, 800),    # small-M kernel: four slabs, two workgroup rows, K = 3.125 tiles
+    (33, 136, 288),     # four slabs, one row of them ragged; K = 1.125 tiles
+    (128, 2100, 256),   # the largest M the small-M kernel takes
 ]
 
 
@@ -363,8 +366,10 @@ def test_mxfp4_gemm_matches_oracle(m, n, k):
 
 def test_mxfp4_one_hot_reads_back_dequantized_weights():
     """A row m holds a single 1.0 at k_m (scale 2^0): C[m, n] = W_deq[n, k_m],
-    exact in bf16 (E2M1 values carry two significant bits)."""
-    n, k = 48, 512
+    exact in bf16 (E2M1 values carry two significant bits).  M = 64 (the
+    small-M kernel); N = 272 spans three groups of eight column tiles, so
+    every position of a tile's scale byte is read back."""
+    n, k = 272, 512
     case_id("mxfp4 one-hot", n, k)
     _, w = wl.mxfp4_operands(1, n, k, seed=5)
     wc, we = oracle.mxfp4_quantize(w)
@@ -421,6 +426,23 @@ def test_mxfp4_scale_product_is_exponent_add_on_device():
     c = host(qg.qgemm_mxfp4(dev(oracle.pack_nibbles_last_axis(a_codes)), dev(a_sc), wp, n))
     want = 32.0 * np.ldexp(1.0, ea[:, None].astype(np.int64) + ew[None, :] - 254)
     assert np.array_equal(c, want)
+
+
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_mxfp4_small_m_full_size_sampled(m):
+    """K = N = 8192 at small M (the small-M kernel), on sampled columns."""
+    n = k = 8192
+    case_id("mxfp4 small-M full", m, n, k)
+    a, w = wl.mxfp4_operands(m, n, k, seed=m)
+    ac_d, ae_d = qg.qgemm_quantize_mxfp4(dev(a))
+    wc_d, we_d = qg.qgemm_quantize_mxfp4(dev(w))
+    wp = qg.qgemm_prepack("mxfp4", wc_d, k, n, w_scales=we_d)
+    c = host(qg.qgemm_mxfp4(ac_d, ae_d, wp, n))
+    cols = np.unique(np.concatenate([np.random.default_rng(m).integers(0, n, 96), [0, n - 1]]))
+    ac, ae = oracle.mxfp4_quantize(a)
+    wc, we = oracle.mxfp4_quantize(w[cols])
+    c_ref, bound = oracle.gemm_mxfp4(ac, ae, wc, we)
+    assert_within(c[:, cols], c_ref, bound, f"mxfp4 small-M full M={m}")
 
 
 def test_mxfp4_full_size_sampled():
