@@ -64,11 +64,18 @@ WORKLOADS = {
     # NVFP4-style weights (e4m3 scale per 16 elements, fp32 per tensor), fp16 X
     "nvfp4_decode": ("nvfp4", (1, 8, 16), 28672, 8192),
     "nvfp4_square": ("nvfp4", (4096,), 4096, 4096),
+    # MXFP4 at decode M, and batched decode (M = 32 .. 128: several 16-row
+    # slabs per workgroup of the small-M kernel)
+    "mxfp4_decode": ("mxfp4", (1, 16), 8192, 8192),
+    "w8a16_batch": ("w8a16", (32, 64, 128), 11008, 4096),
+    "w4a16_batch": ("w4a16", (32, 64, 128), 28672, 8192),
+    "fp8_batch": ("fp8", (32, 64, 128), 8192, 8192),
     # fp32 activations quantized on the device inside the call, then the GEMM
     "fp8_act_decode": ("fp8_act", (16,), 8192, 8192),
     "mxfp4_act_square": ("mxfp4_act", (8192,), 8192, 8192),
 }
 GROUP_K = 128   # group size of the grouped workloads
+SMALL_M_MAX = 128   # the largest M of the bandwidth-reported workloads
 DEFAULT_WORKLOAD = "w8a16_decode"
 
 
@@ -96,7 +103,9 @@ class Setup:
         self.name = name
         fmt, ms, n, k = WORKLOADS[name]
         self.fmt, self.ms, self.n, self.k = fmt, ms, n, k
-        self.kind = "decode" if max(ms) <= 16 else "tile"
+        # up to M = 128 the calls stream the weight through the small-M kernel
+        # (reported as weight GB/s against HBM); beyond, the tile kernels
+        self.kind = "decode" if max(ms) <= SMALL_M_MAX else "tile"
         self.explicit = None   # W8A16 square: the explicit dequantize-then-matmul comparison
         dev = torch.device("cuda:0")
         mmax = max(ms)
@@ -211,13 +220,14 @@ class Setup:
             a_bytes = mmax * k // 2 + mmax * k // 32
             self.copies = self._rotate(packed, w_bytes + a_bytes)
             self.a_copies = [ac] + [ac.clone() for _ in range(len(self.copies) - 1)]
-            ae_d = ae
             self.dtype = "fp4"
-            out = torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
-            alg = w_bytes + a_bytes + 2 * mmax * n
-            self.calls.append((lambda c: qg.qgemm_mxfp4(self.a_copies[c], ae_d, self.copies[c], n,
-                                                        out=out),
-                               alg, w_bytes, 2 * mmax * n * k))
+            for m in ms:
+                out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                aem = ae[:m]
+                alg = w_bytes + m * k // 2 + m * k // 32 + 2 * m * n
+                self.calls.append((lambda c, m=m, aem=aem, out=out: qg.qgemm_mxfp4(
+                    self.a_copies[c][:m], aem, self.copies[c], n, out=out),
+                    alg, w_bytes, 2 * m * n * k))
         elif fmt == "fp8":
             a, b = wl.fp8_operands(mmax, n, k)
             qa, sa = qg.qgemm_quantize_fp8(torch.from_numpy(a).to(dev))
@@ -230,11 +240,12 @@ class Setup:
             self.copies = self._rotate(packed, w_bytes + a_bytes)
             self.a_copies = [qa] + [qa.clone() for _ in range(len(self.copies) - 1)]
             self.dtype = "fp8"
-            out = torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
-            alg = w_bytes + a_bytes + 2 * mmax * n
-            self.calls.append((lambda c: qg.qgemm_fp8(self.a_copies[c], self.copies[c], sa, sb, n,
-                                                      out=out),
-                               alg, w_bytes, 2 * mmax * n * k))
+            for m in ms:
+                out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                alg = w_bytes + m * k + 2 * m * n
+                self.calls.append((lambda c, m=m, out=out: qg.qgemm_fp8(
+                    self.a_copies[c][:m], self.copies[c], sa, sb, n, out=out),
+                    alg, w_bytes, 2 * m * n * k))
         torch.cuda.synchronize()
 
     @staticmethod
@@ -351,7 +362,7 @@ def cpu_baseline(name, budget_s=10.0):
 
     fmt, ms, n, k = WORKLOADS[name]
     mmax = max(ms)
-    if fmt in ("w4a16_grouped", "w8a16_grouped") and mmax <= 16:
+    if fmt in ("w4a16_grouped", "w8a16_grouped") and mmax <= SMALL_M_MAX:
         w4 = fmt == "w4a16_grouped"
         gen = wl.w4a16_grouped if w4 else wl.w8a16_grouped
         ggemm = oracle.gemm_w4a16_grouped if w4 else oracle.gemm_w8a16_grouped
@@ -360,13 +371,30 @@ def cpu_baseline(name, budget_s=10.0):
         w, s, z = np.ascontiguousarray(w[:, :cols]), s[:, :cols], z[:, :cols]
         gemm = lambda xm, w, s: ggemm(xm, w, s, z, GROUP_K)  # noqa: E731
         w_bytes_per_step = sum(((k * cols // 2) if w4 else k * cols) + 3 * s.size for _ in ms)
-    if fmt == "nvfp4" and mmax <= 16:
+    if fmt == "nvfp4" and mmax <= SMALL_M_MAX:
         cols = n if k * n <= 50_000_000 else max(16, int(50_000_000 // k))
         x, codes, scales, g = wl.nvfp4_weight(mmax, k, n)
         w, s = np.ascontiguousarray(codes[:cols]), np.ascontiguousarray(scales[:cols])
         gemm = lambda xm, w, s: oracle.gemm_nvfp4(xm, w, s, g)  # noqa: E731
         w_bytes_per_step = sum(k * cols // 2 + k * cols // 16 for _ in ms)
-    if fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped", "nvfp4") and mmax <= 16:
+    if fmt in ("mxfp4", "fp8") and mmax <= SMALL_M_MAX:
+        # bounded sample: the full K and a column slice sized for ~1 s per step
+        cols = max(16, int(20_000_000 // k))
+        if fmt == "mxfp4":
+            a, wt = wl.mxfp4_operands(mmax, cols, k)
+            ac, ae = oracle.mxfp4_quantize(a)
+            wc, we = oracle.mxfp4_quantize(wt)
+            gemm = lambda xm, w, s: oracle.gemm_mxfp4(ac[:len(xm)], ae[:len(xm)], wc, we)  # noqa: E731
+            w_bytes_per_step = sum(k * cols // 2 + k * cols // 32 for _ in ms)
+        else:
+            a, b = wl.fp8_operands(mmax, cols, k)
+            qa, sa = oracle.fp8_quantize(a)
+            qb, sb = oracle.fp8_quantize(b)
+            gemm = lambda xm, w, s: oracle.gemm_fp8(qa[:len(xm)], qb, sa, sb)  # noqa: E731
+            w_bytes_per_step = sum(k * cols for _ in ms)
+        x, w, s = a, None, None
+    if fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped", "nvfp4", "mxfp4", "fp8") \
+            and mmax <= SMALL_M_MAX:
         if fmt in ("w4a16", "w8a16"):
             gen = wl.w4a16 if fmt == "w4a16" else wl.w8a16
             gemm = oracle.gemm_w4a16 if fmt == "w4a16" else oracle.gemm_w8a16
@@ -492,7 +520,8 @@ def run(name, steps, warmup, with_cpu, use_graph):
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}
     kernel = kernel_name(setup, setup.ms[dom])
-    roof["traffic"] = traffic_for(setup.kind, kernel)
+    roof["traffic"] = traffic_for("decode" if kernel.startswith("decode_gemm_kernel") else "tile",
+                                  kernel)
     roof["kernel"] = kernel
     roof["avg_launch_us"] = round(per_call[dom] * 1e6, 3)
     roof["step_avg_launch_us"] = round(dev_s / (steps * len(setup.calls)) * 1e6, 3)
@@ -547,9 +576,12 @@ def kernel_name(setup, m):
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     # same rules as the library's dispatch
     if setup.fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped", "nvfp4"):
-        big = m >= 256 and setup.n > 128 and setup.k % 8 == 0
+        big = (m >= 256 and setup.n > 128 and setup.k % 8 == 0
+               and -(-m // 256) * -(-setup.n // 256) >= 64)
         name = "pipe256_kernel" if big else "decode_gemm_kernel"
         return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
+    if m <= SMALL_M_MAX:
+        return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     k_tiles = -(-setup.k // (256 if setup.fmt == "mxfp4" else 128))
     big = m > 128 and setup.n > 128 and k_tiles >= 2 and (setup.fmt != "mxfp4" or setup.k % 128 == 0)
     name = "pipe256_kernel" if big else "tile_gemm_kernel"
