@@ -9,11 +9,12 @@
 // instruction with unit scales for e4m3fn), with the M <= 16 rows of X in the
 // A operand and a 16-column fragment tile of W in the B operand.
 //
-// Work split: a workgroup owns G column groups (16 columns each) and one
-// 16-row slab of X; its NW waves split the K tiles round-robin, so at any time
-// the waves of a workgroup read neighbouring tiles.  Each wave keeps D K tiles
-// of loads in flight in a register ring and its fp32 partial sums in
-// registers; the workgroup reduces them through LDS in a fixed order
+// Work split: a workgroup owns G column groups (16 columns each) and S
+// 16-row slabs of X; its NW waves split the K tiles round-robin, so at any
+// time the waves of a workgroup read neighbouring tiles.  Each wave keeps D K
+// tiles of loads in flight in a register ring (above eight rows the
+// activation part of a tile goes to a wave-private LDS slot instead, copied
+// with whole-row DMA reads) and its fp32 partial sums in registers; the workgroup reduces them through LDS in a fixed order
 // (deterministic, no atomics, no workspace) and the epilogue applies the
 // per-column scale (or the per-tensor FP8 / NVFP4 scales) once to the fp32
 // sum before rounding to the output type; the grouped formats apply their
@@ -94,7 +95,30 @@ struct DecodeAddr {
   int64_t meta_cg_stride; // bytes between column groups of metadata
   int meta_kt_stride;     // bytes of metadata per K tile
   uint32_t mlane;         // this lane's entries within a tile
+  // activations staged through LDS: the buffer over X, per (slab, copy
+  // instruction) the byte offset of this lane's 16 B in tile 0, and per
+  // operand piece this lane's byte offset within a staged slab
+  __amdgpu_buffer_rsrc_t xrsrc;
+  uint32_t xdma[8];
+  uint32_t xrd[4];
 };
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr uint32_t kXOutOfRange = 0x80000000u;   // past every activation buffer
+
+// Activation tiles staged through LDS.  A staged slab is the 16 rows x RB
+// bytes (RB = tile_x_bytes: 256 for fp16 X, 128 for e4m3 / E2M1 codes) of
+// one K tile, row-major, with 16-byte chunk c of row r stored at chunk
+// position c ^ swz(r).  The copy reads RB contiguous bytes per row (whole
+// cache lines: 4 rows x 256 B or 8 rows x 128 B per instruction), which the
+// vector memory path serves about three times faster than the 16 rows x 64 B
+// that the matrix-operand layout would read directly; the swizzle makes the
+// operand reads (16 rows, one chunk column each) hit 16 distinct 16-byte bank
+// groups.
+template <int FMT> __device__ __forceinline__ int x_swz(int r) {
+  return tile_x_bytes<FMT>() == 256 ? r : (r >> 1) & 7;
+}
+template <int FMT> constexpr int x_copy_instrs() { return tile_x_bytes<FMT>() == 256 ? 4 : 2; }
 
 // K index of the first element of X piece p of lane group g in tile kt.
 template <int FMT>
@@ -108,15 +132,43 @@ __device__ __forceinline__ int piece_k(int kt, int g, int p) {
 // weight tiles.  X pieces past K read as zero.  Rows past M load row M-1
 // instead (their outputs are never stored); groups past the last column load
 // the last group (likewise discarded).
-template <int FMT, int G, bool X_ELEMENTWISE, int NGT = 0, int S = 1>
+template <int FMT, int G, bool X_ELEMENTWISE, int NGT = 0, int S = 1, bool XL = false>
 __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const DecodeAddr& ad,
-                                           int kt) {
+                                           int kt, uint8_t* xs = nullptr) {
   constexpr int XV = DecodeTraits<FMT>::XV;
   constexpr int TB = DecodeTraits<FMT>::TB;
   constexpr int PSTRIDE = (FMT == 4) ? 16 : 64;    // bytes between a lane's pieces
   const uint8_t* xk = ad.x + (int64_t)kt * tile_x_bytes<FMT>();   // uniform
   const bool full = (kt + 1) * tile_k<FMT>() <= ad.K;             // uniform
-  if constexpr (!X_ELEMENTWISE) {
+  if constexpr (XL) {
+    // copy the S staged slabs of tile kt into this wave's LDS slot `xs`; in
+    // a partial last tile, chunks past K take an offset past the buffer and
+    // land as zeros (K % 8 == 0 for fp16, % 16 for e4m3, % 32 for E2M1: a
+    // chunk is wholly in or out).  Issued before the weight loads of the
+    // chunk, with nothing scheduled across: the weight loads complete after
+    // them.
+    constexpr int RB = tile_x_bytes<FMT>();
+    constexpr int NI = x_copy_instrs<FMT>();
+    constexpr int LPR = RB / 16;                  // lanes per row
+    constexpr int KPC = tile_k<FMT>() / LPR;      // K elements per chunk
+    const uint32_t kb = (uint32_t)kt * RB;
+    const int lane = __lane_id();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        uint32_t off = ad.xdma[q * NI + i] + kb;
+        if (!full) {
+          const int r = i * (64 / LPR) + lane / LPR;
+          const int c = (lane % LPR) ^ x_swz<FMT>(r);
+          if (kt * tile_k<FMT>() + c * KPC >= ad.K) off = kXOutOfRange;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ad.xrsrc, (lds_void_t*)(xs + q * 16 * RB + i * 1024),
+                                                 16, off, 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  } else if constexpr (!X_ELEMENTWISE) {
     if (full) {
 #pragma unroll
       for (int q = 0; q < S; ++q)
@@ -201,14 +253,38 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const Deco
   }
 }
 
-template <int FMT, int G, int NGT = 0, int S = 1>
+// Operand piece p of slab q: from the chunk's registers or, staged, from the
+// LDS slot.
+template <int FMT, int G, int NGT, int S, bool XL>
+__device__ __forceinline__ uintx4 x_piece(const Chunk<FMT, G, NGT, S>& ch, const DecodeAddr& ad,
+                                          const uint8_t* xs, int q, int p) {
+  if constexpr (XL)
+    return *reinterpret_cast<const uintx4*>(xs + q * 16 * tile_x_bytes<FMT>() + ad.xrd[p]);
+  else
+    return ch.x[q][p];
+}
+
+template <int FMT, int G, int NGT = 0, int S = 1, bool XL = false>
 __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
                                               floatx4 (&acc)[S][G], W4Masks mk,
-                                              const DecodeAddr& ad) {
+                                              const DecodeAddr& ad, const uint8_t* xs = nullptr) {
+  if constexpr (XL) {
+    // the staged copies of this tile were issued before its weight loads and
+    // loads complete in order: once the first weight register has landed, so
+    // has the slot.  The empty asm makes the compiler wait for that register
+    // here and keeps the LDS reads after the wait.
+    asm volatile("" ::"v"(ch.w[0][0][0]) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if constexpr (FMT == 3) {
     // two scaled FP4 instructions per group (blocks h = 0, 1); the lane's
     // scale bytes sit in the low byte (A) and at byte (cg & 3) of the loaded
     // word (W)
+    uintx4 xv[S][2];
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) xv[q][h] = x_piece<FMT, G, NGT, S, XL>(ch, ad, xs, q, h);
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -218,13 +294,18 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
         const int sb = (int)(ch.meta[g][h] >> ad.wsh[g]);
 #pragma unroll
         for (int q = 0; q < S; ++q) {
-          const uintx4& xa = ch.x[q][h];
+          const uintx4& xa = xv[q][h];
           const intx8 a = {(int)xa[0], (int)xa[1], (int)xa[2], (int)xa[3], 0, 0, 0, 0};
           acc[q][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               a, b, acc[q][g], kFmtFP4, kFmtFP4, 0, (int)ch.asc[q][h], 0, sb);
         }
       }
   } else if constexpr (FMT == 4) {
+    uintx4 xv[S][2];
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) xv[q][p] = x_piece<FMT, G, NGT, S, XL>(ch, ad, xs, q, p);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const intx8 b = {(int)ch.w[g][0][0], (int)ch.w[g][0][1], (int)ch.w[g][0][2],
@@ -232,9 +313,10 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
                        (int)ch.w[g][1][2], (int)ch.w[g][1][3]};
 #pragma unroll
       for (int q = 0; q < S; ++q) {
-        const intx8 a = {(int)ch.x[q][0][0], (int)ch.x[q][0][1], (int)ch.x[q][0][2],
-                         (int)ch.x[q][0][3], (int)ch.x[q][1][0], (int)ch.x[q][1][1],
-                         (int)ch.x[q][1][2], (int)ch.x[q][1][3]};
+        const uintx4& x0 = xv[q][0];
+        const uintx4& x1 = xv[q][1];
+        const intx8 a = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
         acc[q][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             a, b, acc[q][g], kFmtFP8, kFmtFP8, 0, kE8M0One, 0, kE8M0One);
       }
@@ -242,6 +324,10 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
   } else {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      half8_t xv[S];
+#pragma unroll
+      for (int q = 0; q < S; ++q)
+        xv[q] = __builtin_bit_cast(half8_t, (x_piece<FMT, G, NGT, S, XL>(ch, ad, xs, q, s)));
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         half8_t b;
@@ -264,8 +350,7 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
         }
 #pragma unroll
         for (int q = 0; q < S; ++q)
-          acc[q][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              __builtin_bit_cast(half8_t, ch.x[q][s]), b, acc[q][g], 0, 0, 0);
+          acc[q][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[q], b, acc[q][g], 0, 0, 0);
       }
     }
   }
@@ -274,7 +359,10 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
 // NGT > 0: grouped W4A16 / W8A16 (scales and zero points in the metadata
 // segment at wp + meta_offset; `scales` unused).
 // S: 16-row slabs per workgroup (rows m0 .. m0 + 16 S - 1).
-template <int FMT, int G, int NW, int D, bool X_ELEMENTWISE, int NGT = 0, int S = 1>
+// XL: activation tiles staged through LDS (each wave owns D slots of S
+// staged slabs); the host guarantees that X spans fewer than 2^31 bytes.
+template <int FMT, int G, int NW, int D, bool X_ELEMENTWISE, int NGT = 0, int S = 1,
+          bool XL = false>
 __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ wp,
     const _Float16* __restrict__ scales, const float* __restrict__ scale_a,
@@ -283,8 +371,16 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   static_assert(NW >= 2, "the K split needs at least two waves");
   static_assert(D >= 2 && D <= 4, "prefetch depth 2..4");
   static_assert(S == 1 || S == 2 || S == 4, "1, 2 or 4 slabs");
+  static_assert(!XL || (!X_ELEMENTWISE && S * x_copy_instrs<FMT>() <= 8),
+                "staged activations: aligned rows, at most 8 copy instructions per tile");
   constexpr int TB = DecodeTraits<FMT>::TB;
-  __shared__ floatx4 red[NW][G][kWave];
+  constexpr int RB = tile_x_bytes<FMT>();
+  constexpr int XSLOT = S * 16 * RB;             // one staged tile (S slabs)
+  constexpr int XWAVE = D * XSLOT;               // one wave's ring of slots
+  constexpr int RED_BYTES = NW * G * kWave * 16;
+  constexpr int SMEM = XL && NW * XWAVE > RED_BYTES ? NW * XWAVE : RED_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  floatx4 (*red)[G][kWave] = reinterpret_cast<floatx4 (*)[G][kWave]>(smem);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -329,6 +425,32 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   ad.meta = FMT == 3 ? wp + meta_offset : wp + meta_offset + (int64_t)cg0 * ad.meta_cg_stride;
   ad.mlane = FMT == 7 ? (uint32_t)((lane & 15) * 8 + 4 * (ad.g >> 1))
                       : (uint32_t)((lane & 15) * (NGT > 0 ? NGT : 1) * 4);
+  if constexpr (XL) {
+    constexpr int NI = x_copy_instrs<FMT>();
+    constexpr int LPR = RB / 16;
+    const int64_t rowbytes = FMT == 3 ? K / 2 : FMT == 4 ? (int64_t)K : 2 * (int64_t)K;
+    ad.xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(x), (short)0,
+                                                 (int)(M * rowbytes), 0x00020000);
+    // copy instruction i of slab q: row i * (64 / LPR) + lane / LPR of the
+    // slab, chunk (lane % LPR) ^ swz(row); rows past M copy row M - 1
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int r = i * (64 / LPR) + lane / LPR;
+        const int row = min(m0 + 16 * q + r, M - 1);
+        const int c = (lane % LPR) ^ x_swz<FMT>(r);
+        ad.xdma[q * NI + i] = (uint32_t)(row * rowbytes + 16 * c);
+      }
+    // operand piece p of lane (row r = lane & 15, group g): chunk 4 p + g
+    // (fp16 step p; E2M1 block p) or 2 g + p (e4m3 half p)
+    const int r = lane & 15;
+#pragma unroll
+    for (int p = 0; p < DecodeTraits<FMT>::XV; ++p) {
+      const int c = FMT == 4 ? 2 * ad.g + p : 4 * p + ad.g;
+      ad.xrd[p] = (uint32_t)(r * RB + 16 * (c ^ x_swz<FMT>(r)));
+    }
+  }
 
   W4Masks mk{};
   if constexpr (FMT == 1) mk = W4Masks{vgpr_const(0x000f000fu), vgpr_const(0x00f000f0u)};
@@ -342,25 +464,29 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   // K tiles wave, wave + NW, ...; a ring of D register buffers keeps D tiles
   // of loads in flight per wave
   Chunk<FMT, G, NGT, S> ring[D];
+  uint8_t* const xw = smem + wave * XWAVE;   // this wave's staging slots (XL)
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (wave + d * NW < KT)
-      load_chunk<FMT, G, X_ELEMENTWISE, NGT, S>(ring[d], ad, wave + d * NW);
+      load_chunk<FMT, G, X_ELEMENTWISE, NGT, S, XL>(ring[d], ad, wave + d * NW, xw + d * XSLOT);
   for (int base = wave; base < KT; base += D * NW) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int kt = base + d * NW;
       if (kt < KT) {
-        compute_chunk<FMT, G, NGT, S>(ring[d], acc, mk, ad);
+        compute_chunk<FMT, G, NGT, S, XL>(ring[d], acc, mk, ad, xw + d * XSLOT);
         if (kt + D * NW < KT)
-          load_chunk<FMT, G, X_ELEMENTWISE, NGT, S>(ring[d], ad, kt + D * NW);
+          load_chunk<FMT, G, X_ELEMENTWISE, NGT, S, XL>(ring[d], ad, kt + D * NW,
+                                                        xw + d * XSLOT);
       }
     }
   }
+  // the partial-sum buffer reuses the staging slots of every wave
+  if constexpr (XL) __syncthreads();
 
   // ---- reduce the NW partial tiles in a fixed order, one slab at a time
   const float fp8_scale = (FMT == 4) ? (*scale_a) * (*scale_b) : (FMT == 7) ? *scale_a : 1.0f;
-  const float* redf = reinterpret_cast<const float*>(&red[0][0][0]);
+  const float* redf = reinterpret_cast<const float*>(smem);
   constexpr int OUT = 16 * 16 * G;
 #pragma unroll
   for (int q = 0; q < S; ++q) {
@@ -405,7 +531,24 @@ struct DecodeConfig {
   int nw;  // waves per workgroup (K split)
   int d;   // K tiles in flight per wave
   int s;   // 16-row slabs per workgroup
+  bool xl; // activation tiles staged through LDS
 };
+
+// Whether a launch stages its activation tiles through LDS: with more than
+// eight rows, eight waves, and at most 8 copy instructions per tile (fp16 X:
+// up to two slabs); X must span fewer than 2^31 bytes (32-bit buffer
+// offsets).  Measured on MI355X (K = 4096 / 8192, N = 8192 .. 28672, each
+// shape timed staged and direct in alternation, best of three): at M = 12
+// the two are within 1 %; at M = 16 staging saves 1 % (FP8) to 5 % (INT8),
+// at M = 32 8 % (INT4) to 11 % (grouped INT8), at M = 64 .. 128 up to 21 %
+// (FP8).  The grouped INT4 and NVFP4 launches with seven column groups and
+// one slab are the exception (NVFP4 at M = 16: 25.4 us direct, 26.4
+// staged); they stage from two slabs on.
+bool use_x_lds(int fmt, int64_t M, int nw, int s, int64_t KT) {
+  const int rb = fmt == 3 || fmt == 4 ? 128 : 256;
+  const int ni = rb == 256 ? 4 : 2;
+  return M > 8 && nw == 8 && s * ni <= 8 && M * KT * rb < ((int64_t)1 << 31);
+}
 
 // Launch shape: about one workgroup per CU.  Measured on MI355X at the decode
 // workloads (W8A16 K=4096 N=11008, W4A16 K=8192 N=28672, FP8 K=N=8192, M = 1
@@ -426,20 +569,21 @@ DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
   const int64_t gmax = s == 1 ? (fmt == 1 ? 8 : 4) : s == 2 ? (fmt == 1 ? 7 : 4) : fmt == 3 ? 2 : 3;
   int64_t g = cdiv(CG, 256);
   g = g < 1 ? 1 : (g > gmax ? gmax : g);
-  DecodeConfig c{(int)g, 8, s == 1 && fmt == 2 ? 3 : 2, s};
+  DecodeConfig c{(int)g, 8, s == 1 && fmt == 2 ? 3 : 2, s, false};
   if (KT < 16) c.nw = 4;
+  c.xl = use_x_lds(fmt, M, c.nw, c.s, KT);
   return c;
 }
 
 // MXFP4 (FMT 3): `s` is the A E8M0 array and meta_offset the offset of the W
 // scale segment in the packed weight.
-template <int FMT, int G, int NW, int D, bool ELEMENTWISE, int S = 1>
+template <int FMT, int G, int NW, int D, bool ELEMENTWISE, int S = 1, bool XL = false>
 hipError_t launch_cfg(const void* x, const void* w, const void* s, const float* sa,
                       const float* sb, void* y, int64_t M, int64_t N, int64_t K, int64_t KT,
                       int64_t CG, hipStream_t stream, int64_t meta_offset = 0) {
   dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16 * S));
   dim3 block(NW * kWave);
-  hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, D, ELEMENTWISE, 0, S>), grid, block, 0,
+  hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, D, ELEMENTWISE, 0, S, XL>), grid, block, 0,
                      stream,
                      (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)s, sa, sb,
                      (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT, (int)CG, meta_offset);
@@ -457,12 +601,14 @@ hipError_t launch_fmt_cfg(const DecodeConfig& c, const void* x, const void* w, c
     if (K % 8 != 0)
       return launch_cfg<FMT, 1, 4, 2, true>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream);
   }
-#define QG_CASE(GG, WW, DD, SS)                                                             \
-  if (c.g == GG && c.nw == WW && c.d == DD && c.s == SS)                                    \
-    return launch_cfg<FMT, GG, WW, DD, false, SS>(x, w, s, sa, sb, y, M, N, K, KT, CG, stream, \
-                                                  meta_offset);
-#define QG_G(GG) QG_CASE(GG, 8, DEPTH, 1) QG_CASE(GG, 4, DEPTH, 1)
-#define QG_GS(GG, SS) QG_CASE(GG, 8, 2, SS) QG_CASE(GG, 4, 2, SS)
+#define QG_CASE(GG, WW, DD, SS, XX)                                                         \
+  if (c.g == GG && c.nw == WW && c.d == DD && c.s == SS && c.xl == XX)                      \
+    return launch_cfg<FMT, GG, WW, DD, false, SS, XX>(x, w, s, sa, sb, y, M, N, K, KT, CG,  \
+                                                      stream, meta_offset);
+#define QG_G(GG) \
+  QG_CASE(GG, 8, DEPTH, 1, false) QG_CASE(GG, 4, DEPTH, 1, false) QG_CASE(GG, 8, DEPTH, 1, true)
+#define QG_GS(GG, SS) QG_CASE(GG, 8, 2, SS, false) QG_CASE(GG, 4, 2, SS, false) \
+  if constexpr (SS * (FMT == 3 || FMT == 4 ? 2 : 4) <= 8) { QG_CASE(GG, 8, 2, SS, true) }
   constexpr int DEPTH = FMT == 2 ? 3 : 2;
   QG_G(1) QG_G(2) QG_G(3) QG_G(4)
   if constexpr (FMT == 1) {   // up to eight INT4 column groups fit in registers
@@ -509,13 +655,14 @@ int slab_groups(int64_t CG, int gmax, int64_t KT) {
 
 // Grouped formats: the same kernel with NGT metadata words per column and K
 // tile, D = 2; G and NW as for the per-column formats with fewer rows.
-template <int FMT, int NGT, int G, int NW, int S>
+template <int FMT, int NGT, int G, int NW, int S, bool XL>
 hipError_t launch_grouped_cfg(const void* x, const void* w, void* y, int64_t M, int64_t N,
                               int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
                               hipStream_t stream) {
   dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16 * S));
   dim3 block(NW * kWave);
-  hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, 2, false, NGT, S>), grid, block, 0, stream,
+  hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, 2, false, NGT, S, XL>), grid, block, 0,
+                     stream,
                      (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)nullptr,
                      (const float*)nullptr, (const float*)nullptr, (uint16_t*)y, (int)M, (int)N,
                      (int)K, (int)KT, (int)CG, meta_offset);
@@ -531,19 +678,23 @@ hipError_t launch_grouped_ngt(const void* x, const void* w, void* y, int64_t M, 
   // two slabs with four metadata words per tile leave room for four INT4
   // groups (seven spill)
   const int g = slab_groups(CG, FMT == 1 && !(s == 2 && NGT == 4) ? 7 : 4, KT);
-#define QG_GCASE(GG, WW, SS)                                                               \
-  if (g == GG && nw == WW && s == SS)                                                      \
-    return launch_grouped_cfg<FMT, NGT, GG, WW, SS>(x, w, y, M, N, K, KT, CG, meta_offset,  \
-                                                    stream);
-  QG_GCASE(1, 4, 1) QG_GCASE(1, 8, 1) QG_GCASE(2, 4, 1) QG_GCASE(2, 8, 1) QG_GCASE(3, 8, 1)
-  QG_GCASE(4, 8, 1)
-  QG_GCASE(1, 8, 2) QG_GCASE(2, 8, 2) QG_GCASE(3, 8, 2) QG_GCASE(4, 8, 2)
+  // seven groups with one slab load faster directly
+  const bool xl = use_x_lds(FMT, M, nw, s, KT) && (s > 1 || g <= 4);
+#define QG_GCASE(GG, WW, SS, XX)                                                            \
+  if (g == GG && nw == WW && s == SS && xl == XX)                                           \
+    return launch_grouped_cfg<FMT, NGT, GG, WW, SS, XX>(x, w, y, M, N, K, KT, CG,           \
+                                                        meta_offset, stream);
+#define QG_GCASE2(GG, SS) QG_GCASE(GG, 8, SS, false) QG_GCASE(GG, 8, SS, true)
+  QG_GCASE(1, 4, 1, false) QG_GCASE(2, 4, 1, false)
+  QG_GCASE2(1, 1) QG_GCASE2(2, 1) QG_GCASE2(3, 1) QG_GCASE2(4, 1)
+  QG_GCASE2(1, 2) QG_GCASE2(2, 2) QG_GCASE2(3, 2) QG_GCASE2(4, 2)
   if constexpr (FMT == 1) {
-    QG_GCASE(7, 8, 1)
+    QG_GCASE(7, 8, 1, false)
   }
   if constexpr (FMT == 1 && NGT < 4) {
-    QG_GCASE(7, 8, 2)
+    QG_GCASE2(7, 2)
   }
+#undef QG_GCASE2
 #undef QG_GCASE
   return hipErrorInvalidValue;
 }
@@ -559,13 +710,13 @@ hipError_t launch_grouped_fmt(const void* x, const void* w, void* y, int64_t M, 
   }
 }
 
-template <int G, int NW, int S>
+template <int G, int NW, int S, bool XL>
 hipError_t launch_nvfp4_cfg(const void* x, const void* w, const float* gs, void* y, int64_t M,
                             int64_t N, int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
                             hipStream_t stream) {
   dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16 * S));
   dim3 block(NW * kWave);
-  hipLaunchKernelGGL((decode_gemm_kernel<7, G, NW, 2, false, 1, S>), grid, block, 0, stream,
+  hipLaunchKernelGGL((decode_gemm_kernel<7, G, NW, 2, false, 1, S, XL>), grid, block, 0, stream,
                      (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)nullptr, gs,
                      (const float*)nullptr, (uint16_t*)y, (int)M, (int)N, (int)K, (int)KT,
                      (int)CG, meta_offset);
@@ -580,13 +731,16 @@ hipError_t launch_decode_nvfp4(const void* x, const void* w_packed, const float*
   const int g = slab_groups(pg.cg, 7, pg.kt);
   const int nw = pg.kt < 16 ? 4 : 8;
   const int s = slab_count(M, nw);
-#define QG_NCASE(GG, WW, SS)                                                               \
-  if (g == GG && nw == WW && s == SS)                                                      \
-    return launch_nvfp4_cfg<GG, WW, SS>(x, w_packed, global_scale, y, M, N, K, pg.kt,      \
-                                        pg.cg, pg.scales, stream);
-  QG_NCASE(1, 4, 1) QG_NCASE(1, 8, 1) QG_NCASE(2, 4, 1) QG_NCASE(2, 8, 1) QG_NCASE(3, 8, 1)
-  QG_NCASE(4, 8, 1) QG_NCASE(7, 8, 1)
-  QG_NCASE(1, 8, 2) QG_NCASE(2, 8, 2) QG_NCASE(3, 8, 2) QG_NCASE(4, 8, 2) QG_NCASE(7, 8, 2)
+  const bool xl = use_x_lds(7, M, nw, s, pg.kt) && (s > 1 || g <= 4);   // as for grouped
+#define QG_NCASE(GG, WW, SS, XX)                                                           \
+  if (g == GG && nw == WW && s == SS && xl == XX)                                          \
+    return launch_nvfp4_cfg<GG, WW, SS, XX>(x, w_packed, global_scale, y, M, N, K, pg.kt,  \
+                                            pg.cg, pg.scales, stream);
+#define QG_NCASE2(GG, SS) QG_NCASE(GG, 8, SS, false) QG_NCASE(GG, 8, SS, true)
+  QG_NCASE(1, 4, 1, false) QG_NCASE(2, 4, 1, false)
+  QG_NCASE2(1, 1) QG_NCASE2(2, 1) QG_NCASE2(3, 1) QG_NCASE2(4, 1) QG_NCASE(7, 8, 1, false)
+  QG_NCASE2(1, 2) QG_NCASE2(2, 2) QG_NCASE2(3, 2) QG_NCASE2(4, 2) QG_NCASE2(7, 2)
+#undef QG_NCASE2
 #undef QG_NCASE
   return hipErrorInvalidValue;
 }
