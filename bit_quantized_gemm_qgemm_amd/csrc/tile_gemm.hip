@@ -413,12 +413,13 @@ __device__ __forceinline__ void stage16(const floatx4 (&acc)[8][8], uint8_t* ct,
 }
 
 // Copy the staged tile to C (rows past M and columns past N are dropped).
+template <int NT = kThreads>
 __device__ __forceinline__ void pipe_copy_out(const uint8_t* ct, const PipeOut& o, int m0,
                                               int n0) {
   const bool vec = (o.N & 7) == 0;
 #pragma unroll 4
-  for (int j = 0; j < kCTileBytes / 16 / kThreads; ++j) {
-    const int q = (int)threadIdx.x + kThreads * j;
+  for (int j = 0; j < kCTileBytes / 16 / NT; ++j) {
+    const int q = (int)threadIdx.x + NT * j;
     const int row = q >> 5, ch = q & 31;
     const int gm = m0 + row, gn = n0 + 8 * ch;
     if (gm >= o.M || gn >= o.N) continue;
@@ -452,123 +453,6 @@ __device__ __forceinline__ void stage32(const floatx16 (&acc)[4][4], uint8_t* ct
       }
     }
 }
-
-// MXFP4: 4 x 4 fragments of 32 x 32 per wave; one step = 128 K elements =
-// two v_mfma_scale_f32_32x32x64_f8f6f4 per fragment pair (the 32 x 32 x 64
-// form keeps the matrix pipe fuller than 16 x 16 x 128 on FP4 operands).
-// Lane l feeds row (or column) l & 31 with the 32 contiguous bytes 32 j + [0,
-// 32) of the step (j = l >> 5), i.e. 32-element blocks 2j and 2j + 1; half h
-// of the pair multiplies block 2j + h.  Both operands use this K order, and
-// each lane's scale byte for half h is block 2j + h of its row or column: the
-// lane shifts its scale word so that one byte select serves all lanes.
-// Stage: A | W 16 tiles x 1 KB (half h of each tile as is: [kg 4][column
-// 16][16 B]) | A scales [256 rows][4 blocks] | W scales [wn 2][lane 64][tile
-// 8] (lane = column + 16 kg).
-struct Fp4Pipe {
-  static constexpr int FMT = 3;
-  template <class F>
-  __device__ __forceinline__ static void init(F&, F&) {}
-  static constexpr int GROUP_WORDS = 0;
-  static constexpr int PARTS = 4;
-  static constexpr int STEPS_PER_TILE = 2;
-  static constexpr int B = 16 * 1024, SA = kBig * 4, SB = 2 * 512;
-  static constexpr int STAGE = kStageA + B + SA + SB;
-  static constexpr int DMA = 10;
-  static constexpr int NST = 4;                  // 4 x 34 KB of LDS
-  static constexpr bool CP_INTERLEAVE = true;
-  static constexpr int CP_PIN_PAIRS = 6;         // copies of parts 0 / 1: 4 / 6
-  typedef floatx16 Acc[4][4];
-  struct Frags {
-    uintx4 alo[4], ahi[4];
-    uintx4 blo[4], bhi[4];
-    uint32_t sa[4];   // row scale words (blocks 0-3 of the step)
-    uintx2 sb[2];     // [h] column scale words of tiles 0-3 and 4-7
-  };
-  struct Lane {
-    int alo, ahi, sa, b, sb;
-    uint32_t sha, shb;
-  };
-  __device__ __forceinline__ static int swizzle(int r) { return (r >> 2) & 3; }
-  __device__ __forceinline__ static int row_bytes(int K) { return K / 2; }
-  __device__ __forceinline__ static void issue_rest(uint8_t* st, int ks, int wave, int lane,
-                                                    int m0, int cg0, const PipeArgs& g,
-                                                    const PipeRsrc& rs) {
-    const int kt = ks >> 1, h = ks & 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 4 * wave + j;
-      const uint32_t off = ((uint32_t)(cg0 + t) * g.KT + kt) * kTileBytes + 1024u * h + 16u * lane;
-      dma16(rs.w, st + kStageA + t * 1024, off);
-    }
-    const int sc_cols = g.K / 32;   // K % 128 == 0: four blocks per row are one dword
-    const int r = 64 * wave + lane;
-    const int blk = 4 * ks;
-    const uint32_t off = blk < sc_cols ? (uint32_t)(m0 + r) * (uint32_t)sc_cols + blk
-                                       : kOutOfRange;
-    dma4(rs.sa, st + kStageA + B + 256 * wave, off);
-    const uint32_t soff = ((uint32_t)(cg0 / 8 + (wave >> 1)) * g.KS + ks) * 512u +
-                          256u * (wave & 1) + 4u * lane;
-    dma4(rs.sw, st + kStageA + B + SA + 256 * wave, soff);
-  }
-  __device__ __forceinline__ static Lane lane_offsets(int wm, int wn, int lane) {
-    const int r = wm * 128 + (lane & 31), j = lane >> 5, swz = swizzle(r);
-    const int par = (lane >> 4) & 1;   // column tile 2P + par of fragment P
-    Lane L;
-    L.alo = r * kStepBytes + 16 * ((2 * j) ^ swz);
-    L.ahi = r * kStepBytes + 16 * ((2 * j + 1) ^ swz);
-    L.sa = kStageA + B + 4 * r;
-    L.b = kStageA + (wn * 8 + par) * 1024 + 512 * j + 16 * (lane & 15);
-    L.sb = kStageA + B + SA + wn * 512 + 8 * ((lane & 15) + 32 * j);
-    L.sha = 16u * j;
-    L.shb = 8u * par;
-    return L;
-  }
-  template <int P>
-  __device__ __forceinline__ static void read(Frags& F, const uint8_t* st, const Lane& L) {
-    F.alo[P] = *reinterpret_cast<const uintx4*>(st + L.alo + P * 2048);
-    F.ahi[P] = *reinterpret_cast<const uintx4*>(st + L.ahi + P * 2048);
-    F.sa[P] = *reinterpret_cast<const uint32_t*>(st + L.sa + P * 128);
-    F.blo[P] = *reinterpret_cast<const uintx4*>(st + L.b + P * 2048);
-    F.bhi[P] = *reinterpret_cast<const uintx4*>(st + L.b + P * 2048 + 256);
-    if (P < 2) F.sb[P] = *reinterpret_cast<const uintx2*>(st + L.sb + 128 * P);
-  }
-  // The lane's scale shifts run in the step that uses the words (read one
-  // step earlier): shifting right after the read would make the matrix
-  // instructions behind it wait for the LDS.
-  template <int P, int H>
-  __device__ __forceinline__ static void mma_half(const Frags& F, const Lane& L, Acc& acc) {
-    const uintx4& b = H ? F.bhi[P] : F.blo[P];
-    const intx8 bf = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
-    // byte 2 (P & 1) of the shifted word is the scale of column tile 2P + par
-    const int sb = (int)(F.sb[H][P >> 1] >> L.shb);
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm) {
-      const uintx4& a = H ? F.ahi[fm] : F.alo[fm];
-      const intx8 af = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
-      // byte h of the shifted word is block 2j + h of the row
-      const int sa = (int)(F.sa[fm] >> L.sha);
-      acc[fm][P] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          af, bf, acc[fm][P], kFmtFP4, kFmtFP4, H, sa, 2 * (P & 1), sb);
-    }
-  }
-  template <int P>
-  __device__ __forceinline__ static void mma(const Frags& F, const Lane& L, Acc& acc) {
-    mma_half<P, 0>(F, L, acc);
-    mma_half<P, 1>(F, L, acc);
-  }
-  __device__ __forceinline__ static void zero(Acc& acc) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  }
-  __device__ __forceinline__ static void stage(const Acc& acc, uint8_t* ct, const PipeOut& o,
-                                               int, int wm, int wn, int lane) {
-    stage32(acc, ct, o, wm, wn, lane);
-  }
-};
 
 // FP8: 4 x 4 fragments of 32 x 32 per wave; one step = 64 K elements = one
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) per fragment pair.
@@ -983,6 +867,398 @@ __global__ __launch_bounds__(kThreads) void pipe256_kernel(
   pipe_copy_out(smem, o, m0, cg0 * 16);
 }
 
+// ---- MXFP4, 256 x 256 tiles, 256-element K steps ------------------------
+// 256 x 256 output tile per workgroup, NW waves (4: one per SIMD, each owning
+// a 128 x 128 block of C, 4 x 4 fragments of 32 x 32; 8: two per SIMD, 128 x
+// 64 each).  A K step is one packed W tile: 256 elements, 128 bytes of an A
+// row, so every A copy reads whole 128-byte lines (8 rows x 128 B per
+// instruction).  The earlier 64-byte step read halves of 16 lines per
+// instruction, which the vector memory path serves several times slower; at
+// M = N = K = 8192 the move took the GEMM from 296 to 274 us.  Four and eight
+// waves measured the same (274 / 277 us), and so did issuing all of a step's
+// copies in one quarter or spreading them over two; with no copies in the loop
+// at all the kernel takes 205 us, so the copies and the compute side (matrix
+// instructions, LDS fragment reads, the per-step barrier) each hold part of
+// the time.
+//
+// LDS, two stages s = 0, 1 of each part (the A and W parts of both stages
+// sit below 64 KB and 128 KB so that one address register per quarter and a
+// constant offset reach every fragment):
+//   A  [s][256 rows][128 B] at 32 KB s, 16-byte chunk c of row r at slot
+//      c ^ ((r >> 1) & 7): a fragment read (32 rows, one chunk each) then
+//      hits 16 distinct 16-byte bank groups per 16 lanes;
+//   W  [s][16 tiles][2 KB] at 64 KB + 32 KB s: the packed tiles of the step as
+//      they are ([chunk 8][column 16][16 B], chunk c = K elements 32c + [0,
+//      32) of the step);
+//   SA [s][256 rows][8 B] at 128 KB + 2 KB s: the eight E8M0 bytes of each A
+//      row;
+//   SB [s][2][1 KB] at 132 KB + 2 KB s: the packed W scale chunks of the step
+//      for the two 128-column halves ([chunk 8][column 16][tile 8]).
+// Quarter u (0..3) of a step is one matrix instruction per fragment pair;
+// lane l feeds row (column) l & 31 with chunk 4j + u (j = l >> 5), so the
+// instruction covers blocks u and 4 + u and each lane's scale is byte u of
+// dword j of its row's (column's) eight scale bytes.
+template <int NW>
+struct Mx256 {
+  static constexpr int FN = 16 / NW;                    // 32-column fragments per wave
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int ROW = 128;                         // A bytes per row and step
+  static constexpr int A_STAGE = kBig * ROW;              // 32 KB
+  static constexpr int W_OFF = 2 * A_STAGE;               // 64 KB
+  static constexpr int W_STAGE = 16 * kTileBytes;         // 32 KB
+  static constexpr int SA_OFF = W_OFF + 2 * W_STAGE;      // 128 KB
+  static constexpr int SA_STAGE = kBig * 8;               // 2 KB
+  static constexpr int SB_OFF = SA_OFF + 2 * SA_STAGE;    // 132 KB
+  static constexpr int SB_STAGE = 2048;
+  static constexpr int LDS = SB_OFF + 2 * SB_STAGE;       // 136 KB
+  typedef floatx16 Acc[4][FN];
+  struct Quarter {
+    uintx4 a[4];
+    uintx4 b[FN];
+    uint32_t sb[FN / 2];   // the scale bytes of the lane's column in this wave's tiles
+  };
+  struct Lane {
+    int a[4], b[4], sb, sa;   // stage 0; quarter u of sb is 128 u further
+    uint32_t shb;
+  };
+  __device__ __forceinline__ static int swizzle(int r) { return (r >> 1) & 7; }
+  // wave (wm, wn): rows 128 wm + [0, 128), columns 32 FN wn + [0, 32 FN) =
+  // column tiles 2 FN wn .. 2 FN wn + 2 FN - 1
+  __device__ __forceinline__ static Lane lane_offsets(int wm, int wn, int lane) {
+    const int r = wm * 128 + (lane & 31), j = lane >> 5;
+    const int par = (lane >> 4) & 1;
+    Lane L;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = 4 * j + u;
+      L.a[u] = r * ROW + 16 * (c ^ swizzle(r));
+      L.b[u] = W_OFF + (wn * 2 * FN + par) * kTileBytes + c * 256 + 16 * (lane & 15);
+    }
+    // the wave's tiles are dwords (2 FN wn / 4 ..) of its column's 8-byte
+    // entry in 128-column half 2 FN wn / 8
+    L.sb = SB_OFF + (2 * FN * wn / 8) * 1024 + 4 * j * 128 + 8 * (lane & 15) +
+           4 * ((2 * FN * wn / 4) & 1);
+    L.sa = SA_OFF + 8 * r + 4 * j;
+    L.shb = 8u * par;
+    return L;
+  }
+  template <int S, int U>
+  __device__ __forceinline__ static void read(Quarter& X, const uint8_t* lds, const Lane& L) {
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm)
+      X.a[fm] = *reinterpret_cast<const uintx4*>(lds + L.a[U] + (S * A_STAGE + fm * 32 * ROW));
+#pragma unroll
+    for (int p = 0; p < FN; ++p)
+      X.b[p] =
+          *reinterpret_cast<const uintx4*>(lds + L.b[U] + (S * W_STAGE + p * 2 * kTileBytes));
+#pragma unroll
+    for (int d = 0; d < FN / 2; ++d)
+      X.sb[d] = *reinterpret_cast<const uint32_t*>(lds + L.sb + (S * SB_STAGE + U * 128 + 4 * d));
+  }
+  template <int S>
+  __device__ __forceinline__ static void read_sa(uint32_t (&sa)[4], const uint8_t* lds,
+                                                 const Lane& L) {
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm)
+      sa[fm] = *reinterpret_cast<const uint32_t*>(lds + L.sa + (S * SA_STAGE + fm * 32 * 8));
+  }
+  template <int U, int P>
+  __device__ __forceinline__ static void mma_pair(const Quarter& X, const uint32_t (&sa)[4],
+                                                  const Lane& L, Acc& acc) {
+    const intx8 bf = {(int)X.b[P][0], (int)X.b[P][1], (int)X.b[P][2], (int)X.b[P][3],
+                      0, 0, 0, 0};
+    // byte 2 (P & 1) of the shifted word P / 2: tile 2P + par of the wave's
+    const int sb = (int)(X.sb[P >> 1] >> L.shb);
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      const intx8 af = {(int)X.a[fm][0], (int)X.a[fm][1], (int)X.a[fm][2], (int)X.a[fm][3],
+                        0, 0, 0, 0};
+      acc[fm][P] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          af, bf, acc[fm][P], kFmtFP4, kFmtFP4, U, (int)sa[fm], 2 * (P & 1), sb);
+    }
+  }
+  template <int U>
+  __device__ __forceinline__ static void mma(const Quarter& X, const uint32_t (&sa)[4],
+                                             const Lane& L, Acc& acc) {
+    mma_pair<U, 0>(X, sa, L, acc);
+    mma_pair<U, 1>(X, sa, L, acc);
+    if constexpr (FN == 4) {
+      mma_pair<U, 2>(X, sa, L, acc);
+      mma_pair<U, 3>(X, sa, L, acc);
+    }
+  }
+
+  // The copies of a step (32 of A: 8 rows x 128 B each; 16 W tiles: two 1 KB
+  // halves each; 8 of A scales: 32 rows x 8 B each; 8 of W scales: 256 B
+  // each), split evenly over the waves.  Everything but the step's own
+  // offset is fixed per wave and lane.
+  static constexpr int NA = 32 / NW, NT = 16 / NW, NS = 8 / NW;
+  static constexpr int COPIES = NA + 2 * NT + 2 * NS;
+  struct Copies {
+    __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
+    uint32_t a_base[NA];   // A: row offset plus the lane's chunk
+    int a_kb[NA];          // A: the chunk's byte within a step
+    uint32_t w_base[NT];   // W: the tile's first K tile plus the lane's 16 B
+    uint32_t sa_base[NS];  // A scales: the lane's row and dword
+    int sa_kb;             // A scales: the dword's byte within a step (0 or 4)
+    uint32_t sw_base[NS];  // W scales: the copy's 256 B in step 0
+    int row_bytes, sc_cols, KT;
+    int a_lds[NA], w_lds[NT], sa_lds[NS], sw_lds[NS];
+  };
+  __device__ __forceinline__ static Copies plan(int wave, int lane, int m0, int cg0,
+                                                const PipeArgs& g, const PipeRsrc& rs) {
+    Copies C;
+    C.ra = rs.a;
+    C.rw = rs.w;
+    C.rsa = rs.sa;
+    C.rsw = rs.sw;
+    C.row_bytes = g.K / 2;
+    C.sc_cols = g.K / 32;
+    C.KT = g.KT;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int q = NA * wave + i;
+      const int r = 8 * q + (lane >> 3);
+      const int c = (lane & 7) ^ swizzle(r);
+      C.a_kb[i] = 16 * c;
+      C.a_base[i] = (uint32_t)(m0 + r) * (uint32_t)C.row_bytes + 16u * c;
+      C.a_lds[i] = q * 1024;
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int t = NT * wave + i;
+      C.w_base[i] = (uint32_t)(cg0 + t) * (uint32_t)g.KT * kTileBytes + 16u * lane;
+      C.w_lds[i] = t * kTileBytes;
+    }
+    C.sa_kb = 4 * (lane & 1);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int q = NS * wave + i;   // 0 .. 7
+      C.sa_base[i] = (uint32_t)(m0 + 32 * q + (lane >> 1)) * (uint32_t)C.sc_cols + C.sa_kb;
+      C.sa_lds[i] = 256 * q;
+      C.sw_base[i] = (uint32_t)(cg0 / 8 + (q >> 2)) * (uint32_t)g.KS * 512u + 256u * (q & 3) +
+                     4u * lane;
+      C.sw_lds[i] = 256 * q;
+    }
+    return C;
+  }
+  // K % 128 == 0, so a 16-byte A chunk or a 4-byte scale word is wholly
+  // inside K or past it; past it the copy reads zeros, and so does every copy
+  // of a step s >= KT (all-zero codes and scales: such a step adds exactly 0)
+  // Part H (0 or 1) of the copies of step s: half of the A and W copies and
+  // half of the scale copies (with one scale copy of each kind per wave, the
+  // A scales go in part 0 and the W scales in part 1).
+  static constexpr int PART_COPIES = COPIES / 2;
+  template <int S, int H>
+  __device__ __forceinline__ static void issue(uint8_t* lds, int s, const Copies& C) {
+    uint8_t* const sta = lds + S * A_STAGE;
+    uint8_t* const stw = lds + W_OFF + S * W_STAGE;
+#pragma unroll
+    for (int i = H * NA / 2; i < (H + 1) * NA / 2; ++i) {
+      const int kb = s * ROW + C.a_kb[i];
+      dma16(C.ra, sta + C.a_lds[i],
+            kb < C.row_bytes ? C.a_base[i] + (uint32_t)s * ROW : kOutOfRange);
+    }
+    const bool in_kt = s < C.KT;
+#pragma unroll
+    for (int i = H * NT / 2; i < (H + 1) * NT / 2; ++i) {
+      const uint32_t off = in_kt ? C.w_base[i] + (uint32_t)s * kTileBytes : kOutOfRange;
+      dma16(C.rw, stw + C.w_lds[i], off);
+      dma16(C.rw, stw + C.w_lds[i] + 1024, off + 1024u);
+    }
+    const bool sa_in = 8 * s + C.sa_kb < C.sc_cols;
+    if constexpr (NS == 1) {
+      if constexpr (H == 0)
+        dma4(C.rsa, lds + SA_OFF + S * SA_STAGE + C.sa_lds[0],
+             sa_in ? C.sa_base[0] + 8u * s : kOutOfRange);
+      else
+        dma4(C.rsw, lds + SB_OFF + S * SB_STAGE + C.sw_lds[0],
+             in_kt ? C.sw_base[0] + 1024u * s : kOutOfRange);
+    } else {
+#pragma unroll
+      for (int i = H * NS / 2; i < (H + 1) * NS / 2; ++i) {
+        dma4(C.rsa, lds + SA_OFF + S * SA_STAGE + C.sa_lds[i],
+             sa_in ? C.sa_base[i] + 8u * s : kOutOfRange);
+        dma4(C.rsw, lds + SB_OFF + S * SB_STAGE + C.sw_lds[i],
+             in_kt ? C.sw_base[i] + 1024u * s : kOutOfRange);
+      }
+    }
+  }
+};
+
+// 32 x 32 accumulators of a 128 x 32 FN wave block -> the LDS C tile.
+template <int NW>
+__device__ __forceinline__ void mx256_stage(const typename Mx256<NW>::Acc& acc, uint8_t* ct,
+                                          int wm, int wn, int lane) {
+  constexpr int FN = Mx256<NW>::FN;
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col = wn * 32 * FN + fn * 32 + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = wm * 128 + fm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        *reinterpret_cast<uint16_t*>(ct + c_tile_offset(row, col)) =
+            round_out<false>(acc[fm][fn][e]);
+      }
+    }
+}
+
+// vmcnt(0) and lgkmcnt(0), then a bare workgroup barrier: this wave's copies
+// have landed and its LDS reads have returned
+#define QG_WAIT_ALL_BARRIER()                          \
+  do {                                                 \
+    __builtin_amdgcn_sched_barrier(0);                 \
+    __builtin_amdgcn_s_waitcnt(0x0070);                \
+    __builtin_amdgcn_s_barrier();                      \
+    __builtin_amdgcn_sched_barrier(0);                 \
+  } while (0)
+
+// Step s, in stage S = s % 2.  Quarters 0-2 compute from registers while
+// the next quarter's fragments arrive; then every wave waits for its copies
+// of step s + 1 and for its reads of stage S, and meets the others.  Quarter 3
+// reads quarter 0 of step s + 1 and, as stage S is now free, issues the first
+// half of the copies of step s + 2 into it; quarter 0 of step s + 1 issues the
+// second half (the same time was measured with all of them in quarter 3).
+// Each copy is pinned beside a matrix instruction.  (In the last two steps
+// these read and copy steps past K: zeros, never used.)
+template <class P, int N>
+__device__ __forceinline__ void pin_copies() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one vector memory read
+  }
+}
+
+template <int NW, int S, class P = Mx256<NW>>
+__device__ __forceinline__ void mx256_step(typename P::Quarter& X0, typename P::Quarter& X1,
+                                           uint32_t (&sc)[4], uint32_t (&sn)[4], uint8_t* lds,
+                                           int s, const typename P::Lane& L,
+                                           typename P::Acc& acc, const typename P::Copies& C) {
+  constexpr int PAIRS = P::PART_COPIES < 4 * P::FN ? P::PART_COPIES : 4 * P::FN;
+  P::template read<S, 1>(X1, lds, L);
+  P::template mma<0>(X0, sc, L, acc);
+  P::template issue<1 - S, 1>(lds, s + 1, C);   // second half of step s + 1
+  pin_copies<P, PAIRS>();
+  __builtin_amdgcn_sched_barrier(0);
+  P::template read<S, 2>(X0, lds, L);
+  P::template mma<1>(X1, sc, L, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  P::template read<S, 3>(X1, lds, L);
+  P::template mma<2>(X0, sc, L, acc);
+  QG_WAIT_ALL_BARRIER();
+  P::template read<1 - S, 0>(X0, lds, L);
+  P::template read_sa<1 - S>(sn, lds, L);
+  P::template mma<3>(X1, sc, L, acc);
+  P::template issue<S, 0>(lds, s + 2, C);       // first half of step s + 2
+  pin_copies<P, PAIRS>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// MXFP4, M and N > 128, K % 128 == 0, at least two 256-element K tiles.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void mx256_kernel(
+    const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_sc,
+    const uint8_t* __restrict__ wp, const uint8_t* __restrict__ w_sc,
+    uint16_t* __restrict__ c, PipeArgs g) {
+  using P = Mx256<NW>;
+  constexpr int LDS_BYTES = P::LDS > kCTileBytes ? P::LDS : kCTileBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / (NW / 2);
+  const int wn = wave % (NW / 2);
+
+  // XCD-aware tile walk, as in pipe256_kernel
+  const int T = g.tiles_m * g.tiles_n;
+  const int bid = blockIdx.x;
+  const int id = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  constexpr int GM = 4;
+  const int group = id / (GM * g.tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(g.tiles_m - first_m, GM);
+  const int in_group = id - group * GM * g.tiles_n;
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
+  const int m0 = tm * kBig;
+  const int cg0 = tn * (kBig / 16);
+
+  PipeRsrc rs;
+  rs.a = make_rsrc(a, g.a_bytes);
+  rs.w = make_rsrc(wp, g.w_bytes);
+  rs.sa = make_rsrc(a_sc, g.asc_bytes);
+  rs.sw = make_rsrc(w_sc, g.wsc_bytes);
+  const typename P::Copies C = P::plan(wave, lane, m0, cg0, g, rs);
+  const typename P::Lane L = P::lane_offsets(wm, wn, lane);
+
+  typename P::Acc acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < P::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int KT = g.KT;
+
+  // step s lives in stage s % 2; its copies go out in quarter 3 of step s - 2
+  P::template issue<0, 0>(smem, 0, C);
+  P::template issue<0, 1>(smem, 0, C);
+  P::template issue<1, 0>(smem, 1, C);   // its other half goes out in step 0
+  QG_WAIT_VM_BARRIER(P::PART_COPIES);    // step 0 landed
+  typename P::Quarter X0, X1;
+  uint32_t sa0[4], sa1[4];
+  P::template read<0, 0>(X0, smem, L);
+  P::template read_sa<0>(sa0, smem, L);
+
+  // an even number of steps: for odd KT the last one is all zeros
+  const int KP = KT + (KT & 1);
+  for (int s = 0; s < KP; s += 2) {
+    mx256_step<NW, 0>(X0, X1, sa0, sa1, smem, s, L, acc, C);
+    mx256_step<NW, 1>(X0, X1, sa1, sa0, smem, s + 1, L, acc, C);
+  }
+  // the copies of steps KP and KP + 1 (all zeros) land before the LDS is
+  // reused for the output tile
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  PipeOut o;
+  o.c = c;
+  o.M = g.M;
+  o.N = g.N;
+  __syncthreads();   // every wave has finished with the last stage
+  mx256_stage<NW>(acc, smem, wm, wn, lane);
+  __syncthreads();
+  pipe_copy_out<64 * NW>(smem, o, m0, cg0 * 16);
+}
+
+// waves per workgroup (four and eight measured the same)
+constexpr int kMx256Waves = 4;
+
+hipError_t launch_mx256(const void* a, const void* a_sc, const void* wp, void* c, int64_t M,
+                        int64_t N, int64_t K, hipStream_t stream) {
+  const PackGeom pg = pack_geom(3, K, N);
+  PipeArgs g;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.KT = (int)pg.kt;
+  g.KS = 2 * (int)pg.kt;
+  g.CG = (int)pg.cg;
+  g.tiles_m = (int)cdiv(M, kBig);
+  g.tiles_n = (int)cdiv(N, kBig);
+  g.a_bytes = (uint32_t)(M * (K / 2));
+  g.w_bytes = (uint32_t)pg.codes;
+  g.asc_bytes = (uint32_t)(M * (K / 32));
+  g.wsc_bytes = (uint32_t)(pg.total - pg.scales);
+  const uint8_t* w_sc = static_cast<const uint8_t*>(wp) + pg.scales;
+  hipLaunchKernelGGL(mx256_kernel<kMx256Waves>, dim3((unsigned)(g.tiles_m * g.tiles_n)),
+                     dim3(64 * kMx256Waves), 0,
+                     stream, static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(a_sc),
+                     static_cast<const uint8_t*>(wp), w_sc, static_cast<uint16_t*>(c), g);
+  return hipGetLastError();
+}
+
 // a_sc: MXFP4 activation scales; col_scale: W4A16/W8A16 column scales;
 // sa, sb: FP8 per-tensor scales (unused arguments may be null).
 template <class Ops, int NST>
@@ -1109,8 +1385,7 @@ hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const vo
   const bool big = M > 128 && N > 128 && cdiv(K, kTileK8) >= 2 && pipe_fits(fmt, M, N, K, 0);
   if (fmt == 3) {
     if (big && K % 128 == 0 && cdiv(K, kTileK4) >= 2)
-      return launch_pipe<Fp4Pipe>(a, a_e8m0, w_packed, scale_a, scale_b, nullptr, c, M, N, K,
-                                  stream);
+      return launch_mx256(a, a_e8m0, w_packed, c, M, N, K, stream);
     return launch_tiles<true, 4, 4>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
   }
   if (fmt == 4) {
