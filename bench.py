@@ -602,8 +602,9 @@ def main():
                     help="first run 4 plain device copies of 256 MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the kernels run on one GPU's share; see DESIGN.md for how they would shard).",
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path; its "
+              "kernels run one GPU's share of a column-parallel (decode) or output-tile "
+              "(square GEMM) split, which needs no exchange between GPUs.",
               file=sys.stderr)
         sys.exit(2)
     import torch
