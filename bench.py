@@ -343,6 +343,45 @@ def time_callable(fn, reps=20):
     return e0.elapsed_time(e1) / 1e3 / reps
 
 
+def read_ceiling(nbytes, reps=60, grids=(256, 512, 1024, 2048)):
+    """The plain streaming-read reference for `nbytes` of weight: the library's
+    read probe over rotating copies totalling >= ROTATE_BYTES (cold cache, as
+    the GEMMs see their weights), timed like the GEMM calls (a graph of
+    `reps` launches between HIP events on the launch stream); the fastest of a
+    few grid sizes."""
+    import torch
+    import bit_quantized_gemm_qgemm_amd as qg
+
+    n = -(-int(nbytes) // 16) * 16
+    r = max(2, math.ceil(ROTATE_BYTES / n))
+    bufs = [torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda") for _ in range(r)]
+    sink = torch.empty(max(grids), dtype=torch.int32, device="cuda")
+    best = None
+    for wgs in grids:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                qg.qgemm_read_probe(bufs[i % r], sink, wgs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / reps
+        if best is None or t < best[0]:
+            best = (t, wgs)
+    del bufs, sink
+    torch.cuda.empty_cache()
+    t, wgs = best
+    return {"bytes": n, "us": round(t * 1e6, 3), "GBps": round(n / t / 1e9, 1),
+            "frac_of_peak": round(n / t / 1e9 / HBM_PEAK_GBS, 4), "workgroups": wgs,
+            "kernel": "read_probe_kernel (qgemm_read_probe)"}
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on the host
 # ---------------------------------------------------------------------------
@@ -354,6 +393,18 @@ def blas_threads():
         return max(n) if n else 1
     except Exception:
         return 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(name, budget_s=10.0):
@@ -474,8 +525,11 @@ def cpu_baseline(name, budget_s=10.0):
         value = 2.0 * rows * n * k * done / dt / 1e12
         sample = (f"oracle {fmt} GEMM of {rows} x {k} by {k} x {n} (dequantize + fp64 matmul), "
                   f"{done} runs in {dt:.1f} s")
+    # cores = the BLAS threads the oracle's matmul ran on; the host's model and
+    # the CPUs this process may use are stated beside it
     return {"value": value, "unit": unit, "cores": blas_threads(), "kind": "oracle",
-            "sample": sample}
+            "sample": sample, "cpu_model": cpu_model(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 # ---------------------------------------------------------------------------
@@ -494,7 +548,7 @@ def traffic_for(kind, kernel):
     return None
 
 
-def run(name, steps, warmup, with_cpu, use_graph):
+def run(name, steps, warmup, with_cpu, use_graph, with_ceiling=True):
     import torch
 
     setup = Setup(name)
@@ -535,6 +589,11 @@ def run(name, steps, warmup, with_cpu, use_graph):
         detail.append(d)
     if setup.explicit is not None:
         detail[0]["explicit_dequant_us"] = round(time_callable(setup.explicit) * 1e6, 3)
+    ceiling = None
+    if decode and with_ceiling:
+        # the same weight byte count read by a plain streaming-read kernel
+        ceiling = read_ceiling(setup.calls[dom][2])
+        roof["frac_of_read_ceiling"] = round(ceiling["us"] / (per_call[dom] * 1e6), 4)
     cfg = {"workload": name, "format": setup.fmt, "M": list(setup.ms), "N": setup.n,
            "K": setup.k, "weight_copies": len(setup.copies),
            "timing": "hip-graph replay" if use_graph else "eager launches"}
@@ -556,11 +615,34 @@ def run(name, steps, warmup, with_cpu, use_graph):
         "detail": detail,
         "device": torch.cuda.get_device_name(0),
     }
+    if ceiling is not None:
+        line["read_ceiling"] = ceiling
     if with_cpu:
         line["cpu_baseline"] = cpu_baseline(name)
     del setup
     torch.cuda.empty_cache()
     return line
+
+
+# The configurations the metric is quoted on besides the default one: the
+# small W4A16 case, W4A16 decode, the 8192^3 MXFP4 and FP8 GEMMs and FP8 at
+# decode M.  The default run times each the same way (graph replay of the
+# timed steps, per-call HIP events) and reports them under "configs".
+OTHER_CONFIGS = ("w4a16_small", "w4a16_decode", "mxfp4_square", "fp8_square", "fp8_decode")
+
+
+def config_summary(line):
+    """The parts of a workload's line that the default line carries per config."""
+    r = line["roofline"]
+    out = {"workload": line["config"]["workload"], "value": line["value"], "unit": line["unit"],
+           "ms_per_step": line["ms_per_step"], "steps": line["steps"], "dtype": line["dtype"],
+           "kernel": r["kernel"], "avg_launch_us": r["avg_launch_us"],
+           "roofline_bound": r["bound"], "roofline_frac": round(r["frac"], 4),
+           "per_call": line["detail"]}
+    if "read_ceiling" in line:
+        out["read_ceiling"] = line["read_ceiling"]
+        out["frac_of_read_ceiling"] = r["frac_of_read_ceiling"]
+    return out
 
 
 def kernel_name(setup, m):
@@ -598,6 +680,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of a graph")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default workload only: skip the other configurations' summaries")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run 4 plain device copies of 256 MiB (counter calibration)")
     args = ap.parse_args()
@@ -620,13 +704,28 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log(f"bench: ran 4 copies of {CALIB_BYTES} bytes for counter calibration")
-    names = sorted(WORKLOADS) if args.all else [args.workload]
-    for name in names:
+    def steps_for(name):
         square = WORKLOADS[name][1][0] > 16
         steps = args.steps if args.steps is not None else (20 if square else 200)
         warmup = args.warmup if args.warmup is not None else (3 if square else 20)
+        return steps, warmup
+
+    names = sorted(WORKLOADS) if args.all else [args.workload]
+    for name in names:
+        steps, warmup = steps_for(name)
         log(f"bench: {name} steps={steps} warmup={warmup}")
         line = run(name, steps, warmup, with_cpu=not args.no_cpu, use_graph=not args.eager)
+        if name == DEFAULT_WORKLOAD and not args.all and not args.no_configs:
+            configs = []
+            for other in OTHER_CONFIGS:
+                o_steps, o_warmup = steps_for(other)
+                # at least as many steps as the default line, at most 20 for the
+                # square GEMMs (each step is a 0.3-0.5 ms call)
+                o_steps = min(o_steps, 20) if WORKLOADS[other][1][0] > 16 else o_steps
+                log(f"bench: {other} steps={o_steps} warmup={o_warmup} (config summary)")
+                o = run(other, o_steps, o_warmup, with_cpu=False, use_graph=not args.eager)
+                configs.append(config_summary(o))
+            line["configs"] = configs
         print(json.dumps(line), flush=True)
 
 

@@ -49,6 +49,7 @@ _SIGNATURES = [
     ("qgemm_act_workspace_bytes", ctypes.c_int64, [ctypes.c_int, _I64, _I64]),
     ("qgemm_mxfp4_act", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     ("qgemm_fp8_act", ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    ("qgemm_read_probe", ctypes.c_int, [_P, _I64, _P, _I64, _P]),
 ]
 
 _lib = None
@@ -104,6 +105,18 @@ def _need(t, dtype, ndim, name):
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous (row-major, no padding)")
+
+
+def _out(out, M, N, dtype, device):
+    """The caller's output tensor, checked to be a contiguous [M, N] device
+    tensor of `dtype` (the library writes M * N elements through its pointer),
+    or a new one."""
+    if out is None:
+        return torch.empty((M, N), dtype=dtype, device=device)
+    _need(out, dtype, 2, "out")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M}, {N}], got {list(out.shape)}")
+    return out
 
 
 def qgemm_prepack_bytes(fmt, K, N):
@@ -185,12 +198,7 @@ def _weight_only(name, x, w_packed, scales, N, out):
     fmt = QGEMM_W4A16 if name == "qgemm_w4a16" else QGEMM_W8A16
     if w_packed.numel() < qgemm_prepack_bytes(fmt, K, N):
         raise ValueError("w_packed is smaller than the packed size for this K, N")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    else:
-        _need(out, torch.float16, 2, "out")
-        if tuple(out.shape) != (M, N):
-            raise ValueError("out must be [M, N]")
+    out = _out(out, M, N, torch.float16, x.device)
     fn = getattr(lib(), name)
     _check(fn(_ptr(x), _ptr(w_packed), _ptr(scales), _ptr(out), M, N, K, _stream(x)), name)
     return out
@@ -217,10 +225,7 @@ def qgemm_mxfp4(a_codes, a_e8m0, w_packed, N, out=None):
         raise ValueError("a_e8m0 must be [M, K/32]")
     if w_packed.numel() < qgemm_prepack_bytes(QGEMM_MXFP4, K, N):
         raise ValueError("w_packed is smaller than the packed size for this K, N")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
-    else:
-        _need(out, torch.bfloat16, 2, "out")
+    out = _out(out, M, N, torch.bfloat16, a_codes.device)
     _check(lib().qgemm_mxfp4(_ptr(a_codes), _ptr(a_e8m0), _ptr(w_packed), _ptr(out), M, N, K,
                              _stream(a_codes)), "qgemm_mxfp4")
     return out
@@ -238,10 +243,7 @@ def qgemm_fp8(a, b_packed, scale_a, scale_b, N, out=None):
     M, K = a.shape
     if b_packed.numel() < qgemm_prepack_bytes(QGEMM_FP8, K, N):
         raise ValueError("b_packed is smaller than the packed size for this K, N")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    else:
-        _need(out, torch.bfloat16, 2, "out")
+    out = _out(out, M, N, torch.bfloat16, a.device)
     _check(lib().qgemm_fp8(_ptr(a), _ptr(b_packed), _ptr(scale_a), _ptr(scale_b), _ptr(out), M,
                            N, K, _stream(a)), "qgemm_fp8")
     return out
@@ -293,12 +295,7 @@ def _grouped(name, fmt, x, w_packed, N, group_k, out):
     M, K = x.shape
     if w_packed.numel() < qgemm_prepack_grouped_bytes(fmt, K, N, group_k):
         raise ValueError("w_packed is smaller than the packed size for this K, N, group_k")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    else:
-        _need(out, torch.float16, 2, "out")
-        if tuple(out.shape) != (M, N):
-            raise ValueError("out must be [M, N]")
+    out = _out(out, M, N, torch.float16, x.device)
     _check(getattr(lib(), name)(_ptr(x), _ptr(w_packed), _ptr(out), M, N, K, int(group_k),
                                 _stream(x)), name)
     return out
@@ -324,12 +321,7 @@ def qgemm_nvfp4(x, w_packed, global_scale, N, out=None):
     M, K = x.shape
     if w_packed.numel() < qgemm_prepack_bytes(QGEMM_NVFP4, K, N):
         raise ValueError("w_packed is smaller than the packed size for this K, N")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    else:
-        _need(out, torch.float16, 2, "out")
-        if tuple(out.shape) != (M, N):
-            raise ValueError("out must be [M, N]")
+    out = _out(out, M, N, torch.float16, x.device)
     _check(lib().qgemm_nvfp4(_ptr(x), _ptr(w_packed), _ptr(global_scale), _ptr(out), M, N, K,
                              _stream(x)), "qgemm_nvfp4")
     return out
@@ -363,10 +355,7 @@ def qgemm_mxfp4_act(a, w_packed, N, workspace=None, out=None):
     if w_packed.numel() < qgemm_prepack_bytes(QGEMM_MXFP4, K, N):
         raise ValueError("w_packed is smaller than the packed size for this K, N")
     workspace = _act_workspace(QGEMM_MXFP4, a, workspace)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    else:
-        _need(out, torch.bfloat16, 2, "out")
+    out = _out(out, M, N, torch.bfloat16, a.device)
     _check(lib().qgemm_mxfp4_act(_ptr(a), _ptr(w_packed), _ptr(out), _ptr(workspace), M, N, K,
                                  _stream(a)), "qgemm_mxfp4_act")
     return out, workspace
@@ -384,10 +373,19 @@ def qgemm_fp8_act(a, b_packed, scale_b, N, workspace=None, out=None):
     if b_packed.numel() < qgemm_prepack_bytes(QGEMM_FP8, K, N):
         raise ValueError("b_packed is smaller than the packed size for this K, N")
     workspace = _act_workspace(QGEMM_FP8, a, workspace)
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    else:
-        _need(out, torch.bfloat16, 2, "out")
+    out = _out(out, M, N, torch.bfloat16, a.device)
     _check(lib().qgemm_fp8_act(_ptr(a), _ptr(b_packed), _ptr(scale_b), _ptr(out), _ptr(workspace),
                                M, N, K, _stream(a)), "qgemm_fp8_act")
     return out, workspace
+
+
+def qgemm_read_probe(buf, sink, workgroups):
+    """Read all of the uint8 device tensor `buf` once (the plain-read
+    reference of the weight stream); sink is an int32 device tensor with at
+    least `workgroups` entries."""
+    _need(buf, torch.uint8, 1, "buf")
+    _need(sink, torch.int32, 1, "sink")
+    if sink.numel() < workgroups:
+        raise ValueError("sink needs one entry per workgroup")
+    _check(lib().qgemm_read_probe(_ptr(buf), buf.numel(), _ptr(sink), int(workgroups),
+                                  _stream(buf)), "qgemm_read_probe")

@@ -20,7 +20,8 @@ LIB_NAME = "libqgemm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["decode_gemm.hip", "tile_gemm.hip", "quantize.hip", "prepack.hip", "api.cpp"]
+SOURCES = ["decode_gemm.hip", "tile_gemm.hip", "quantize.hip", "prepack.hip", "read_probe.hip",
+           "api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

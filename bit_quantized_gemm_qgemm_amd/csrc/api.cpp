@@ -3,6 +3,7 @@
 // call returns its status without touching the HIP runtime.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -62,8 +63,13 @@ int check_sizes(int fmt, int64_t M, int64_t N, int64_t K) {
   return QGEMM_OK;
 }
 
-// Device architecture check, cached per device ordinal.
+// Device architecture check, cached per device ordinal.  The environment
+// variable QGEMM_ARCH_OVERRIDE, when set, stands in for the current device's
+// architecture name and no device is queried (host-side tests of the
+// ERR_ARCH path on machines without the GPU).
 int check_device() {
+  if (const char* forced = std::getenv("QGEMM_ARCH_OVERRIDE"))
+    return std::strncmp(forced, "gfx950", 6) == 0 ? QGEMM_OK : QGEMM_ERR_ARCH;
   static std::mutex mu;
   static int cached[64];
   static bool init = false;
@@ -135,6 +141,39 @@ int grouped_gemm(int fmt, const void* x, const void* w_packed, void* y, int64_t 
                                                            as_stream(stream)));
   return launched(qgemm::launch_decode_grouped(fmt, x, w_packed, y, M, N, K, group_k,
                                                as_stream(stream)));
+}
+
+// ---- FP8 GEMM with fp32 A quantized on the device --------------------------
+
+// Checks of qgemm_fp8_act other than the workspace.
+int check_fp8_act(const float* a, const void* b_packed, const float* scale_b, void* c,
+                  int64_t M, int64_t N, int64_t K) {
+  int st = check_sizes(QGEMM_FP8, M, N, K);
+  if (st != QGEMM_OK) return st;
+  if (!present(a, M * K) || !present(b_packed, K * N) || !present(c, M * N) || !scale_b)
+    return QGEMM_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b_packed, 16) || !aligned(c, 16) || !aligned(scale_b, 4))
+    return QGEMM_ERR_ALIGN;
+  return QGEMM_OK;
+}
+
+// Quantize A into ws (codes [M*K], the fp32 scale at round_up(M*K, 16), the
+// partial maxima 16 bytes after it), then the GEMM; everything on `stream`.
+int fp8_act_run(const float* a, const void* b_packed, const float* scale_b, void* c, uint8_t* ws,
+                int64_t M, int64_t N, int64_t K, void* stream) {
+  uint8_t* codes = ws;
+  float* scale_a = reinterpret_cast<float*>(codes + qgemm::cdiv(M * K, 16) * 16);
+  float* partials = scale_a + 4;
+  // an empty A still gets its scale (1.0, the all-zero rule); K % 16 == 0,
+  // so A is whole 16-byte pieces
+  int st = launched(
+      qgemm::launch_quantize_fp8_ws(a, M * K, codes, scale_a, partials, as_stream(stream)));
+  if (st != QGEMM_OK || N == 0) return st;
+  if (M <= kDecodeMaxM)
+    return launched(qgemm::launch_decode_gemm(QGEMM_FP8, codes, b_packed, nullptr, scale_a,
+                                              scale_b, c, M, N, K, as_stream(stream)));
+  return launched(qgemm::launch_tile_gemm(QGEMM_FP8, codes, nullptr, b_packed, scale_a, scale_b,
+                                          c, M, N, K, as_stream(stream)));
 }
 
 }  // namespace
@@ -336,29 +375,24 @@ int qgemm_mxfp4_act(const float* a, const void* w_packed, void* c, void* workspa
 
 int qgemm_fp8_act(const float* a, const void* b_packed, const float* scale_b, void* c,
                   void* workspace, int64_t M, int64_t N, int64_t K, void* stream) {
-  int st = check_sizes(QGEMM_FP8, M, N, K);
+  int st = check_fp8_act(a, b_packed, scale_b, c, M, N, K);
   if (st != QGEMM_OK) return st;
-  if (!present(a, M * K) || !present(b_packed, K * N) || !present(c, M * N) || !scale_b ||
-      !workspace)
-    return QGEMM_ERR_NULL;
-  if (!aligned(a, 16) || !aligned(b_packed, 16) || !aligned(c, 16) || !aligned(workspace, 16) ||
-      !aligned(scale_b, 4))
-    return QGEMM_ERR_ALIGN;
+  if (!workspace) return QGEMM_ERR_NULL;
+  if (!aligned(workspace, 16)) return QGEMM_ERR_ALIGN;
   if (M == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
-  uint8_t* codes = static_cast<uint8_t*>(workspace);
-  float* scale_a = reinterpret_cast<float*>(codes + qgemm::cdiv(M * K, 16) * 16);
-  float* partials = scale_a + 4;
-  // an empty A still gets its scale (1.0, the all-zero rule); K % 16 == 0,
-  // so A is whole 16-byte pieces
-  st = launched(
-      qgemm::launch_quantize_fp8_ws(a, M * K, codes, scale_a, partials, as_stream(stream)));
-  if (st != QGEMM_OK || N == 0) return st;
-  if (M <= kDecodeMaxM)
-    return launched(qgemm::launch_decode_gemm(QGEMM_FP8, codes, b_packed, nullptr, scale_a,
-                                              scale_b, c, M, N, K, as_stream(stream)));
-  return launched(qgemm::launch_tile_gemm(QGEMM_FP8, codes, nullptr, b_packed, scale_a, scale_b,
-                                          c, M, N, K, as_stream(stream)));
+  return fp8_act_run(a, b_packed, scale_b, c, static_cast<uint8_t*>(workspace), M, N, K, stream);
+}
+
+int qgemm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int64_t workgroups,
+                     void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || workgroups < 1 || workgroups > (1 << 20))
+    return QGEMM_ERR_SHAPE;
+  if (!present(buf, bytes) || !sink) return QGEMM_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return QGEMM_ERR_ALIGN;
+  int st = check_device();
+  if (st != QGEMM_OK) return st;
+  return launched(qgemm::launch_read_probe(buf, bytes, sink, workgroups, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -192,6 +192,11 @@ hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const vo
                             const float* scale_a, const float* scale_b, void* c,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// Streaming read of `bytes` bytes (a multiple of 16, buf 16-byte aligned) by
+// `workgroups` workgroups; one word per workgroup goes to sink.
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int64_t workgroups,
+                             hipStream_t stream);
+
 // ---- device helpers --------------------------------------------------------
 
 // fp32 -> bf16 bits, round to nearest even (inputs are finite here; a NaN

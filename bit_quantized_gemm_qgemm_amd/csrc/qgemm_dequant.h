@@ -7,6 +7,14 @@
 // the int8 weight).  Two nibbles (or bytes) become two fp16 lanes of one
 // register per operation; the per-column scale is applied later to the fp32
 // sum, where it is exact to factor it out.
+//
+// This exponent-bias conversion is the published technique of Kim et al.,
+// "Who Says Elephants Can't Run: Bringing Large Scale MoE Models into Cloud
+// Scale Production" (2022), with the INT4 nibble interleave of NVIDIA's
+// FasterTransformer: the fp16 format fixes its constants (0x6400 = 1024,
+// 1024 + 8 = 1032 to remove the bias and the zero point, 1/16 and -72 for the
+// nibble that sits four bits higher), so any implementation of the method
+// uses the same ones.
 #pragma once
 
 #include "qgemm_common.h"

@@ -72,7 +72,10 @@ enum qgemm_status {
                              needs, or a size too large for 32-bit indexing */
   QGEMM_ERR_ALIGN = -3,   /* a pointer is not 16-byte (scales: 4-byte)
                              aligned                                         */
-  QGEMM_ERR_ARCH = -4,    /* the current device is not gfx950               */
+  QGEMM_ERR_ARCH = -4,    /* the current device is not gfx950 (if the
+                             environment variable QGEMM_ARCH_OVERRIDE is
+                             set, its value is taken as the device's
+                             architecture name and no device is queried)  */
   QGEMM_ERR_LAUNCH = -5,  /* the HIP runtime reported a launch error        */
   QGEMM_ERR_FORMAT = -6,  /* unknown format id                               */
   QGEMM_ERR_DEVICE = -7   /* no HIP device could be queried                  */
@@ -266,6 +269,20 @@ int qgemm_w4a16_grouped(const void* x, const void* w_packed, void* y, int64_t M,
                         int64_t K, int64_t group_k, void* stream);
 int qgemm_w8a16_grouped(const void* x, const void* w_packed, void* y, int64_t M, int64_t N,
                         int64_t K, int64_t group_k, void* stream);
+
+/*
+ * qgemm_read_probe -- measurement reference, not part of any GEMM: reads the
+ * `bytes` bytes of buf once with the weight stream's access pattern (16-byte
+ * non-temporal loads per lane, eight in flight per lane, one contiguous chunk
+ * of whole 1 KB pieces per workgroup, `workgroups` workgroups of 256 threads)
+ * and writes one 32-bit fold of its chunk per workgroup to sink[workgroups].
+ * Timed around a launch it gives the plain HBM read rate for that byte
+ * count, against which the decode GEMMs' weight streaming is compared (W8A16
+ * page, performance analysis: weight read bandwidth).  bytes % 16 == 0; buf
+ * 16-byte aligned; 1 <= workgroups <= 2^20.
+ */
+int qgemm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int64_t workgroups,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -202,3 +202,25 @@ def test_binding_refuses_to_run_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(qg, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         qg.lib()
+
+
+def test_arch_check_rejects_other_architectures(lib, monkeypatch):
+    """QGEMM_ERR_ARCH: a valid call on a device that is not gfx950 returns the
+    status before anything is launched (the architecture name is injected)."""
+    s = P(0)
+    monkeypatch.setenv("QGEMM_ARCH_OVERRIDE", "gfx942")
+    assert lib.qgemm_w8a16(GOOD, GOOD, GOOD, GOOD, 4, 16, 32, s) == ERR_ARCH
+    assert lib.qgemm_w4a16(GOOD, GOOD, GOOD, GOOD, 4, 16, 32, s) == ERR_ARCH
+    assert lib.qgemm_mxfp4(GOOD, GOOD, GOOD, GOOD, 4, 16, 64, s) == ERR_ARCH
+    assert lib.qgemm_fp8(GOOD, GOOD, GOOD, GOOD, GOOD, 4, 16, 64, s) == ERR_ARCH
+    assert lib.qgemm_nvfp4(GOOD, GOOD, GOOD, GOOD, 4, 16, 64, s) == ERR_ARCH
+    assert lib.qgemm_w8a16_grouped(GOOD, GOOD, GOOD, 4, 16, 128, 128, s) == ERR_ARCH
+    assert lib.qgemm_prepack(2, GOOD, None, GOOD, 32, 32, s) == ERR_ARCH
+    assert lib.qgemm_quantize_mxfp4(GOOD, 4, 32, GOOD, GOOD, s) == ERR_ARCH
+    assert lib.qgemm_quantize_fp8(GOOD, 16, GOOD, GOOD, s) == ERR_ARCH
+    assert lib.qgemm_fp8_act(GOOD, GOOD, GOOD, GOOD, GOOD, 4, 16, 64, s) == ERR_ARCH
+    # argument errors still come first, and empty calls stay no-ops
+    assert lib.qgemm_w8a16(None, GOOD, GOOD, GOOD, 4, 16, 32, s) == ERR_NULL
+    assert lib.qgemm_w8a16(GOOD, GOOD, GOOD, GOOD, 0, 16, 32, s) == OK
+    monkeypatch.setenv("QGEMM_ARCH_OVERRIDE", "gfx90a")
+    assert lib.qgemm_w8a16(GOOD, GOOD, GOOD, GOOD, 4, 16, 32, s) == ERR_ARCH

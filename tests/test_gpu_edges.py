@@ -109,3 +109,65 @@ def test_quantizers_empty():
     assert codes.numel() == 0 and scale.item() == 1.0
     c, e = qg.qgemm_quantize_mxfp4(z((0, 64), torch.float32))
     assert c.shape == (0, 32) and e.shape == (0, 2)
+
+
+# --------------------------------------------------------------------------
+# packed weights of 2^31 bytes or more: past the 32-bit buffer offsets of the
+# 256 x 256 kernels, so these calls take the 128 x 128 kernel, which
+# addresses with 64 bits; columns whose packed bytes sit on both sides of the
+# 2^31-byte mark are checked against the oracle
+# --------------------------------------------------------------------------
+
+def random_bytes(shape, seed, lo=0, hi=256):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return torch.randint(lo, hi, shape, generator=g, device="cuda", dtype=torch.int32).to(
+        torch.uint8)
+
+
+def test_fp8_packed_weight_over_2gib():
+    import oracle
+    m, k = 256, 65536
+    n = 32768 + 64           # packed B: 2^31 + 4 MiB (column group 2048 starts at 2^31)
+    case_id("fp8 packed B over 2 GiB", m, n, k)
+    assert qg.qgemm_prepack_bytes(4, k, n) > 1 << 31
+    a = random_bytes((m, k), 21)
+    b = random_bytes((k, n), 22)
+    a[(a & 0x7f) == 0x7f] = 0x38          # no NaN codes
+    b[(b & 0x7f) == 0x7f] = 0x30
+    sa = torch.tensor([0.01], dtype=torch.float32, device="cuda")
+    sb = torch.tensor([0.02], dtype=torch.float32, device="cuda")
+    bp = qg.qgemm_prepack("fp8", b, k, n)
+    c = qg.qgemm_fp8(a, bp, sa, sb, n)
+    cols = np.array([0, 1, 32767, 32768, 32769, 32800, n - 1])
+    cols_d = torch.from_numpy(cols).cuda()
+    got = c[:, cols_d].float().cpu().numpy().astype(np.float64)
+    qa = a.cpu().numpy()
+    qb = b[:, cols_d].cpu().numpy()
+    del c, bp, b
+    torch.cuda.empty_cache()
+    c_ref, bound = oracle.gemm_fp8(qa, qb, np.float32(0.01), np.float32(0.02))
+    assert np.all(oracle.within_tolerance(got, c_ref, bound))
+
+
+def test_mxfp4_packed_weight_over_2gib():
+    import oracle
+    m, k = 256, 65536
+    n = 61696                # codes 1928 MiB, then a scale segment reaching past 2^31
+    case_id("mxfp4 packed W over 2 GiB", m, n, k)
+    assert qg.qgemm_prepack_bytes(3, k, n) > 1 << 31
+    ac = random_bytes((m, k // 2), 31)
+    ae = random_bytes((m, k // 32), 32, 120, 135)
+    wc = random_bytes((n, k // 2), 33)
+    we = random_bytes((n, k // 32), 34, 120, 135)
+    wp = qg.qgemm_prepack("mxfp4", wc, k, n, w_scales=we)
+    c = qg.qgemm_mxfp4(ac, ae, wp, n)
+    # column groups from 3840 (column 61440) on keep their scales past 2^31
+    cols = np.array([0, 1, 30000, 61439, 61440, 61441, n - 1])
+    cols_d = torch.from_numpy(cols).cuda()
+    got = c[:, cols_d].float().cpu().numpy().astype(np.float64)
+    w_c, w_e = wc[cols_d].cpu().numpy(), we[cols_d].cpu().numpy()
+    a_c, a_e = ac.cpu().numpy(), ae.cpu().numpy()
+    del c, wp, wc, we
+    torch.cuda.empty_cache()
+    c_ref, bound = oracle.gemm_mxfp4(a_c, a_e, w_c, w_e)
+    assert np.all(oracle.within_tolerance(got, c_ref, bound))

@@ -347,6 +347,10 @@ MX_CASES = [
     (100, 520, 800),    # small-M kernel: four slabs, two workgroup rows, K = 3.125 tiles
     (33, 136, 288),     # four slabs, one row of them ragged; K = 1.125 tiles
     (128, 2100, 256),   # the largest M the small-M kernel takes
+    (1024, 2048, 512),  # 4 x 8 tiles of 256 x 256: the tile count is a multiple of 8,
+                        # so the XCD-remapped walk and its 4-row groups run
+    (1280, 1792, 768),  # 5 x 7 = 35 tiles (plain walk), ragged group of tile rows
+    (2048, 1024, 1024), # 8 x 4 tiles: remapped walk, two 4-row groups
 ]
 
 
@@ -445,7 +449,19 @@ def test_mxfp4_small_m_full_size_sampled(m):
     assert_within(c[:, cols], c_ref, bound, f"mxfp4 small-M full M={m}")
 
 
-def test_mxfp4_full_size_sampled():
+def tile_row_sample(m, seed, tile=256):
+    """One row inside each tile row of a tile x tile output grid, at a random
+    offset, plus the first and the last row."""
+    rng = np.random.default_rng(seed)
+    starts = np.arange(0, m, tile)
+    rows = starts + rng.integers(0, tile, size=len(starts))
+    return np.unique(np.concatenate([rows[rows < m], [0, m - 1]]))
+
+
+def test_mxfp4_full_size_full_rows():
+    """8192^3 through the 256 x 256 kernel and its XCD-remapped tile walk:
+    whole output rows, one in each of the 32 tile rows, so every output tile
+    is checked element by element (34 rows x 8192 columns)."""
     m = n = k = 8192
     case_id("mxfp4 full", m, n, k)
     a, w = wl.mxfp4_operands(m, n, k)
@@ -453,18 +469,19 @@ def test_mxfp4_full_size_sampled():
     wc_d, we_d = qg.qgemm_quantize_mxfp4(dev(w))
     wp = qg.qgemm_prepack("mxfp4", wc_d, k, n, w_scales=we_d)
     c = qg.qgemm_mxfp4(ac_d, ae_d, wp, n)
-    rows, cols = wl.sample_indices(m, n, 256)
-    ur, uc = np.unique(rows), np.unique(cols)
-    ac, ae = oracle.mxfp4_quantize(a[ur])
-    wc, we = oracle.mxfp4_quantize(w[uc])
-    # device quantizer bytes equal the oracle's on the sampled rows
-    assert np.array_equal(ac_d[torch.from_numpy(ur)].cpu().numpy(), ac)
-    assert np.array_equal(we_d[torch.from_numpy(uc)].cpu().numpy(), we)
+    rows = tile_row_sample(m, 1)
+    got = host(c[torch.from_numpy(rows).cuda()])
+    del c, wp
+    ac, ae = oracle.mxfp4_quantize(a[rows])
+    wc = np.empty((n, k // 2), np.uint8)
+    we = np.empty((n, k // 32), np.uint8)
+    for r0 in range(0, n, 1024):                 # the oracle quantizes W in row chunks
+        wc[r0:r0 + 1024], we[r0:r0 + 1024] = oracle.mxfp4_quantize(w[r0:r0 + 1024])
+    # the device quantizer's bytes equal the oracle's on these A rows and all of W
+    assert np.array_equal(ac_d[torch.from_numpy(rows).cuda()].cpu().numpy(), ac)
+    assert np.array_equal(wc_d.cpu().numpy(), wc) and np.array_equal(we_d.cpu().numpy(), we)
     c_ref, bound = oracle.gemm_mxfp4(ac, ae, wc, we)
-    ri = np.searchsorted(ur, rows)
-    ci = np.searchsorted(uc, cols)
-    got = host(c[torch.from_numpy(rows), torch.from_numpy(cols)])
-    assert np.all(oracle.within_tolerance(got, c_ref[ri, ci], bound[ri, ci]))
+    assert_within(got, c_ref, bound, "mxfp4 8192^3 full rows")
 
 
 # --------------------------------------------------------------------------
@@ -503,6 +520,9 @@ FP8_CASES = [
     (64, 1024, 2048),   # four slabs
     (100, 512, 384),    # four slabs, two workgroup rows, ragged
     (128, 2048, 256),   # the largest M the small-M kernel takes
+    (1024, 2048, 512),  # 4 x 8 tiles of 256 x 256: the XCD-remapped walk
+    (2048, 1024, 1024), # 8 x 4 tiles: remapped walk, two 4-row groups
+    (1200, 1800, 528),  # 5 x 8 = 40 tiles, remapped, ragged last tile row and column
 ]
 
 
@@ -556,7 +576,7 @@ def test_fp8_one_hot_through_large_tiles():
     assert np.array_equal(c, oracle.round_bf16(bdeq[ks]))
 
 
-@pytest.mark.parametrize("m", [16, 64, 8192])
+@pytest.mark.parametrize("m", [16, 64])
 def test_fp8_full_size_sampled(m):
     n = k = 8192
     case_id("fp8 full", m, n, k)
@@ -576,6 +596,27 @@ def test_fp8_full_size_sampled(m):
     ci = np.searchsorted(uc, cols)
     got = host(c[torch.from_numpy(rows), torch.from_numpy(cols)])
     assert np.all(oracle.within_tolerance(got, c_ref[ri, ci], bound[ri, ci]))
+
+
+def test_fp8_full_size_full_rows():
+    """8192^3 through the 256 x 256 kernel and its XCD-remapped tile walk:
+    whole output rows, one in each of the 32 tile rows (34 rows x 8192)."""
+    m = n = k = 8192
+    case_id("fp8 full rows", m, n, k)
+    a, b = wl.fp8_operands(m, n, k)
+    qa_d, sa_d = qg.qgemm_quantize_fp8(dev(a))
+    qb_d, sb_d = qg.qgemm_quantize_fp8(dev(b))
+    bp = qg.qgemm_prepack("fp8", qb_d, k, n)
+    c = qg.qgemm_fp8(qa_d, bp, sa_d, sb_d, n)
+    rows = tile_row_sample(m, 2)
+    got = host(c[torch.from_numpy(rows).cuda()])
+    del c, bp
+    qa, sa = oracle.fp8_quantize(a)
+    qb, sb = oracle.fp8_quantize(b)
+    assert sa_d.item() == sa and sb_d.item() == sb
+    assert np.array_equal(qb_d.cpu().numpy(), qb)
+    c_ref, bound = oracle.gemm_fp8(qa[rows], qb, sa, sb)
+    assert_within(got, c_ref, bound, "fp8 8192^3 full rows")
 
 
 def test_weight_only_activations_over_2gib():

@@ -351,25 +351,34 @@ def test_mxfp4_negative_zero_and_small_negatives():
     assert nibbles_by_string(codes_p[0, 1])[0] == 8
 
 
-def test_mxfp4_matches_page_torch_simulator_steps():
-    """The page's quantized element values (fp32 torch steps) equal the
-    dequantized oracle codes, block by block."""
+def test_mxfp4_values_are_nearest_points_of_the_block_grid():
+    """MXFP4 page, section 3, in words: a 32-element block shares one power of
+    two, the smallest one whose grid {0, .5, 1, 1.5, 2, 3, 4, 6} times it
+    reaches the block's largest magnitude, and each element becomes the point
+    of the signed, scaled grid nearest to it (an exact tie going to the
+    smaller magnitude, as the page's first-minimum search does).  Checked on
+    the dequantized values in exact arithmetic, on the page's own demo input
+    kind (seed 42, N(0, 0.5^2)), plus a tiny block and an all-zero block."""
     g = torch.Generator().manual_seed(42)
-    x = (torch.randn(8, 256, generator=g) * 0.5)
-    x[3, :32] *= 1e-3
+    x = (torch.randn(8, 256, generator=g) * 0.5).numpy()
+    x[3, :32] *= np.float32(1e-3)
     x[5, 64:96] = 0
-    blocks = x.view(8, 8, 32)
-    amax = blocks.abs().max(dim=-1).values.clamp(min=1e-8)
-    exp_int = torch.ceil(torch.log2(amax / 6.0)).int()
-    normalized = blocks / torch.pow(2.0, exp_int.float()).unsqueeze(-1)
-    lut = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
-    idx = torch.argmin((normalized.abs().unsqueeze(-1) - lut.view(1, 1, 1, 8)).abs(), dim=-1)
-    page_vals = (torch.sign(normalized) * lut[idx]).double()
-    page_deq = (page_vals * torch.pow(2.0, exp_int.double()).unsqueeze(-1)).reshape(8, 256)
-
-    codes, e8 = oracle.mxfp4_quantize(x.numpy())
-    assert np.array_equal((e8.astype(np.int64) - 127), exp_int.numpy())
-    assert np.array_equal(oracle.mxfp4_dequant(codes, e8), page_deq.numpy())
+    codes, e8 = oracle.mxfp4_quantize(x)
+    deq = oracle.mxfp4_dequant(codes, e8)
+    mags = [Fraction(int(2 * m), 2) for m in (0, .5, 1, 1.5, 2, 3, 4, 6)]
+    for r in range(8):
+        for b in range(8):
+            blk = [Fraction(float(v)) for v in x[r, 32 * b:32 * b + 32]]
+            amax = max(max(abs(v) for v in blk), Fraction(float(np.float32(1e-8))))
+            e = -200
+            while 6 * pow2(e) < amax:      # smallest power of two that fits
+                e += 1
+            assert int(e8[r, b]) - 127 == e
+            for i, v in enumerate(blk):
+                points = sorted({m * pow2(e) for m in mags})
+                best = min(points, key=lambda p: (abs(abs(v) - p), p))
+                want = -best if v < 0 else best
+                assert Fraction(float(deq[r, 32 * b + i])) == want, (r, b, i)
 
 
 def test_mxfp4_dequant_by_fields():
