@@ -652,7 +652,7 @@ def kernel_name(setup, m):
         return (f"qgemm_fp8_act call: quantize kernels + decode_gemm_kernel[fp8, M={m}, "
                 f"N={setup.n}, K={setup.k}]")
     if setup.fmt == "mxfp4_act":
-        return (f"qgemm_mxfp4_act call: quantize_mxfp4_kernel + mx256_kernel[mxfp4, M={m}, "
+        return (f"qgemm_mxfp4_act call: quantize_mxfp4_kernel + mxw_kernel[mxfp4, M={m}, "
                 f"N={setup.n}, K={setup.k}]")
     if setup.kind == "decode":
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
@@ -666,7 +666,7 @@ def kernel_name(setup, m):
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     k_tiles = -(-setup.k // (256 if setup.fmt == "mxfp4" else 128))
     big = m > 128 and setup.n > 128 and k_tiles >= 2 and (setup.fmt != "mxfp4" or setup.k % 128 == 0)
-    name = ("mx256_kernel" if setup.fmt == "mxfp4" else "pipe256_kernel") if big \
+    name = ("mxw_kernel" if setup.fmt == "mxfp4" else "pipe256_kernel") if big \
         else "tile_gemm_kernel"
     return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
 

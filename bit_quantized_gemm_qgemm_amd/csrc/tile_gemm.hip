@@ -867,311 +867,228 @@ __global__ __launch_bounds__(kThreads) void pipe256_kernel(
   pipe_copy_out(smem, o, m0, cg0 * 16);
 }
 
-// ---- MXFP4, 256 x 256 tiles, 256-element K steps ------------------------
-// 256 x 256 output tile per workgroup, NW waves (4: one per SIMD, each owning
-// a 128 x 128 block of C, 4 x 4 fragments of 32 x 32; 8: two per SIMD, 128 x
-// 64 each).  A K step is one packed W tile: 256 elements, 128 bytes of an A
-// row, so every A copy reads whole 128-byte lines (8 rows x 128 B per
-// instruction).  The earlier 64-byte step read halves of 16 lines per
-// instruction, which the vector memory path serves several times slower; at
-// M = N = K = 8192 the move took the GEMM from 296 to 274 us.  Four and eight
-// waves measured the same (274 / 277 us), and so did issuing all of a step's
-// copies in one quarter or spreading them over two; with no copies in the loop
-// at all the kernel takes 205 us, so the copies and the compute side (matrix
-// instructions, LDS fragment reads, the per-step barrier) each hold part of
-// the time.
+// ---- MXFP4, 256 x 256 tiles, W fragments straight to registers -----------
+// Each of the 4 waves owns all 256 rows and 64 columns (4 column tiles) of
+// the workgroup's output tile: 8 x 2 fragments of 32 x 32.  No other wave
+// reads a wave's W columns, so its W fragments go from global memory straight
+// into registers (the packed tiles are already in lane order; one 16-byte
+// load per lane and fragment feeds one matrix instruction), and only A and
+// its E8M0 bytes pass through LDS, 34 KB per 256-element K step.  That fits a
+// ring of four LDS stages, so the copies of step s + 3 go out spread evenly
+// over all four quarters of step s instead of in bursts.
 //
-// LDS, two stages s = 0, 1 of each part (the A and W parts of both stages
-// sit below 64 KB and 128 KB so that one address register per quarter and a
-// constant offset reach every fragment):
-//   A  [s][256 rows][128 B] at 32 KB s, 16-byte chunk c of row r at slot
-//      c ^ ((r >> 1) & 7): a fragment read (32 rows, one chunk each) then
-//      hits 16 distinct 16-byte bank groups per 16 lanes;
-//   W  [s][16 tiles][2 KB] at 64 KB + 32 KB s: the packed tiles of the step as
-//      they are ([chunk 8][column 16][16 B], chunk c = K elements 32c + [0,
-//      32) of the step);
-//   SA [s][256 rows][8 B] at 128 KB + 2 KB s: the eight E8M0 bytes of each A
-//      row;
-//   SB [s][2][1 KB] at 132 KB + 2 KB s: the packed W scale chunks of the step
-//      for the two 128-column halves ([chunk 8][column 16][tile 8]).
-// Quarter u (0..3) of a step is one matrix instruction per fragment pair;
-// lane l feeds row (column) l & 31 with chunk 4j + u (j = l >> 5), so the
-// instruction covers blocks u and 4 + u and each lane's scale is byte u of
-// dword j of its row's (column's) eight scale bytes.
-template <int NW>
-struct Mx256 {
-  static constexpr int FN = 16 / NW;                    // 32-column fragments per wave
-  static constexpr int THREADS = 64 * NW;
-  static constexpr int ROW = 128;                         // A bytes per row and step
-  static constexpr int A_STAGE = kBig * ROW;              // 32 KB
-  static constexpr int W_OFF = 2 * A_STAGE;               // 64 KB
-  static constexpr int W_STAGE = 16 * kTileBytes;         // 32 KB
-  static constexpr int SA_OFF = W_OFF + 2 * W_STAGE;      // 128 KB
-  static constexpr int SA_STAGE = kBig * 8;               // 2 KB
-  static constexpr int SB_OFF = SA_OFF + 2 * SA_STAGE;    // 132 KB
-  static constexpr int SB_STAGE = 2048;
-  static constexpr int LDS = SB_OFF + 2 * SB_STAGE;       // 136 KB
-  typedef floatx16 Acc[4][FN];
-  struct Quarter {
-    uintx4 a[4];
-    uintx4 b[FN];
-    uint32_t sb[FN / 2];   // the scale bytes of the lane's column in this wave's tiles
-  };
-  struct Lane {
-    int a[4], b[4], sb, sa;   // stage 0; quarter u of sb is 128 u further
-    uint32_t shb;
-  };
-  __device__ __forceinline__ static int swizzle(int r) { return (r >> 1) & 7; }
-  // wave (wm, wn): rows 128 wm + [0, 128), columns 32 FN wn + [0, 32 FN) =
-  // column tiles 2 FN wn .. 2 FN wn + 2 FN - 1
-  __device__ __forceinline__ static Lane lane_offsets(int wm, int wn, int lane) {
-    const int r = wm * 128 + (lane & 31), j = lane >> 5;
-    const int par = (lane >> 4) & 1;
-    Lane L;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = 4 * j + u;
-      L.a[u] = r * ROW + 16 * (c ^ swizzle(r));
-      L.b[u] = W_OFF + (wn * 2 * FN + par) * kTileBytes + c * 256 + 16 * (lane & 15);
-    }
-    // the wave's tiles are dwords (2 FN wn / 4 ..) of its column's 8-byte
-    // entry in 128-column half 2 FN wn / 8
-    L.sb = SB_OFF + (2 * FN * wn / 8) * 1024 + 4 * j * 128 + 8 * (lane & 15) +
-           4 * ((2 * FN * wn / 4) & 1);
-    L.sa = SA_OFF + 8 * r + 4 * j;
-    L.shb = 8u * par;
-    return L;
-  }
-  template <int S, int U>
-  __device__ __forceinline__ static void read(Quarter& X, const uint8_t* lds, const Lane& L) {
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
-      X.a[fm] = *reinterpret_cast<const uintx4*>(lds + L.a[U] + (S * A_STAGE + fm * 32 * ROW));
-#pragma unroll
-    for (int p = 0; p < FN; ++p)
-      X.b[p] =
-          *reinterpret_cast<const uintx4*>(lds + L.b[U] + (S * W_STAGE + p * 2 * kTileBytes));
-#pragma unroll
-    for (int d = 0; d < FN / 2; ++d)
-      X.sb[d] = *reinterpret_cast<const uint32_t*>(lds + L.sb + (S * SB_STAGE + U * 128 + 4 * d));
-  }
-  template <int S>
-  __device__ __forceinline__ static void read_sa(uint32_t (&sa)[4], const uint8_t* lds,
-                                                 const Lane& L) {
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm)
-      sa[fm] = *reinterpret_cast<const uint32_t*>(lds + L.sa + (S * SA_STAGE + fm * 32 * 8));
-  }
-  template <int U, int P>
-  __device__ __forceinline__ static void mma_pair(const Quarter& X, const uint32_t (&sa)[4],
-                                                  const Lane& L, Acc& acc) {
-    const intx8 bf = {(int)X.b[P][0], (int)X.b[P][1], (int)X.b[P][2], (int)X.b[P][3],
-                      0, 0, 0, 0};
-    // byte 2 (P & 1) of the shifted word P / 2: tile 2P + par of the wave's
-    const int sb = (int)(X.sb[P >> 1] >> L.shb);
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm) {
-      const intx8 af = {(int)X.a[fm][0], (int)X.a[fm][1], (int)X.a[fm][2], (int)X.a[fm][3],
-                        0, 0, 0, 0};
-      acc[fm][P] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          af, bf, acc[fm][P], kFmtFP4, kFmtFP4, U, (int)sa[fm], 2 * (P & 1), sb);
-    }
-  }
-  template <int U>
-  __device__ __forceinline__ static void mma(const Quarter& X, const uint32_t (&sa)[4],
-                                             const Lane& L, Acc& acc) {
-    mma_pair<U, 0>(X, sa, L, acc);
-    mma_pair<U, 1>(X, sa, L, acc);
-    if constexpr (FN == 4) {
-      mma_pair<U, 2>(X, sa, L, acc);
-      mma_pair<U, 3>(X, sa, L, acc);
-    }
-  }
+// The matrix instruction takes W as its first operand and A as its second,
+// which yields C transposed in the accumulators: lane l holds C row
+// (l & 31) of its 32-row fragment and, for each e >> 2, four consecutive
+// columns 8 (e >> 2) + 4 (l >> 5) + [0, 4) of its 32-column fragment, so the
+// epilogue writes 8 bytes per lane.
+//
+// Per quarter u of a step (one 64-element K slice, blocks u and 4 + u of the
+// step; lane l feeds chunk 4 (l >> 5) + u of its row or column):
+//   - LDS reads of the next quarter's 8 A fragments (and in quarter 3, after
+//     the barrier, those of quarter 0 of step s + 1 plus its A scales);
+//   - 16 matrix instructions, each beside one memory instruction: the 2 W
+//     fragment loads and the W scale dword of the same quarter of step
+//     s + WB - 1, then this quarter's share of the copies of step s + 3
+//     (8 A copies of 8 rows x 128 B, 2 A-scale copies of 32 rows x 8 B);
+//   - after quarter 2: wait until this wave's copies of step s + 1 have
+//     landed and its LDS reads have returned, and meet the other waves.
+//
+// Measured at M = N = K = 8192 against the earlier kernel (2 x 2 waves of
+// 128 x 128, A and W both through a two-stage LDS ring with the copies in two
+// of the four quarters): 257-270 us against 266-277 us, box to box; a
+// three-step W register ring measured the same as two.  Counters on this
+// kernel: the matrix pipe 57% busy at 1.76-1.82 GHz, and the clock falls as
+// that share rises (1.95 GHz at 45% busy with K = 4096, 1.70 GHz at 63% with
+// K = 16384), so part of the remaining gap is the power the operand traffic
+// and the matrix pipe draw together.  A persistent form (one workgroup per
+// CU, the copy ring running across tile boundaries, results stored straight
+// from the accumulators) took the same kernel time and was not kept.
+namespace mxw {
+constexpr int kRow = 128;                     // A bytes per row and step
+constexpr int kAStage = kBig * kRow;          // 32 KB
+constexpr int kStage = kAStage + kBig * 8;    // + 8 scale bytes per row
+constexpr int kStages = 4;
+constexpr int kLds = kStages * kStage;        // 136 KB
+constexpr int kOps[4] = {6, 6, 5, 5};         // memory instructions per quarter
+// ops issued after the copies of step s + 1 when the wait after quarter 2 of
+// step s runs: all of step s - 1 and quarters 0-2 of step s
+constexpr int kCopyWait = 22 + 6 + 6 + 5;
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+}  // namespace mxw
 
-  // The copies of a step (32 of A: 8 rows x 128 B each; 16 W tiles: two 1 KB
-  // halves each; 8 of A scales: 32 rows x 8 B each; 8 of W scales: 256 B
-  // each), split evenly over the waves.  Everything but the step's own
-  // offset is fixed per wave and lane.
-  static constexpr int NA = 32 / NW, NT = 16 / NW, NS = 8 / NW;
-  static constexpr int COPIES = NA + 2 * NT + 2 * NS;
-  struct Copies {
-    __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
-    uint32_t a_base[NA];   // A: row offset plus the lane's chunk
-    int a_kb[NA];          // A: the chunk's byte within a step
-    uint32_t w_base[NT];   // W: the tile's first K tile plus the lane's 16 B
-    uint32_t sa_base[NS];  // A scales: the lane's row and dword
-    int sa_kb;             // A scales: the dword's byte within a step (0 or 4)
-    uint32_t sw_base[NS];  // W scales: the copy's 256 B in step 0
-    int row_bytes, sc_cols, KT;
-    int a_lds[NA], w_lds[NT], sa_lds[NS], sw_lds[NS];
-  };
-  __device__ __forceinline__ static Copies plan(int wave, int lane, int m0, int cg0,
-                                                const PipeArgs& g, const PipeRsrc& rs) {
-    Copies C;
-    C.ra = rs.a;
-    C.rw = rs.w;
-    C.rsa = rs.sa;
-    C.rsw = rs.sw;
-    C.row_bytes = g.K / 2;
-    C.sc_cols = g.K / 32;
-    C.KT = g.KT;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int q = NA * wave + i;
-      const int r = 8 * q + (lane >> 3);
-      const int c = (lane & 7) ^ swizzle(r);
-      C.a_kb[i] = 16 * c;
-      C.a_base[i] = (uint32_t)(m0 + r) * (uint32_t)C.row_bytes + 16u * c;
-      C.a_lds[i] = q * 1024;
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int t = NT * wave + i;
-      C.w_base[i] = (uint32_t)(cg0 + t) * (uint32_t)g.KT * kTileBytes + 16u * lane;
-      C.w_lds[i] = t * kTileBytes;
-    }
-    C.sa_kb = 4 * (lane & 1);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int q = NS * wave + i;   // 0 .. 7
-      C.sa_base[i] = (uint32_t)(m0 + 32 * q + (lane >> 1)) * (uint32_t)C.sc_cols + C.sa_kb;
-      C.sa_lds[i] = 256 * q;
-      C.sw_base[i] = (uint32_t)(cg0 / 8 + (q >> 2)) * (uint32_t)g.KS * 512u + 256u * (q & 3) +
-                     4u * lane;
-      C.sw_lds[i] = 256 * q;
-    }
-    return C;
-  }
-  // K % 128 == 0, so a 16-byte A chunk or a 4-byte scale word is wholly
-  // inside K or past it; past it the copy reads zeros, and so does every copy
-  // of a step s >= KT (all-zero codes and scales: such a step adds exactly 0)
-  // Part H (0 or 1) of the copies of step s: half of the A and W copies and
-  // half of the scale copies (with one scale copy of each kind per wave, the
-  // A scales go in part 0 and the W scales in part 1).
-  static constexpr int PART_COPIES = COPIES / 2;
-  template <int S, int H>
-  __device__ __forceinline__ static void issue(uint8_t* lds, int s, const Copies& C) {
-    uint8_t* const sta = lds + S * A_STAGE;
-    uint8_t* const stw = lds + W_OFF + S * W_STAGE;
-#pragma unroll
-    for (int i = H * NA / 2; i < (H + 1) * NA / 2; ++i) {
-      const int kb = s * ROW + C.a_kb[i];
-      dma16(C.ra, sta + C.a_lds[i],
-            kb < C.row_bytes ? C.a_base[i] + (uint32_t)s * ROW : kOutOfRange);
-    }
-    const bool in_kt = s < C.KT;
-#pragma unroll
-    for (int i = H * NT / 2; i < (H + 1) * NT / 2; ++i) {
-      const uint32_t off = in_kt ? C.w_base[i] + (uint32_t)s * kTileBytes : kOutOfRange;
-      dma16(C.rw, stw + C.w_lds[i], off);
-      dma16(C.rw, stw + C.w_lds[i] + 1024, off + 1024u);
-    }
-    const bool sa_in = 8 * s + C.sa_kb < C.sc_cols;
-    if constexpr (NS == 1) {
-      if constexpr (H == 0)
-        dma4(C.rsa, lds + SA_OFF + S * SA_STAGE + C.sa_lds[0],
-             sa_in ? C.sa_base[0] + 8u * s : kOutOfRange);
-      else
-        dma4(C.rsw, lds + SB_OFF + S * SB_STAGE + C.sw_lds[0],
-             in_kt ? C.sw_base[0] + 1024u * s : kOutOfRange);
-    } else {
-#pragma unroll
-      for (int i = H * NS / 2; i < (H + 1) * NS / 2; ++i) {
-        dma4(C.rsa, lds + SA_OFF + S * SA_STAGE + C.sa_lds[i],
-             sa_in ? C.sa_base[i] + 8u * s : kOutOfRange);
-        dma4(C.rsw, lds + SB_OFF + S * SB_STAGE + C.sw_lds[i],
-             in_kt ? C.sw_base[i] + 1024u * s : kOutOfRange);
-      }
-    }
-  }
-};
-
-// 32 x 32 accumulators of a 128 x 32 FN wave block -> the LDS C tile.
-template <int NW>
-__device__ __forceinline__ void mx256_stage(const typename Mx256<NW>::Acc& acc, uint8_t* ct,
-                                          int wm, int wn, int lane) {
-  constexpr int FN = Mx256<NW>::FN;
-#pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int col = wn * 32 * FN + fn * 32 + (lane & 31);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = wm * 128 + fm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        *reinterpret_cast<uint16_t*>(ct + c_tile_offset(row, col)) =
-            round_out<false>(acc[fm][fn][e]);
-      }
-    }
-}
-
-// vmcnt(0) and lgkmcnt(0), then a bare workgroup barrier: this wave's copies
-// have landed and its LDS reads have returned
-#define QG_WAIT_ALL_BARRIER()                          \
-  do {                                                 \
-    __builtin_amdgcn_sched_barrier(0);                 \
-    __builtin_amdgcn_s_waitcnt(0x0070);                \
-    __builtin_amdgcn_s_barrier();                      \
-    __builtin_amdgcn_sched_barrier(0);                 \
+// vmcnt = n and lgkmcnt = 0, then a bare workgroup barrier
+#define QG_WAIT_VM_LGKM_BARRIER(n)                                              \
+  do {                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                          \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | 0x70);  \
+    __builtin_amdgcn_s_barrier();                                               \
+    __builtin_amdgcn_sched_barrier(0);                                          \
   } while (0)
 
-// Step s, in stage S = s % 2.  Quarters 0-2 compute from registers while
-// the next quarter's fragments arrive; then every wave waits for its copies
-// of step s + 1 and for its reads of stage S, and meets the others.  Quarter 3
-// reads quarter 0 of step s + 1 and, as stage S is now free, issues the first
-// half of the copies of step s + 2 into it; quarter 0 of step s + 1 issues the
-// second half (the same time was measured with all of them in quarter 3).
-// Each copy is pinned beside a matrix instruction.  (In the last two steps
-// these read and copy steps past K: zeros, never used.)
-template <class P, int N>
-__device__ __forceinline__ void pin_copies() {
+struct MxwPlan {
+  __amdgpu_buffer_rsrc_t ra, rsa, rw, rsw;
+  int rd_a[4];          // LDS: A chunk of quarter u within a stage (fragment fm: + 4096 fm)
+  int rd_sa;            // LDS: the lane's row's scale dword (fragment fm: + 256 fm)
+  uint32_t w[2];        // W fragment f of step 0 (step s: + 2048 s; quarter u: + 256 u)
+  uint32_t ws;          // W scale dword of step 0 (step s: + 1024 s; quarter u: + 128 u)
+  uint32_t a_g[8];      // A copy i of step 0 (step s: + 128 s)
+  int a_kb[8];          // its chunk's byte within a step
+  uint32_t sa_g[2];     // A scale copy i of step 0 (step s: + 8 s)
+  int sa_kb;
+  int a_lds[8], sa_lds[2];
+  uint32_t shb;         // 8 * ((lane >> 4) & 1): the W scale byte of the lane's tile
+  int row_bytes, sc_cols, KT;
+};
+
+struct MxwW {
+  uintx4 b[4][2];       // [quarter][fragment]
+  uint32_t s[4];        // [quarter] W scale dword (the wave's 4 tiles)
+};
+
+typedef floatx16 MxwAcc[8][2];
+
+template <int U>
+__device__ __forceinline__ void mxw_read_a(uintx4 (&x)[8], const uint8_t* st, const MxwPlan& P) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one vector memory read
+  for (int fm = 0; fm < 8; ++fm)
+    x[fm] = *reinterpret_cast<const uintx4*>(st + P.rd_a[U] + fm * 4096);
+}
+
+__device__ __forceinline__ void mxw_read_sa(uint32_t (&sa)[8], const uint8_t* st,
+                                            const MxwPlan& P) {
+#pragma unroll
+  for (int fm = 0; fm < 8; ++fm)
+    sa[fm] = *reinterpret_cast<const uint32_t*>(st + P.rd_sa + fm * 256);
+}
+
+template <int U>
+__device__ __forceinline__ void mxw_load_w(MxwW& W, int s, const MxwPlan& P) {
+  const bool in = s < P.KT;
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+    W.b[U][f] = __builtin_amdgcn_raw_buffer_load_b128(
+        P.rw, in ? P.w[f] + (uint32_t)s * 2048u + 256u * U : kOutOfRange, 0, 0);
+  W.s[U] = __builtin_amdgcn_raw_buffer_load_b32(
+      P.rsw, in ? P.ws + (uint32_t)s * 1024u + 128u * U : kOutOfRange, 0, 0);
+}
+
+// quarter U's share of the copies of step s into stage memory cst
+template <int U>
+__device__ __forceinline__ void mxw_copies(uint8_t* cst, int s, const MxwPlan& P) {
+#pragma unroll
+  for (int i = 2 * U; i < 2 * U + 2; ++i) {
+    const int kb = s * mxw::kRow + P.a_kb[i];
+    dma16(P.ra, cst + P.a_lds[i], kb < P.row_bytes ? P.a_g[i] + (uint32_t)s * mxw::kRow
+                                                   : kOutOfRange);
+  }
+  if constexpr (U < 2) {
+    const bool in = 8 * s + P.sa_kb < P.sc_cols;
+    dma4(P.rsa, cst + mxw::kAStage + P.sa_lds[U], in ? P.sa_g[U] + 8u * s : kOutOfRange);
   }
 }
 
-template <int NW, int S, class P = Mx256<NW>>
-__device__ __forceinline__ void mx256_step(typename P::Quarter& X0, typename P::Quarter& X1,
-                                           uint32_t (&sc)[4], uint32_t (&sn)[4], uint8_t* lds,
-                                           int s, const typename P::Lane& L,
-                                           typename P::Acc& acc, const typename P::Copies& C) {
-  constexpr int PAIRS = P::PART_COPIES < 4 * P::FN ? P::PART_COPIES : 4 * P::FN;
-  P::template read<S, 1>(X1, lds, L);
-  P::template mma<0>(X0, sc, L, acc);
-  P::template issue<1 - S, 1>(lds, s + 1, C);   // second half of step s + 1
-  pin_copies<P, PAIRS>();
+template <int U, int F>
+__device__ __forceinline__ void mxw_mma_f(const uintx4 (&x)[8], const MxwW& W,
+                                          const uint32_t (&sa)[8], int sw, MxwAcc& acc) {
+  const intx8 wf = {(int)W.b[U][F][0], (int)W.b[U][F][1], (int)W.b[U][F][2],
+                    (int)W.b[U][F][3], 0, 0, 0, 0};
+#pragma unroll
+  for (int fm = 0; fm < 8; ++fm) {
+    const intx8 af = {(int)x[fm][0], (int)x[fm][1], (int)x[fm][2], (int)x[fm][3], 0, 0, 0, 0};
+    acc[fm][F] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        wf, af, acc[fm][F], kFmtFP4, kFmtFP4, 2 * F, sw, U, (int)sa[fm]);
+  }
+}
+
+template <int U>
+__device__ __forceinline__ void mxw_mma(const uintx4 (&x)[8], const MxwW& W,
+                                        const uint32_t (&sa)[8], uint32_t shb, MxwAcc& acc) {
+  const int sw = (int)(W.s[U] >> shb);   // byte 2 f: the lane's tile of fragment f
+  mxw_mma_f<U, 0>(x, W, sa, sw, acc);
+  mxw_mma_f<U, 1>(x, W, sa, sw, acc);
+}
+
+// the quarter's LDS reads first, then one matrix instruction beside one
+// memory instruction, N times
+template <int N, int R = 8>
+__device__ __forceinline__ void mxw_pin() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
+// step s; W[B] holds its W fragments, sa[B] its A scales, x[0] its quarter-0
+// A fragments
+template <int WB, int B>
+__device__ __forceinline__ void mxw_step(int s, uint8_t* lds, MxwW (&W)[WB],
+                                         uintx4 (&x)[2][8], uint32_t (&sa)[WB][8],
+                                         const MxwPlan& P, MxwAcc& acc) {
+  constexpr int BN = (B + WB - 1) % WB;   // W of step s + WB - 1
+  constexpr int BS = (B + 1) % WB;        // A scales of step s + 1
+  const uint8_t* st = lds + (s & 3) * mxw::kStage;
+  const uint8_t* nst = lds + ((s + 1) & 3) * mxw::kStage;
+  uint8_t* cst = lds + ((s + 3) & 3) * mxw::kStage;
+  const int sw = s + WB - 1;
+
+  mxw_read_a<1>(x[1], st, P);
+  mxw_mma<0>(x[0], W[B], sa[B], P.shb, acc);
+  mxw_load_w<0>(W[BN], sw, P);
+  mxw_copies<0>(cst, s + 3, P);
+  mxw_pin<mxw::kOps[0]>();
   __builtin_amdgcn_sched_barrier(0);
-  P::template read<S, 2>(X0, lds, L);
-  P::template mma<1>(X1, sc, L, acc);
+
+  mxw_read_a<2>(x[0], st, P);
+  mxw_mma<1>(x[1], W[B], sa[B], P.shb, acc);
+  mxw_load_w<1>(W[BN], sw, P);
+  mxw_copies<1>(cst, s + 3, P);
+  mxw_pin<mxw::kOps[1]>();
   __builtin_amdgcn_sched_barrier(0);
-  P::template read<S, 3>(X1, lds, L);
-  P::template mma<2>(X0, sc, L, acc);
-  QG_WAIT_ALL_BARRIER();
-  P::template read<1 - S, 0>(X0, lds, L);
-  P::template read_sa<1 - S>(sn, lds, L);
-  P::template mma<3>(X1, sc, L, acc);
-  P::template issue<S, 0>(lds, s + 2, C);       // first half of step s + 2
-  pin_copies<P, PAIRS>();
+
+  mxw_read_a<3>(x[1], st, P);
+  mxw_mma<2>(x[0], W[B], sa[B], P.shb, acc);
+  mxw_load_w<2>(W[BN], sw, P);
+  mxw_copies<2>(cst, s + 3, P);
+  mxw_pin<mxw::kOps[2]>();
+  QG_WAIT_VM_LGKM_BARRIER(mxw::kCopyWait);
+
+  mxw_read_a<0>(x[0], nst, P);
+  mxw_read_sa(sa[BS], nst, P);
+  mxw_mma<3>(x[1], W[B], sa[B], P.shb, acc);
+  mxw_load_w<3>(W[BN], sw, P);
+  mxw_copies<3>(cst, s + 3, P);
+  mxw_pin<mxw::kOps[3], 16>();
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// C tile in LDS for this kernel: row-major [256][512 B], 16-byte chunk k of
+// row r at slot k ^ (r & 15), so the 8-byte writes of 32 consecutive rows
+// fall into 16 different bank groups.
+__device__ __forceinline__ int mxw_c_offset(int row, int col) {
+  return row * (kBig * 2) + 16 * ((col >> 3) ^ (row & 15)) + 2 * (col & 7);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 
 // MXFP4, M and N > 128, K % 128 == 0, at least two 256-element K tiles.
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void mx256_kernel(
-    const uint8_t* __restrict__ a, const uint8_t* __restrict__ a_sc,
-    const uint8_t* __restrict__ wp, const uint8_t* __restrict__ w_sc,
-    uint16_t* __restrict__ c, PipeArgs g) {
-  using P = Mx256<NW>;
-  constexpr int LDS_BYTES = P::LDS > kCTileBytes ? P::LDS : kCTileBytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+template <int WB>
+__global__ __launch_bounds__(256) void mxw_kernel(const uint8_t* __restrict__ a,
+                                                  const uint8_t* __restrict__ a_sc,
+                                                  const uint8_t* __restrict__ wp,
+                                                  const uint8_t* __restrict__ w_sc,
+                                                  uint16_t* __restrict__ c, PipeArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[mxw::kLds];
+  static_assert(mxw::kLds >= kCTileBytes, "the C tile reuses the stage memory");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / (NW / 2);
-  const int wn = wave % (NW / 2);
 
-  // XCD-aware tile walk, as in pipe256_kernel
+  // XCD-aware tile walk, as in the other 256 x 256 kernels
   const int T = g.tiles_m * g.tiles_n;
   const int bid = blockIdx.x;
   const int id = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
@@ -1185,58 +1102,128 @@ __global__ __launch_bounds__(64 * NW) void mx256_kernel(
   const int m0 = tm * kBig;
   const int cg0 = tn * (kBig / 16);
 
-  PipeRsrc rs;
-  rs.a = make_rsrc(a, g.a_bytes);
-  rs.w = make_rsrc(wp, g.w_bytes);
-  rs.sa = make_rsrc(a_sc, g.asc_bytes);
-  rs.sw = make_rsrc(w_sc, g.wsc_bytes);
-  const typename P::Copies C = P::plan(wave, lane, m0, cg0, g, rs);
-  const typename P::Lane L = P::lane_offsets(wm, wn, lane);
-
-  typename P::Acc acc;
+  MxwPlan P;
+  P.ra = make_rsrc(a, g.a_bytes);
+  P.rsa = make_rsrc(a_sc, g.asc_bytes);
+  P.rw = make_rsrc(wp, g.w_bytes);
+  P.rsw = make_rsrc(w_sc, g.wsc_bytes);
+  P.row_bytes = g.K / 2;
+  P.sc_cols = g.K / 32;
+  P.KT = g.KT;
+  {
+    const int cl = lane & 31, j = lane >> 5, par = (lane >> 4) & 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int u = 0; u < 4; ++u) P.rd_a[u] = cl * mxw::kRow + 16 * ((4 * j + u) ^ mxw::swz(cl));
+    P.rd_sa = mxw::kAStage + 8 * cl + 4 * j;
 #pragma unroll
-    for (int j = 0; j < P::FN; ++j)
+    for (int f = 0; f < 2; ++f)
+      P.w[f] = (uint32_t)(cg0 + 4 * wave + 2 * f + par) * (uint32_t)g.KT * 2048u +
+               1024u * j + 16u * (lane & 15);
+    P.ws = (uint32_t)(cg0 / 8 + (wave >> 1)) * (uint32_t)g.KS * 512u + 512u * j +
+           8u * (lane & 15) + 4u * (wave & 1);
+    P.shb = 8u * par;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  const int KT = g.KT;
-
-  // step s lives in stage s % 2; its copies go out in quarter 3 of step s - 2
-  P::template issue<0, 0>(smem, 0, C);
-  P::template issue<0, 1>(smem, 0, C);
-  P::template issue<1, 0>(smem, 1, C);   // its other half goes out in step 0
-  QG_WAIT_VM_BARRIER(P::PART_COPIES);    // step 0 landed
-  typename P::Quarter X0, X1;
-  uint32_t sa0[4], sa1[4];
-  P::template read<0, 0>(X0, smem, L);
-  P::template read_sa<0>(sa0, smem, L);
-
-  // an even number of steps: for odd KT the last one is all zeros
-  const int KP = KT + (KT & 1);
-  for (int s = 0; s < KP; s += 2) {
-    mx256_step<NW, 0>(X0, X1, sa0, sa1, smem, s, L, acc, C);
-    mx256_step<NW, 1>(X0, X1, sa1, sa0, smem, s + 1, L, acc, C);
+    for (int i = 0; i < 8; ++i) {
+      const int q = 8 * wave + i;
+      const int r = 8 * q + (lane >> 3);
+      const int ch = (lane & 7) ^ mxw::swz(r);
+      P.a_kb[i] = 16 * ch;
+      P.a_g[i] = (uint32_t)(m0 + r) * (uint32_t)P.row_bytes + 16u * ch;
+      P.a_lds[i] = q * 1024;
+    }
+    P.sa_kb = 4 * (lane & 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = 2 * wave + i;
+      P.sa_g[i] = (uint32_t)(m0 + 32 * q + (lane >> 1)) * (uint32_t)P.sc_cols + P.sa_kb;
+      P.sa_lds[i] = 256 * q;
+    }
   }
-  // the copies of steps KP and KP + 1 (all zeros) land before the LDS is
-  // reused for the output tile
-  __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  PipeOut o;
-  o.c = c;
-  o.M = g.M;
-  o.N = g.N;
-  __syncthreads();   // every wave has finished with the last stage
-  mx256_stage<NW>(acc, smem, wm, wn, lane);
+  MxwAcc acc;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][f][e] = 0.f;
+
+  // prologue: the copies of steps 0, 1, 2 and the W of steps 0 .. WB - 2
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    uint8_t* cst = smem + s * mxw::kStage;
+    mxw_copies<0>(cst, s, P);
+    mxw_copies<1>(cst, s, P);
+    mxw_copies<2>(cst, s, P);
+    mxw_copies<3>(cst, s, P);
+  }
+  MxwW W[WB];
+#pragma unroll
+  for (int b = 0; b < WB - 1; ++b) {
+    mxw_load_w<0>(W[b], b, P);
+    mxw_load_w<1>(W[b], b, P);
+    mxw_load_w<2>(W[b], b, P);
+    mxw_load_w<3>(W[b], b, P);
+  }
+  // step 0's copies are the oldest: all but the later 20 copies and the W loads
+  QG_WAIT_VM_BARRIER(20 + 12 * (WB - 1));
+  uintx4 x[2][8];
+  uint32_t sa[WB][8];
+  mxw_read_a<0>(x[0], smem, P);
+  mxw_read_sa(sa[0], smem, P);
+
+  const int KS = g.KT;   // one step per 256-element K tile
+  int s = 0;
+  for (; s + WB <= KS; s += WB) {
+    mxw_step<WB, 0>(s, smem, W, x, sa, P, acc);
+    mxw_step<WB, 1>(s + 1, smem, W, x, sa, P, acc);
+    if constexpr (WB == 3) mxw_step<WB, 2>(s + 2, smem, W, x, sa, P, acc);
+  }
+  if (s < KS) mxw_step<WB, 0>(s, smem, W, x, sa, P, acc);
+  if constexpr (WB == 3)
+    if (s + 1 < KS) mxw_step<WB, 1>(s + 1, smem, W, x, sa, P, acc);
+
+  // every copy and load (those past K read zeros) has landed before the stage
+  // memory becomes the C tile
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  pipe_copy_out<64 * NW>(smem, o, m0, cg0 * 16);
+#pragma unroll
+  for (int fm = 0; fm < 8; ++fm)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 32 * fm + (lane & 31);
+        const int col = 64 * wave + 32 * f + 8 * q + 4 * (lane >> 5);
+        const uintx2 v = {pack_bf16x2(acc[fm][f][4 * q], acc[fm][f][4 * q + 1]),
+                          pack_bf16x2(acc[fm][f][4 * q + 2], acc[fm][f][4 * q + 3])};
+        *reinterpret_cast<uintx2*>(smem + mxw_c_offset(row, col)) = v;
+      }
+  __syncthreads();
+  const bool vec = (g.N & 7) == 0;
+  const int n0 = cg0 * 16;
+#pragma unroll 4
+  for (int jj = 0; jj < kCTileBytes / 16 / 256; ++jj) {
+    const int q = (int)threadIdx.x + 256 * jj;
+    const int row = q >> 5, ch = q & 31;
+    const int gm = m0 + row, gn = n0 + 8 * ch;
+    if (gm >= g.M || gn >= g.N) continue;
+    const uintx4 v = *reinterpret_cast<const uintx4*>(smem + row * (kBig * 2) +
+                                                      16 * (ch ^ (row & 15)));
+    uint16_t* dst = c + (int64_t)gm * g.N + gn;
+    if (vec) {
+      *reinterpret_cast<uintx4*>(dst) = v;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (gn + t < g.N) dst[t] = (uint16_t)(v[t >> 1] >> (16 * (t & 1)));
+    }
+  }
 }
 
-// waves per workgroup (four and eight measured the same)
-constexpr int kMx256Waves = 4;
-
-hipError_t launch_mx256(const void* a, const void* a_sc, const void* wp, void* c, int64_t M,
-                        int64_t N, int64_t K, hipStream_t stream) {
+template <int WB>
+hipError_t launch_mxw(const void* a, const void* a_sc, const void* wp, void* c, int64_t M,
+                      int64_t N, int64_t K, hipStream_t stream) {
   const PackGeom pg = pack_geom(3, K, N);
   PipeArgs g;
   g.M = (int)M;
@@ -1252,8 +1239,7 @@ hipError_t launch_mx256(const void* a, const void* a_sc, const void* wp, void* c
   g.asc_bytes = (uint32_t)(M * (K / 32));
   g.wsc_bytes = (uint32_t)(pg.total - pg.scales);
   const uint8_t* w_sc = static_cast<const uint8_t*>(wp) + pg.scales;
-  hipLaunchKernelGGL(mx256_kernel<kMx256Waves>, dim3((unsigned)(g.tiles_m * g.tiles_n)),
-                     dim3(64 * kMx256Waves), 0,
+  hipLaunchKernelGGL(mxw_kernel<WB>, dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256), 0,
                      stream, static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(a_sc),
                      static_cast<const uint8_t*>(wp), w_sc, static_cast<uint16_t*>(c), g);
   return hipGetLastError();
@@ -1385,7 +1371,7 @@ hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const vo
   const bool big = M > 128 && N > 128 && cdiv(K, kTileK8) >= 2 && pipe_fits(fmt, M, N, K, 0);
   if (fmt == 3) {
     if (big && K % 128 == 0 && cdiv(K, kTileK4) >= 2)
-      return launch_mx256(a, a_e8m0, w_packed, c, M, N, K, stream);
+      return launch_mxw<2>(a, a_e8m0, w_packed, c, M, N, K, stream);
     return launch_tiles<true, 4, 4>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
   }
   if (fmt == 4) {
