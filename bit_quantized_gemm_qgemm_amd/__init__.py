@@ -49,8 +49,12 @@ _SIGNATURES = [
     ("qgemm_act_workspace_bytes", ctypes.c_int64, [ctypes.c_int, _I64, _I64]),
     ("qgemm_mxfp4_act", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     ("qgemm_fp8_act", ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    ("qgemm_fp8_act_noalloc", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     ("qgemm_read_probe", ctypes.c_int, [_P, _I64, _P, _I64, _P]),
 ]
+
+# largest M * K that qgemm_fp8_act_noalloc accepts (its fixed scratch)
+FP8_ACT_NOALLOC_MAX_ELEMS = 16 * 1024 * 1024
 
 _lib = None
 
@@ -377,6 +381,25 @@ def qgemm_fp8_act(a, b_packed, scale_b, N, workspace=None, out=None):
     _check(lib().qgemm_fp8_act(_ptr(a), _ptr(b_packed), _ptr(scale_b), _ptr(out), _ptr(workspace),
                                M, N, K, _stream(a)), "qgemm_fp8_act")
     return out, workspace
+
+
+def qgemm_fp8_act_noalloc(a, b_packed, scale_b, N, out):
+    """As qgemm_fp8_act, with the quantized A in the library's fixed per-GPU
+    scratch instead of a workspace: the entry point allocates nothing, so the
+    caller passes the output.  M * K <= FP8_ACT_NOALLOC_MAX_ELEMS."""
+    _need(a, torch.float32, 2, "a")
+    _need(b_packed, torch.uint8, 1, "b_packed")
+    if scale_b.dtype != torch.float32 or not scale_b.is_cuda or scale_b.numel() != 1:
+        raise TypeError("scale_b must be a one-element float32 device tensor")
+    M, K = a.shape
+    if b_packed.numel() < qgemm_prepack_bytes(QGEMM_FP8, K, N):
+        raise ValueError("b_packed is smaller than the packed size for this K, N")
+    if out is None:
+        raise ValueError("qgemm_fp8_act_noalloc needs a caller-allocated out [M, N]")
+    out = _out(out, M, N, torch.bfloat16, a.device)
+    _check(lib().qgemm_fp8_act_noalloc(_ptr(a), _ptr(b_packed), _ptr(scale_b), _ptr(out), M, N,
+                                       K, _stream(a)), "qgemm_fp8_act_noalloc")
+    return out
 
 
 def qgemm_read_probe(buf, sink, workgroups):

@@ -145,7 +145,8 @@ int grouped_gemm(int fmt, const void* x, const void* w_packed, void* y, int64_t 
 
 // ---- FP8 GEMM with fp32 A quantized on the device --------------------------
 
-// Checks of qgemm_fp8_act other than the workspace.
+// Checks shared by qgemm_fp8_act and qgemm_fp8_act_noalloc (everything but
+// the workspace).
 int check_fp8_act(const float* a, const void* b_packed, const float* scale_b, void* c,
                   int64_t M, int64_t N, int64_t K) {
   int st = check_sizes(QGEMM_FP8, M, N, K);
@@ -176,6 +177,36 @@ int fp8_act_run(const float* a, const void* b_packed, const float* scale_b, void
                                           c, M, N, K, as_stream(stream)));
 }
 
+// Fixed scratch of qgemm_fp8_act_noalloc, one copy per GPU, held from the
+// moment the code object is loaded on that GPU until the process ends: the
+// codes of A (at most QGEMM_FP8_ACT_NOALLOC_MAX_ELEMS bytes), 16 bytes holding
+// the fp32 scale, then the partial maxima of the quantizer.  Every call on a
+// GPU shares that GPU's copy.  Nothing in it needs to start at zero: each
+// call writes every byte it later reads.
+constexpr int64_t kNoAllocScratchBytes =
+    QGEMM_FP8_ACT_NOALLOC_MAX_ELEMS + 16 + 4 * qgemm::kFp8Partials;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// The device address of this GPU's copy of `scratch`.  In host code the
+// array's name is only a host-side stand-in, so kernels receive the address
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current.
+int scratch_of_current_device(uint8_t** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return QGEMM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return QGEMM_ERR_DEVICE;
+    addr[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(addr[dev]);
+  return QGEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,6 +221,7 @@ const char* qgemm_status_string(int status) {
     case QGEMM_ERR_LAUNCH: return "kernel launch failed";
     case QGEMM_ERR_FORMAT: return "unknown format id";
     case QGEMM_ERR_DEVICE: return "no HIP device available";
+    case QGEMM_ERR_TOO_LARGE: return "input larger than the entry point's fixed scratch";
     default: return "unknown status";
   }
 }
@@ -382,6 +414,18 @@ int qgemm_fp8_act(const float* a, const void* b_packed, const float* scale_b, vo
   if (M == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
   return fp8_act_run(a, b_packed, scale_b, c, static_cast<uint8_t*>(workspace), M, N, K, stream);
+}
+
+int qgemm_fp8_act_noalloc(const float* a, const void* b_packed, const float* scale_b, void* c,
+                          int64_t M, int64_t N, int64_t K, void* stream) {
+  int st = check_fp8_act(a, b_packed, scale_b, c, M, N, K);
+  if (st != QGEMM_OK) return st;
+  if (M * K > QGEMM_FP8_ACT_NOALLOC_MAX_ELEMS) return QGEMM_ERR_TOO_LARGE;
+  if (M == 0) return QGEMM_OK;
+  if ((st = check_device()) != QGEMM_OK) return st;
+  uint8_t* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != QGEMM_OK) return st;
+  return fp8_act_run(a, b_packed, scale_b, c, ws, M, N, K, stream);
 }
 
 int qgemm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int64_t workgroups,

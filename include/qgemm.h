@@ -78,7 +78,9 @@ enum qgemm_status {
                              architecture name and no device is queried)  */
   QGEMM_ERR_LAUNCH = -5,  /* the HIP runtime reported a launch error        */
   QGEMM_ERR_FORMAT = -6,  /* unknown format id                               */
-  QGEMM_ERR_DEVICE = -7   /* no HIP device could be queried                  */
+  QGEMM_ERR_DEVICE = -7,  /* no HIP device could be queried                  */
+  QGEMM_ERR_TOO_LARGE = -8  /* the input exceeds an entry point's fixed
+                               scratch (qgemm_fp8_act_noalloc)              */
 };
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -213,6 +215,24 @@ int qgemm_mxfp4_act(const float* a, const void* w_packed, void* c, void* workspa
 /* C[M,N] bf16 = (FP8(a) * B) * s_a * (*scale_b), a fp32 [M, K]; K % 16 == 0. */
 int qgemm_fp8_act(const float* a, const void* b_packed, const float* scale_b, void* c,
                   void* workspace, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * qgemm_fp8_act_noalloc -- qgemm_fp8_act without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * same kernels and bit-identical output; the quantized A, its scale and the
+ * quantizer's partial maxima go to a fixed scratch array that the library
+ * holds on each GPU (QGEMM_FP8_ACT_NOALLOC_MAX_ELEMS bytes of codes plus
+ * 1040 bytes), so the call allocates nothing.  M * K above
+ * QGEMM_FP8_ACT_NOALLOC_MAX_ELEMS returns QGEMM_ERR_TOO_LARGE and enqueues
+ * nothing.  Every call on one GPU uses that GPU's one scratch array: calls
+ * that may overlap on the same GPU (other streams, other host threads) race
+ * and must be ordered by the caller.  The scratch is not readable by the
+ * caller.
+ */
+#define QGEMM_FP8_ACT_NOALLOC_MAX_ELEMS ((int64_t)16 * 1024 * 1024)
+int qgemm_fp8_act_noalloc(const float* a, const void* b_packed, const float* scale_b, void* c,
+                          int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * qgemm_nvfp4 -- Y[M,N] fp16 = X[M,K] fp16 * W_deq^T with

@@ -18,6 +18,7 @@ HEADER = os.path.join(ROOT, "include", "qgemm.h")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ARCH, ERR_LAUNCH, ERR_FORMAT, ERR_DEVICE = (
     0, -1, -2, -3, -4, -5, -6, -7)
+ERR_TOO_LARGE = -8
 
 
 @pytest.fixture(scope="module")
@@ -41,7 +42,7 @@ def test_header_declares_the_expected_entry_points():
                  "qgemm_status_string", "qgemm_abi_version", "qgemm_prepack_grouped",
                  "qgemm_prepack_grouped_bytes", "qgemm_w4a16_grouped", "qgemm_w8a16_grouped",
                  "qgemm_nvfp4", "qgemm_act_workspace_bytes", "qgemm_mxfp4_act",
-                 "qgemm_fp8_act"):
+                 "qgemm_fp8_act", "qgemm_fp8_act_noalloc"):
         assert want in names
 
 
@@ -54,7 +55,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in (OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ARCH, ERR_LAUNCH, ERR_FORMAT, ERR_DEVICE):
+    for st in (OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ARCH, ERR_LAUNCH, ERR_FORMAT, ERR_DEVICE,
+               ERR_TOO_LARGE):
         s = qg.status_string(st)
         assert s and s != "unknown status"
     assert qg.status_string(12345) == "unknown status"
@@ -224,3 +226,17 @@ def test_arch_check_rejects_other_architectures(lib, monkeypatch):
     assert lib.qgemm_w8a16(GOOD, GOOD, GOOD, GOOD, 0, 16, 32, s) == OK
     monkeypatch.setenv("QGEMM_ARCH_OVERRIDE", "gfx90a")
     assert lib.qgemm_w8a16(GOOD, GOOD, GOOD, GOOD, 4, 16, 32, s) == ERR_ARCH
+
+
+def test_fp8_act_noalloc_argument_errors_need_no_device(lib):
+    s = P(0)
+    fn = lib.qgemm_fp8_act_noalloc
+    assert fn(GOOD, GOOD, None, GOOD, 4, 16, 64, s) == ERR_NULL
+    assert fn(GOOD, ODD, GOOD, GOOD, 4, 16, 64, s) == ERR_ALIGN
+    assert fn(GOOD, GOOD, GOOD, GOOD, 4, 16, 40, s) == ERR_SHAPE
+    assert fn(GOOD, GOOD, GOOD, GOOD, 0, 16, 64, s) == OK
+    # M * K past the fixed scratch (16 Mi elements) is refused on the host
+    limit = qg.FP8_ACT_NOALLOC_MAX_ELEMS
+    assert limit == 16 * 1024 * 1024
+    assert fn(GOOD, GOOD, GOOD, GOOD, limit // 8192 + 1, 16, 8192, s) == ERR_TOO_LARGE
+    assert fn(GOOD, GOOD, GOOD, GOOD, 1, 16, limit + 16, s) == ERR_TOO_LARGE
