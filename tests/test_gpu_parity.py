@@ -351,10 +351,9 @@ MX_CASES = [
                         # so the XCD-remapped walk and its 4-row groups run
     (1280, 1792, 768),  # 5 x 7 = 35 tiles (plain walk), ragged group of tile rows
     (2048, 1024, 1024), # 8 x 4 tiles: remapped walk, two 4-row groups
-    # the persistent kernel (M, N multiples of 256, K % 512 == 0, K >= 2048):
-    (512, 768, 2048),   # 6 tiles: one per workgroup, plain walk, the shortest K
-    (2304, 2560, 2560), # 90 tiles, ten K tiles per output tile
-    (4352, 4096, 2048), # 272 tiles: workgroups with one and with two tiles, remapped walk
+    (512, 768, 2048),   # 6 tiles (plain walk), eight K steps
+    (2304, 2560, 2560), # 90 tiles, ten K steps: the copy ring wraps its four stages
+    (4352, 4096, 2048), # 272 tiles: more than one per CU, remapped walk
 ]
 
 
@@ -395,9 +394,8 @@ def test_mxfp4_one_hot_reads_back_dequantized_weights():
 
 @pytest.mark.parametrize("m,n,k", [(300, 272, 512), (512, 768, 2048)])
 def test_mxfp4_one_hot_through_large_tiles(m, n, k):
-    """One-hot read-back through the 256 x 256 kernels (M, N > 128; the
-    second shape takes the persistent one): every (row tile, column tile, K
-    step, scale byte) mapping is hit, bit-exact."""
+    """One-hot read-back through the 256 x 256 kernel (M, N > 128): every
+    (row tile, column tile, K step, scale byte) mapping is hit, bit-exact."""
     case_id("mxfp4 one-hot large tiles", m, n, k)
     _, w = wl.mxfp4_operands(1, n, k, seed=9)
     wc, we = oracle.mxfp4_quantize(w)
