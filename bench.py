@@ -666,7 +666,7 @@ def kernel_name(setup, m):
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     k_tiles = -(-setup.k // (256 if setup.fmt == "mxfp4" else 128))
     big = m > 128 and setup.n > 128 and k_tiles >= 2 and (setup.fmt != "mxfp4" or setup.k % 128 == 0)
-    name = ("mxw_kernel" if setup.fmt == "mxfp4" else "pipe256_kernel") if big \
+    name = ("mxw_kernel" if setup.fmt == "mxfp4" else "f8w_kernel") if big \
         else "tile_gemm_kernel"
     return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
 

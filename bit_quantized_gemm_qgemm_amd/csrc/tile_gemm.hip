@@ -271,10 +271,11 @@ __global__ __launch_bounds__(kThreads) void tile_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large tiles: 256 x 256 per workgroup, 128 x 128 per wave (256 fp32
-// accumulators per lane, all in AGPRs).  K advances in steps of 64 bytes per
-// row (128 FP4 or 64 FP8 elements) through a 4-deep ring of LDS stages that
-// the buffer unit fills directly from global memory (no VGPR staging).
+// Large tiles for the weight-only formats (fp16 X; MXFP4 and FP8 have their
+// own 256 x 256 kernels further down): 256 x 256 per workgroup, 128 x 128
+// per wave (256 fp32 accumulators per lane, all in AGPRs).  K advances in
+// steps of 64 bytes per row (32 fp16 elements) through a ring of LDS stages
+// that the buffer unit fills directly from global memory (no VGPR staging).
 // Buffer resources bound every operand, so rows past M, column tiles past N
 // and K chunks past K read as zero without predication.
 //
@@ -359,7 +360,7 @@ struct PipeRsrc {
 struct PipeOut {
   uint16_t* c;
   const uint16_t* col_scale;   // W4A16 / W8A16: fp16 scale per output column
-  float s;                     // FP8: scale_a * scale_b
+  float s;                     // NVFP4 weights: the per-tensor scale
   int M, N;
 };
 
@@ -436,107 +437,7 @@ __device__ __forceinline__ void pipe_copy_out(const uint8_t* ct, const PipeOut& 
   }
 }
 
-// 32 x 32 accumulator layout of v_mfma_*_32x32x*: lane holds rows
-// 8 (e >> 2) + 4 (lane >> 5) + (e & 3) of its fragment, column lane & 31.
-__device__ __forceinline__ void stage32(const floatx16 (&acc)[4][4], uint8_t* ct,
-                                        const PipeOut& o, int wm, int wn, int lane) {
-#pragma unroll
-  for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < 4; ++fn) {
-      const int col = wn * 128 + fn * 32 + (lane & 31);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = wm * 128 + fm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        *reinterpret_cast<uint16_t*>(ct + c_tile_offset(row, col)) =
-            round_out<false>(acc[fm][fn][e] * o.s);
-      }
-    }
-}
 
-// FP8: 4 x 4 fragments of 32 x 32 per wave; one step = 64 K elements = one
-// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) per fragment pair.
-// Lane l feeds row (or column) l & 31 with K elements 32 (l >> 5) + [0, 32)
-// of the step, the same K order on both sides.
-// Stage: A | W 16 tiles x 1 KB: bytes [16h, 16h + 16) of the lane group pair
-// 2s, 2s + 1 (s = step within the tile) from both 1 KB halves h.
-struct Fp8Pipe {
-  static constexpr int FMT = 4;
-  template <class F>
-  __device__ __forceinline__ static void init(F&, F&) {}
-  static constexpr int GROUP_WORDS = 0;
-  static constexpr int PARTS = 4;
-  static constexpr int STEPS_PER_TILE = 2;
-  static constexpr int B = 16 * 1024;
-  static constexpr int STAGE = kStageA + B;
-  static constexpr int DMA = 8;
-  static constexpr int NST = 4;                  // 4 x 32 KB
-  static constexpr bool CP_INTERLEAVE = true;
-  static constexpr int CP_PIN_PAIRS = 4;         // copies of parts 0 / 1: 4 / 4
-  typedef floatx16 Acc[4][4];
-  struct Frags {
-    uintx4 alo[4], ahi[4];
-    uintx4 blo[4], bhi[4];
-  };
-  struct Lane {
-    int alo, ahi, b;
-  };
-  __device__ __forceinline__ static int swizzle(int r) { return (r >> 2) & 3; }
-  __device__ __forceinline__ static int row_bytes(int K) { return K; }
-  __device__ __forceinline__ static void issue_rest(uint8_t* st, int ks, int wave, int lane,
-                                                    int, int cg0, const PipeArgs& g,
-                                                    const PipeRsrc& rs) {
-    const int kt = ks >> 1, h = ks & 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 4 * wave + j;
-      const uint32_t off = ((uint32_t)(cg0 + t) * g.KT + kt) * kTileBytes +
-                           1024u * (lane >> 5) + 512u * h + 16u * (lane & 31);
-      dma16(rs.w, st + kStageA + t * 1024, off);
-    }
-  }
-  __device__ __forceinline__ static Lane lane_offsets(int wm, int wn, int lane) {
-    const int r = wm * 128 + (lane & 31), hh = lane >> 5, swz = swizzle(r);
-    Lane L;
-    L.alo = r * kStepBytes + 16 * ((2 * hh) ^ swz);
-    L.ahi = r * kStepBytes + 16 * ((2 * hh + 1) ^ swz);
-    // column tile wn*8 + 2P + ((lane >> 4) & 1); lane group pair half hh
-    L.b = kStageA + (wn * 8 + ((lane >> 4) & 1)) * 1024 + 256 * hh + 16 * (lane & 15);
-    return L;
-  }
-  template <int P>
-  __device__ __forceinline__ static void read(Frags& F, const uint8_t* st, const Lane& L) {
-    F.alo[P] = *reinterpret_cast<const uintx4*>(st + L.alo + P * 2048);
-    F.ahi[P] = *reinterpret_cast<const uintx4*>(st + L.ahi + P * 2048);
-    F.blo[P] = *reinterpret_cast<const uintx4*>(st + L.b + P * 2048);
-    F.bhi[P] = *reinterpret_cast<const uintx4*>(st + L.b + P * 2048 + 512);
-  }
-  template <int P>
-  __device__ __forceinline__ static void mma(const Frags& F, const Lane&, Acc& acc) {
-    const intx8 bf = {(int)F.blo[P][0], (int)F.blo[P][1], (int)F.blo[P][2], (int)F.blo[P][3],
-                      (int)F.bhi[P][0], (int)F.bhi[P][1], (int)F.bhi[P][2], (int)F.bhi[P][3]};
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm) {
-      const intx8 af = {(int)F.alo[fm][0], (int)F.alo[fm][1], (int)F.alo[fm][2],
-                        (int)F.alo[fm][3], (int)F.ahi[fm][0], (int)F.ahi[fm][1],
-                        (int)F.ahi[fm][2], (int)F.ahi[fm][3]};
-      acc[fm][P] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          af, bf, acc[fm][P], kFmtFP8, kFmtFP8, 0, kE8M0One, 0, kE8M0One);
-    }
-  }
-  __device__ __forceinline__ static void zero(Acc& acc) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  }
-  __device__ __forceinline__ static void stage(const Acc& acc, uint8_t* ct, const PipeOut& o,
-                                               int, int wm, int wn, int lane) {
-    stage32(acc, ct, o, wm, wn, lane);
-  }
-};
 
 // W4A16 / W8A16 with fp16 X: 8 x 8 fragments of 16 x 16 per wave; one step =
 // 32 K elements = one v_mfma_f32_16x16x32_f16 per fragment pair.  The step's
@@ -858,7 +759,7 @@ __global__ __launch_bounds__(kThreads) void pipe256_kernel(
   PipeOut o;
   o.c = c;
   o.col_scale = col_scale;
-  o.s = (Ops::FMT == 4) ? (*scale_a) * (*scale_b) : (Ops::FMT == 7) ? *scale_a : 1.0f;
+  o.s = (Ops::FMT == 7) ? *scale_a : 1.0f;
   o.M = g.M;
   o.N = g.N;
   __syncthreads();   // every wave has finished with the last stage
@@ -1148,15 +1049,10 @@ __global__ __launch_bounds__(256) void mxw_kernel(const uint8_t* __restrict__ a,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][f][e] = 0.f;
 
-  // prologue: the copies of steps 0, 1, 2 and the W of steps 0 .. WB - 2
-#pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    uint8_t* cst = smem + s * mxw::kStage;
-    mxw_copies<0>(cst, s, P);
-    mxw_copies<1>(cst, s, P);
-    mxw_copies<2>(cst, s, P);
-    mxw_copies<3>(cst, s, P);
-  }
+  // prologue: the W of steps 0 .. WB - 2, then the copies of steps 0, 1, 2.
+  // The W loads go first so that, as in the loop, plenty of memory
+  // instructions follow each of them: the compiler's waits for these
+  // registers at the loop head take the smaller count of the two paths.
   MxwW W[WB];
 #pragma unroll
   for (int b = 0; b < WB - 1; ++b) {
@@ -1165,12 +1061,23 @@ __global__ __launch_bounds__(256) void mxw_kernel(const uint8_t* __restrict__ a,
     mxw_load_w<2>(W[b], b, P);
     mxw_load_w<3>(W[b], b, P);
   }
-  // step 0's copies are the oldest: all but the later 20 copies and the W loads
-  QG_WAIT_VM_BARRIER(20 + 12 * (WB - 1));
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    uint8_t* cst = smem + s * mxw::kStage;
+    mxw_copies<0>(cst, s, P);
+    mxw_copies<1>(cst, s, P);
+    mxw_copies<2>(cst, s, P);
+    mxw_copies<3>(cst, s, P);
+  }
+  QG_WAIT_VM_BARRIER(20);   // the W loads and step 0's copies landed
   uintx4 x[2][8];
   uint32_t sa[WB][8];
   mxw_read_a<0>(x[0], smem, P);
   mxw_read_sa(sa[0], smem, P);
+  // nothing of the lgkm counter left pending on the way into the loop (the
+  // kernel-argument loads count there too, out of order), so the compiler's
+  // wait at the loop head is the loop's own
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
 
   const int KS = g.KT;   // one step per 256-element K tile
   int s = 0;
@@ -1242,6 +1149,303 @@ hipError_t launch_mxw(const void* a, const void* a_sc, const void* wp, void* c, 
   hipLaunchKernelGGL(mxw_kernel<WB>, dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256), 0,
                      stream, static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(a_sc),
                      static_cast<const uint8_t*>(wp), w_sc, static_cast<uint16_t*>(c), g);
+  return hipGetLastError();
+}
+
+// ---- FP8, 256 x 256 tiles, B fragments straight to registers -------------
+// The MXFP4 kernel's design with e4m3 operands: each of the 4 waves owns all
+// 256 rows and 64 columns (4 column tiles) of the output tile, loads its B
+// fragments straight from the packed tiles into a two-step register ring, and
+// reads A from a four-stage LDS ring of 128-byte steps (128 K elements: one
+// cache line of every A row, 32 KB per step).  A step is two matrix
+// instructions per fragment pair (64 K elements each); lane l feeds row
+// (column) l & 31 with the 32-element chunk q = 2 (l >> 5) + u of the step in
+// instruction u, i.e. 16-byte chunks 2q, 2q + 1 of the A row and halves 0, 1
+// of the packed B tile's lane group q.  An FP8 fragment is 32 bytes per lane,
+// so the step runs in four quarters (instruction u, row fragments 4 v ..
+// 4 v + 3) to keep the A registers at two quarters' worth.  B is the first
+// operand, so the accumulators hold C transposed and the epilogue writes
+// 8 bytes per lane; s_a * s_b multiplies the fp32 result.
+namespace f8w {
+constexpr int kRow = 128;                     // A bytes per row and step
+constexpr int kStage = kBig * kRow;           // 32 KB
+constexpr int kStages = 4;
+constexpr int kLds = kStages * kStage;        // 128 KB
+constexpr int kOps = 4;                       // memory instructions per quarter
+// ops issued after the copies of step s + 1 when the wait after quarter 2 of
+// step s runs: all of step s - 1 and quarters 0-2 of step s
+constexpr int kCopyWait = 16 + 3 * kOps;
+}  // namespace f8w
+
+struct F8wPlan {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int rd_a;             // LDS: A chunk 4 (l >> 5) of the lane's row (XOR 16 (2u + h))
+  uint32_t b[2];        // B fragment f of step 0 (step s: + 2048 s; instruction u: + 256 u,
+                        // half h: + 1024 h)
+  uint32_t a_g[2];      // A copies i = 0, 1 of step 0; copy i: + (i >> 1) * a_step
+  int a_kb[2];          // their chunk's byte within a step
+  uint32_t a_step;
+  int row_bytes, KT;
+};
+
+struct F8wB {
+  uintx4 b[2][2][2];    // [instruction u][fragment f][half h]
+};
+
+typedef floatx16 F8wAcc[8][2];
+
+// quarter Q: instruction u = Q >> 1, row fragments 4 (Q & 1) + [0, 4)
+template <int Q>
+__device__ __forceinline__ void f8w_read_a(uintx4 (&x)[4][2], const uint8_t* st,
+                                           const F8wPlan& P) {
+  constexpr int U = Q >> 1, V = Q & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      x[i][h] = *reinterpret_cast<const uintx4*>(st + (P.rd_a ^ (16 * (2 * U + h))) +
+                                                 (4 * V + i) * 4096);
+}
+
+// B fragment f of instruction U of step s (two 16-byte loads)
+template <int U, int F>
+__device__ __forceinline__ void f8w_load_b(F8wB& B, int s, const F8wPlan& P) {
+  const bool in = s < P.KT;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    B.b[U][F][h] = __builtin_amdgcn_raw_buffer_load_b128(
+        P.rb, in ? P.b[F] + (uint32_t)s * 2048u + 256u * U + 1024u * h : kOutOfRange, 0, 0);
+}
+
+// copies 2 Q, 2 Q + 1 of this wave for step s (8 rows x 128 B each)
+// (a chunk past K reads zeros: the bytes there belong to the next row and
+// could be NaN codes, which would survive a multiply by B's zero padding)
+template <int Q>
+__device__ __forceinline__ void f8w_copies(uint8_t* cst, int s, int wave, const F8wPlan& P) {
+#pragma unroll
+  for (int i = 2 * Q; i < 2 * Q + 2; ++i) {
+    const uint32_t off = P.a_g[i & 1] + (uint32_t)(i >> 1) * P.a_step + (uint32_t)s * f8w::kRow;
+    dma16(P.ra, cst + (8 * wave + i) * 1024,
+          s * f8w::kRow + P.a_kb[i & 1] < P.row_bytes ? off : kOutOfRange);
+  }
+}
+
+template <int Q>
+__device__ __forceinline__ void f8w_mma(const uintx4 (&x)[4][2], const F8wB& B, F8wAcc& acc) {
+  constexpr int U = Q >> 1, V = Q & 1;
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const intx8 bf = {(int)B.b[U][f][0][0], (int)B.b[U][f][0][1], (int)B.b[U][f][0][2],
+                      (int)B.b[U][f][0][3], (int)B.b[U][f][1][0], (int)B.b[U][f][1][1],
+                      (int)B.b[U][f][1][2], (int)B.b[U][f][1][3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const intx8 af = {(int)x[i][0][0], (int)x[i][0][1], (int)x[i][0][2], (int)x[i][0][3],
+                        (int)x[i][1][0], (int)x[i][1][1], (int)x[i][1][2], (int)x[i][1][3]};
+      acc[4 * V + i][f] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          bf, af, acc[4 * V + i][f], kFmtFP8, kFmtFP8, 0, kE8M0One, 0, kE8M0One);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void f8w_pin() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the quarter's LDS reads first
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
+// step s, in stage S = s % 4; B[S % 2] holds its B fragments, x[0] its
+// quarter-0 A fragments
+template <int S>
+__device__ __forceinline__ void f8w_step(int s, uint8_t* lds, F8wB (&B)[2], uintx4 (&x)[2][4][2],
+                                         int wave, const F8wPlan& P, F8wAcc& acc) {
+  constexpr int BC = S & 1, BN = 1 - BC;
+  const uint8_t* st = lds + S * f8w::kStage;
+  const uint8_t* nst = lds + ((S + 1) & 3) * f8w::kStage;
+  uint8_t* cst = lds + ((S + 3) & 3) * f8w::kStage;
+
+  f8w_read_a<1>(x[1], st, P);
+  f8w_mma<0>(x[0], B[BC], acc);
+  f8w_load_b<0, 0>(B[BN], s + 1, P);
+  f8w_copies<0>(cst, s + 3, wave, P);
+  f8w_pin<f8w::kOps>();
+  __builtin_amdgcn_sched_barrier(0);
+
+  f8w_read_a<2>(x[0], st, P);
+  f8w_mma<1>(x[1], B[BC], acc);
+  f8w_load_b<0, 1>(B[BN], s + 1, P);
+  f8w_copies<1>(cst, s + 3, wave, P);
+  f8w_pin<f8w::kOps>();
+  __builtin_amdgcn_sched_barrier(0);
+
+  f8w_read_a<3>(x[1], st, P);
+  f8w_mma<2>(x[0], B[BC], acc);
+  f8w_load_b<1, 0>(B[BN], s + 1, P);
+  f8w_copies<2>(cst, s + 3, wave, P);
+  f8w_pin<f8w::kOps>();
+  QG_WAIT_VM_LGKM_BARRIER(f8w::kCopyWait);
+
+  f8w_read_a<0>(x[0], nst, P);
+  f8w_mma<3>(x[1], B[BC], acc);
+  f8w_load_b<1, 1>(B[BN], s + 1, P);
+  f8w_copies<3>(cst, s + 3, wave, P);
+  f8w_pin<f8w::kOps>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// FP8, M and N > 128, at least two 128-element K tiles (K % 16 == 0).
+__global__ __launch_bounds__(256) void f8w_kernel(const uint8_t* __restrict__ a,
+                                                  const uint8_t* __restrict__ bp,
+                                                  const float* __restrict__ scale_a,
+                                                  const float* __restrict__ scale_b,
+                                                  uint16_t* __restrict__ c, PipeArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[f8w::kLds];
+  static_assert(f8w::kLds >= kCTileBytes, "the C tile reuses the stage memory");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  const int T = g.tiles_m * g.tiles_n;
+  const int bid = blockIdx.x;
+  const int id = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  constexpr int GM = 4;
+  const int group = id / (GM * g.tiles_n);
+  const int first_m = group * GM;
+  const int gsize = min(g.tiles_m - first_m, GM);
+  const int in_group = id - group * GM * g.tiles_n;
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
+  const int m0 = tm * kBig;
+  const int cg0 = tn * (kBig / 16);
+
+  F8wPlan P;
+  P.ra = make_rsrc(a, g.a_bytes);
+  P.rb = make_rsrc(bp, g.w_bytes);
+  P.row_bytes = g.K;
+  P.KT = g.KT;
+  {
+    const int cl = lane & 31, j = lane >> 5, par = (lane >> 4) & 1;
+    P.rd_a = cl * f8w::kRow + 16 * ((4 * j) ^ mxw::swz(cl));
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      P.b[f] = (uint32_t)(cg0 + 4 * wave + 2 * f + par) * (uint32_t)g.KT * 2048u + 512u * j +
+               16u * (lane & 15);
+    // copy i covers rows 64 wave + 8 i + [0, 8); copies i and i + 2 differ by
+    // 16 rows and share the chunk swizzle
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 64 * wave + 8 * i + (lane >> 3);
+      const int ch = (lane & 7) ^ mxw::swz(r);
+      P.a_g[i] = (uint32_t)(m0 + r) * (uint32_t)P.row_bytes + 16u * ch;
+      P.a_kb[i] = 16 * ch;
+    }
+    P.a_step = 16u * (uint32_t)P.row_bytes;
+  }
+
+  F8wAcc acc;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][f][e] = 0.f;
+
+  // prologue: the B of step 0, then the copies of steps 0, 1, 2.  The B
+  // loads go first so that, as in the loop, at least 14 memory instructions
+  // follow each of them: the compiler's waits for these registers at the
+  // loop head take the smaller count of the two paths into it.
+  F8wB B[2];
+  f8w_load_b<0, 0>(B[0], 0, P);
+  f8w_load_b<0, 1>(B[0], 0, P);
+  f8w_load_b<1, 0>(B[0], 0, P);
+  f8w_load_b<1, 1>(B[0], 0, P);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    uint8_t* cst = smem + s * f8w::kStage;
+    f8w_copies<0>(cst, s, wave, P);
+    f8w_copies<1>(cst, s, wave, P);
+    f8w_copies<2>(cst, s, wave, P);
+    f8w_copies<3>(cst, s, wave, P);
+  }
+  QG_WAIT_VM_BARRIER(16);   // B and step 0's copies landed
+  uintx4 x[2][4][2];
+  f8w_read_a<0>(x[0], smem, P);
+  // nothing of the lgkm counter left pending on the way into the loop (the
+  // kernel-argument loads count there too, out of order), so the compiler's
+  // wait at the loop head is the loop's own
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+
+  const int KS = g.KT;   // one step per 128-element K tile
+  int s = 0;
+  for (; s + 4 <= KS; s += 4) {
+    f8w_step<0>(s, smem, B, x, wave, P, acc);
+    f8w_step<1>(s + 1, smem, B, x, wave, P, acc);
+    f8w_step<2>(s + 2, smem, B, x, wave, P, acc);
+    f8w_step<3>(s + 3, smem, B, x, wave, P, acc);
+  }
+  if (s < KS) f8w_step<0>(s, smem, B, x, wave, P, acc);
+  if (s + 1 < KS) f8w_step<1>(s + 1, smem, B, x, wave, P, acc);
+  if (s + 2 < KS) f8w_step<2>(s + 2, smem, B, x, wave, P, acc);
+
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const float sc = (*scale_a) * (*scale_b);
+#pragma unroll
+  for (int fm = 0; fm < 8; ++fm)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 32 * fm + (lane & 31);
+        const int col = 64 * wave + 32 * f + 8 * q + 4 * (lane >> 5);
+        const uintx2 v = {pack_bf16x2(acc[fm][f][4 * q] * sc, acc[fm][f][4 * q + 1] * sc),
+                          pack_bf16x2(acc[fm][f][4 * q + 2] * sc, acc[fm][f][4 * q + 3] * sc)};
+        *reinterpret_cast<uintx2*>(smem + mxw_c_offset(row, col)) = v;
+      }
+  __syncthreads();
+  const bool vec = (g.N & 7) == 0;
+  const int n0 = cg0 * 16;
+#pragma unroll 4
+  for (int jj = 0; jj < kCTileBytes / 16 / 256; ++jj) {
+    const int q = (int)threadIdx.x + 256 * jj;
+    const int row = q >> 5, ch = q & 31;
+    const int gm = m0 + row, gn = n0 + 8 * ch;
+    if (gm >= g.M || gn >= g.N) continue;
+    const uintx4 v = *reinterpret_cast<const uintx4*>(smem + row * (kBig * 2) +
+                                                      16 * (ch ^ (row & 15)));
+    uint16_t* dst = c + (int64_t)gm * g.N + gn;
+    if (vec) {
+      *reinterpret_cast<uintx4*>(dst) = v;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (gn + t < g.N) dst[t] = (uint16_t)(v[t >> 1] >> (16 * (t & 1)));
+    }
+  }
+}
+
+hipError_t launch_f8w(const void* a, const void* bp, const float* sa, const float* sb, void* c,
+                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const PackGeom pg = pack_geom(4, K, N);
+  PipeArgs g;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.KT = (int)pg.kt;
+  g.KS = (int)pg.kt;
+  g.CG = (int)pg.cg;
+  g.tiles_m = (int)cdiv(M, kBig);
+  g.tiles_n = (int)cdiv(N, kBig);
+  g.a_bytes = (uint32_t)(M * K);
+  g.w_bytes = (uint32_t)pg.codes;
+  g.asc_bytes = 0;
+  g.wsc_bytes = 0;
+  hipLaunchKernelGGL(f8w_kernel, dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(bp), sa, sb,
+                     static_cast<uint16_t*>(c), g);
   return hipGetLastError();
 }
 
@@ -1375,9 +1579,7 @@ hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const vo
     return launch_tiles<true, 4, 4>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
   }
   if (fmt == 4) {
-    if (big)
-      return launch_pipe<Fp8Pipe>(a, a_e8m0, w_packed, scale_a, scale_b, nullptr, c, M, N, K,
-                                  stream);
+    if (big) return launch_f8w(a, w_packed, scale_a, scale_b, c, M, N, K, stream);
     return launch_tiles<false, 4, 4>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
   }
   return hipErrorInvalidValue;
