@@ -382,6 +382,45 @@ def read_ceiling(nbytes, reps=60, grids=(256, 512, 1024, 2048)):
             "kernel": "read_probe_kernel (qgemm_read_probe)"}
 
 
+def mfma_ceiling(dtype, launches=10, workgroups=256):
+    """The practical rate of the scaled 32x32x64 matrix instruction on this GPU:
+    the library's matrix-pipe probe (register operands of random bytes, no
+    other instruction in its loop) over a graph of `launches` launches of about
+    a millisecond each, timed like the GEMM calls."""
+    import torch
+    import bit_quantized_gemm_qgemm_amd as qg
+
+    fp4 = dtype == "fp4"
+    iters = 4096 if fp4 else 2048
+    g = torch.Generator(device="cuda").manual_seed(0)
+    ops = torch.randint(0, 256, (272 * 256 * workgroups,), generator=g, dtype=torch.uint8,
+                        device="cuda")
+    if not fp4:
+        ops[(ops & 0x7F) == 0x7F] -= 1           # no e4m3 NaN codes
+    sink = torch.empty(workgroups, dtype=torch.float32, device="cuda")
+    fmt = "mxfp4" if fp4 else "fp8"
+    qg.qgemm_mfma_probe(fmt, ops, iters, sink, workgroups)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for _ in range(launches):
+            qg.qgemm_mfma_probe(fmt, ops, iters, sink, workgroups)
+    gr.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / launches
+    flops = workgroups * 4 * iters * 16 * 131072
+    tf = flops / t / 1e12
+    return {"TFLOPS": round(tf, 1), "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS[dtype], 4),
+            "us_per_launch": round(t * 1e6, 1), "iters": iters, "workgroups": workgroups,
+            "kernel": "mfma_probe_kernel (qgemm_mfma_probe)"}
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on the host
 # ---------------------------------------------------------------------------
@@ -594,6 +633,11 @@ def run(name, steps, warmup, with_cpu, use_graph, with_ceiling=True):
         # the same weight byte count read by a plain streaming-read kernel
         ceiling = read_ceiling(setup.calls[dom][2])
         roof["frac_of_read_ceiling"] = round(ceiling["us"] / (per_call[dom] * 1e6), 4)
+    mceiling = None
+    if not decode and with_ceiling and setup.dtype in ("fp4", "fp8"):
+        # the matrix instruction's own practical rate on this GPU
+        mceiling = mfma_ceiling(setup.dtype)
+        roof["frac_of_mfma_ceiling"] = round(achieved / mceiling["TFLOPS"], 4)
     cfg = {"workload": name, "format": setup.fmt, "M": list(setup.ms), "N": setup.n,
            "K": setup.k, "weight_copies": len(setup.copies),
            "timing": "hip-graph replay" if use_graph else "eager launches"}
@@ -617,6 +661,8 @@ def run(name, steps, warmup, with_cpu, use_graph, with_ceiling=True):
     }
     if ceiling is not None:
         line["read_ceiling"] = ceiling
+    if mceiling is not None:
+        line["mfma_ceiling"] = mceiling
     if with_cpu:
         line["cpu_baseline"] = cpu_baseline(name)
     del setup
@@ -642,6 +688,9 @@ def config_summary(line):
     if "read_ceiling" in line:
         out["read_ceiling"] = line["read_ceiling"]
         out["frac_of_read_ceiling"] = r["frac_of_read_ceiling"]
+    if "mfma_ceiling" in line:
+        out["mfma_ceiling"] = line["mfma_ceiling"]
+        out["frac_of_mfma_ceiling"] = r["frac_of_mfma_ceiling"]
     return out
 
 

@@ -51,6 +51,7 @@ _SIGNATURES = [
     ("qgemm_fp8_act", ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     ("qgemm_fp8_act_noalloc", ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     ("qgemm_read_probe", ctypes.c_int, [_P, _I64, _P, _I64, _P]),
+    ("qgemm_mfma_probe", ctypes.c_int, [ctypes.c_int, _P, _I64, _P, _I64, _P]),
 ]
 
 # largest M * K that qgemm_fp8_act_noalloc accepts (its fixed scratch)
@@ -412,3 +413,16 @@ def qgemm_read_probe(buf, sink, workgroups):
         raise ValueError("sink needs one entry per workgroup")
     _check(lib().qgemm_read_probe(_ptr(buf), buf.numel(), _ptr(sink), int(workgroups),
                                   _stream(buf)), "qgemm_read_probe")
+
+
+def qgemm_mfma_probe(fmt, operands, iters, sink, workgroups):
+    """Back-to-back scaled matrix instructions on register operands loaded from
+    the uint8 device tensor `operands` (272 bytes per thread); sink is a
+    float32 device tensor with at least `workgroups` entries."""
+    _need(operands, torch.uint8, 1, "operands")
+    _need(sink, torch.float32, 1, "sink")
+    if operands.numel() < 272 * 256 * workgroups or sink.numel() < workgroups:
+        raise ValueError("operands needs 272 bytes per thread, sink one entry per workgroup")
+    _check(lib().qgemm_mfma_probe(int(FORMATS.get(fmt, fmt)), _ptr(operands), int(iters),
+                                  _ptr(sink), int(workgroups), _stream(operands)),
+           "qgemm_mfma_probe")

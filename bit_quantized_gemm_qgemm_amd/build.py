@@ -20,7 +20,7 @@ LIB_NAME = "libqgemm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["decode_gemm.hip", "tile_gemm.hip", "quantize.hip", "prepack.hip", "read_probe.hip",
+SOURCES = ["decode_gemm.hip", "tile_gemm.hip", "quantize.hip", "prepack.hip", "probes.hip",
            "api.cpp"]
 
 HIPCC_FLAGS = [

@@ -439,4 +439,16 @@ int qgemm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int64_t wor
   return launched(qgemm::launch_read_probe(buf, bytes, sink, workgroups, as_stream(stream)));
 }
 
+int qgemm_mfma_probe(int fmt, const void* operands, int64_t iters, float* sink,
+                     int64_t workgroups, void* stream) {
+  if (fmt != QGEMM_MXFP4 && fmt != QGEMM_FP8) return QGEMM_ERR_FORMAT;
+  if (iters < 0 || workgroups < 1 || workgroups > (1 << 20)) return QGEMM_ERR_SHAPE;
+  if (!operands || !sink) return QGEMM_ERR_NULL;
+  if (!aligned(operands, 16) || !aligned(sink, 4)) return QGEMM_ERR_ALIGN;
+  int st = check_device();
+  if (st != QGEMM_OK) return st;
+  return launched(qgemm::launch_mfma_probe(fmt == QGEMM_MXFP4, operands, iters, sink, workgroups,
+                                           as_stream(stream)));
+}
+
 }  // extern "C"

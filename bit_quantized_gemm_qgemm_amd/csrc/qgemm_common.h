@@ -196,6 +196,11 @@ hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const vo
 // `workgroups` workgroups; one word per workgroup goes to sink.
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int64_t workgroups,
                              hipStream_t stream);
+// Back-to-back scaled 32 x 32 x 64 matrix instructions (FP4 or FP8 operands)
+// on register-held data: `iters` rounds of 16 per wave; ops holds 272 bytes
+// per thread (workgroups x 256 threads); one float per workgroup to sink.
+hipError_t launch_mfma_probe(bool fp4, const void* ops, int64_t iters, float* sink,
+                             int64_t workgroups, hipStream_t stream);
 
 // ---- device helpers --------------------------------------------------------
 

@@ -304,6 +304,22 @@ int qgemm_w8a16_grouped(const void* x, const void* w_packed, void* y, int64_t M,
 int qgemm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int64_t workgroups,
                      void* stream);
 
+/*
+ * qgemm_mfma_probe -- measurement reference, not part of any GEMM: the
+ * practical rate of the scaled matrix instruction that the MXFP4 and FP8 tile
+ * GEMMs are built on (MXFP4 page, section 2: the block dot product with the
+ * exponent-add scale product in one step).  Each of `workgroups` workgroups
+ * (256 threads, 4 waves) loads register operands from `operands` (272 bytes
+ * per thread, 16-byte aligned: random bytes give operand data like the
+ * GEMMs'), then issues iters x 16 v_mfma_scale_f32_32x32x64_f8f6f4 per wave
+ * with nothing else in the loop (fmt QGEMM_MXFP4: E2M1 operands and E8M0
+ * scales 120..127; QGEMM_FP8: e4m3 operands, unit scales) and writes one
+ * float per workgroup to sink[workgroups].  Flops per launch =
+ * workgroups * 4 * iters * 16 * 131072.  1 <= workgroups <= 2^20.
+ */
+int qgemm_mfma_probe(int fmt, const void* operands, int64_t iters, float* sink,
+                     int64_t workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
