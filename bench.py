@@ -39,9 +39,13 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 ROTATE_BYTES = 600e6
 CALIB_BYTES = 256 * 1024 * 1024
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# GEMM kernel name -> the source file whose hash keys its traffic record
 KERNEL_SOURCES = {
-    "decode": "bit_quantized_gemm_qgemm_amd/csrc/decode_gemm.hip",
-    "tile": "bit_quantized_gemm_qgemm_amd/csrc/tile_gemm.hip",
+    "decode_gemm_kernel": "bit_quantized_gemm_qgemm_amd/csrc/decode_gemm.hip",
+    "tile_gemm_kernel": "bit_quantized_gemm_qgemm_amd/csrc/tile_gemm.hip",
+    "pipe256_kernel": "bit_quantized_gemm_qgemm_amd/csrc/tile_wo256.hip",
+    "mxw_kernel": "bit_quantized_gemm_qgemm_amd/csrc/tile_mx256.hip",
+    "f8w_kernel": "bit_quantized_gemm_qgemm_amd/csrc/tile_mx256.hip",
 }
 
 WORKLOADS = {
@@ -83,8 +87,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash(kind):
-    with open(os.path.join(ROOT, KERNEL_SOURCES[kind]), "rb") as f:
+def source_hash(kernel):
+    """Hash prefix of the source file that defines the GEMM kernel named in
+    `kernel` (a bench label)."""
+    src = next(v for k, v in KERNEL_SOURCES.items() if k in kernel)
+    with open(os.path.join(ROOT, src), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -573,16 +580,16 @@ def cpu_baseline(name, budget_s=10.0):
 
 # ---------------------------------------------------------------------------
 
-def traffic_for(kind, kernel):
+def traffic_for(kernel):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None when
     missing or taken on a different version of the kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
         ent = data.get(kernel)
-        if ent and ent.get("source_sha") == source_hash(kind):
+        if ent and ent.get("source_sha") == source_hash(kernel):
             return ent["bytes_per_launch"]
-    except (OSError, ValueError, KeyError):
+    except (OSError, ValueError, KeyError, StopIteration):
         pass
     return None
 
@@ -613,8 +620,7 @@ def run(name, steps, warmup, with_cpu, use_graph, with_ceiling=True):
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}
     kernel = kernel_name(setup, setup.ms[dom])
-    roof["traffic"] = traffic_for("decode" if kernel.startswith("decode_gemm_kernel") else "tile",
-                                  kernel)
+    roof["traffic"] = traffic_for(kernel)
     roof["kernel"] = kernel
     roof["avg_launch_us"] = round(per_call[dom] * 1e6, 3)
     roof["step_avg_launch_us"] = round(dev_s / (steps * len(setup.calls)) * 1e6, 3)

@@ -20,7 +20,8 @@ LIB_NAME = "libqgemm.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["decode_gemm.hip", "tile_gemm.hip", "quantize.hip", "prepack.hip", "probes.hip",
+SOURCES = ["decode_gemm.hip", "tile_gemm.hip", "tile_wo256.hip", "tile_mx256.hip", "quantize.hip",
+           "prepack.hip", "probes.hip",
            "api.cpp"]
 
 HIPCC_FLAGS = [

@@ -191,6 +191,14 @@ hipError_t launch_weight_only_tile_grouped(int fmt, const void* x, const void* w
 hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const void* w_packed,
                             const float* scale_a, const float* scale_b, void* c,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+// Its 256 x 256 kernels (M and N > 128, operands within pipe_fits): MXFP4
+// with K % 128 == 0 and at least two 256-element K tiles, FP8 with at least
+// two 128-element K tiles.
+hipError_t launch_mxfp4_256(const void* a, const void* a_e8m0, const void* w_packed, void* c,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_fp8_256(const void* a, const void* b_packed, const float* scale_a,
+                          const float* scale_b, void* c, int64_t M, int64_t N, int64_t K,
+                          hipStream_t stream);
 
 // Streaming read of `bytes` bytes (a multiple of 16, buf 16-byte aligned) by
 // `workgroups` workgroups; one word per workgroup goes to sink.
