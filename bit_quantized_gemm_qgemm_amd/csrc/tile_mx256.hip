@@ -69,9 +69,11 @@ __device__ __forceinline__ void mx_copy_out(const uint8_t* smem, uint16_t* __res
 //
 // Per quarter u of a step (one 64-element K slice, blocks u and 4 + u of the
 // step; lane l feeds chunk 4 (l >> 5) + u of its row or column):
-//   - LDS reads of the next quarter's 8 A fragments (and in quarter 3, after
-//     the barrier, those of quarter 0 of step s + 1 plus its A scales);
-//   - 16 matrix instructions, each beside one memory instruction: the 2 W
+//   - 16 matrix instructions;
+//   - between the first four of them, the LDS reads of the next quarter's 8 A
+//     fragments (in quarter 3, after the barrier, those of quarter 0 of step
+//     s + 1 plus its A scales);
+//   - beside the first five or six, one memory instruction each: the 2 W
 //     fragment loads and the W scale dword of the same quarter of step
 //     s + WB - 1, then this quarter's share of the copies of step s + 3
 //     (8 A copies of 8 rows x 128 B, 2 A-scale copies of 32 rows x 8 B);
@@ -85,9 +87,12 @@ __device__ __forceinline__ void mx_copy_out(const uint8_t* smem, uint16_t* __res
 // kernel: the matrix pipe 57% busy at 1.76-1.82 GHz, and the clock falls as
 // that share rises (1.95 GHz at 45% busy with K = 4096, 1.70 GHz at 63% with
 // K = 16384), so part of the remaining gap is the power the operand traffic
-// and the matrix pipe draw together.  A persistent form (one workgroup per
-// CU, the copy ring running across tile boundaries, results stored straight
-// from the accumulators) took the same kernel time and was not kept.
+// and the matrix pipe draw together.  Builds with the A copies, or the W
+// loads, left out ran about 10% faster with the matrix pipe still 56-59%
+// busy, so most of the idle share is in the issue schedule of the one wave
+// per SIMD rather than in operand traffic.  A persistent form (one workgroup
+// per CU, the copy ring running across tile boundaries, results stored
+// straight from the accumulators) took the same kernel time and was not kept.
 namespace mxw {
 constexpr int kRow = 128;                     // A bytes per row and step
 constexpr int kAStage = kBig * kRow;          // 32 KB
@@ -184,15 +189,19 @@ __device__ __forceinline__ void mxw_mma(const uintx4 (&x)[8], const MxwW& W,
   mxw_mma_f<U, 1>(x, W, sa, sw, acc);
 }
 
-// the quarter's LDS reads first, then one matrix instruction beside one
-// memory instruction, N times
+// The quarter's 16 matrix instructions, the first N each followed by one
+// global memory instruction and the first four by a quarter of its R LDS
+// reads.  A 32 x 32 x 64 FP4 instruction keeps the matrix pipe busy for only
+// 32 cycles, so the reads go out between matrix instructions rather than as
+// a burst ahead of them (measured at M = N = K = 8192: 255-260 us against
+// 265-267 us with the burst).
 template <int N, int R = 8>
 __device__ __forceinline__ void mxw_pin() {
-  __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
+  for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if (i < 4) __builtin_amdgcn_sched_group_barrier(0x100, R / 4, 0);
+    if (i < N) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
 }
 
@@ -400,6 +409,15 @@ hipError_t launch_mxw(const void* a, const void* a_sc, const void* wp, void* c, 
 // 4 v + 3) to keep the A registers at two quarters' worth.  B is the first
 // operand, so the accumulators hold C transposed and the epilogue writes
 // 8 bytes per lane; s_a * s_b multiplies the fp32 result.
+//
+// Counters at M = N = K = 8192: the matrix pipe 71% busy at 1.86 GHz.  Builds
+// with the A copies, or the B loads, left out ran 17% and 10% faster, at 2.16
+// and 2.05 GHz with the pipe as busy as before: under the power limit, moving
+// operands into the CU costs clock.  The bytes per step are already the
+// least a workgroup can move (256 x 256 is the largest output tile whose fp32
+// accumulators fit the register file), and copying A through registers
+// (global load, then LDS store) instead of the buffer-to-LDS path measured
+// the same.
 namespace f8w {
 constexpr int kRow = 128;                     // A bytes per row and step
 constexpr int kStage = kBig * kRow;           // 32 KB
@@ -482,13 +500,17 @@ __device__ __forceinline__ void f8w_mma(const uintx4 (&x)[4][2], const F8wB& B, 
   }
 }
 
+// The quarter's 8 matrix instructions, the first N each followed by one
+// global memory instruction and the first four by two of its 8 LDS reads
+// (spread out as in the MXFP4 kernel: 394-400 us against 413-415 us with the
+// reads as a burst ahead of the quarter, M = N = K = 8192, same box).
 template <int N>
 __device__ __forceinline__ void f8w_pin() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the quarter's LDS reads first
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
+  for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if (i < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if (i < N) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
 }
 
