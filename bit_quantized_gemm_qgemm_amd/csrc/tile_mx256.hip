@@ -107,18 +107,19 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 }  // namespace mxw
 
 struct MxwPlan {
-  __amdgpu_buffer_rsrc_t ra, rsa, rw, rsw;
+  __amdgpu_buffer_rsrc_t rsa;
+  const uint8_t *a_base, *w_base, *wsc_base;   // A codes, W codes, W scales
+  uint32_t a_n, w_n, wsc_n;     // their sizes in bytes
   int rd_a[4];          // LDS: A chunk of quarter u within a stage (fragment fm: + 4096 fm)
   int rd_sa;            // LDS: the lane's row's scale dword (fragment fm: + 256 fm)
   uint32_t w[2];        // W fragment f of step 0 (step s: + 2048 s; quarter u: + 256 u)
   uint32_t ws;          // W scale dword of step 0 (step s: + 1024 s; quarter u: + 128 u)
   uint32_t a_g[8];      // A copy i of step 0 (step s: + 128 s)
-  int a_kb[8];          // its chunk's byte within a step
   uint32_t sa_g[2];     // A scale copy i of step 0 (step s: + 8 s)
   int sa_kb;
   int a_lds[8], sa_lds[2];
   uint32_t shb;         // 8 * ((lane >> 4) & 1): the W scale byte of the lane's tile
-  int row_bytes, sc_cols, KT;
+  int row_bytes, sc_cols;
 };
 
 struct MxwW {
@@ -142,26 +143,38 @@ __device__ __forceinline__ void mxw_read_sa(uint32_t (&sa)[8], const uint8_t* st
     sa[fm] = *reinterpret_cast<const uint32_t*>(st + P.rd_sa + fm * 256);
 }
 
+// A buffer resource over p + off .. p + n (empty once off >= n): the step
+// offset lives in the resource, so the lane offsets stay constant and the
+// range check still bounds every read
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_from(const uint8_t* p, uint32_t n,
+                                                           uint32_t off) {
+  // readfirstlane: the clamped difference would otherwise become a VALU
+  // saturating subtract and the resource a per-lane value
+  const uint32_t left = __builtin_amdgcn_readfirstlane(n > off ? n - off : 0u);
+  return make_rsrc(p + off, left);
+}
+
+// (a step past the last K tile reads the next column group's tiles, or
+// zeros past the end; those registers are never used)
 template <int U>
 __device__ __forceinline__ void mxw_load_w(MxwW& W, int s, const MxwPlan& P) {
-  const bool in = s < P.KT;
+  const __amdgpu_buffer_rsrc_t rw = rsrc_from(P.w_base, P.w_n, (uint32_t)s * 2048u);
+  const __amdgpu_buffer_rsrc_t rsw = rsrc_from(P.wsc_base, P.wsc_n, (uint32_t)s * 1024u);
 #pragma unroll
   for (int f = 0; f < 2; ++f)
-    W.b[U][f] = __builtin_amdgcn_raw_buffer_load_b128(
-        P.rw, in ? P.w[f] + (uint32_t)s * 2048u + 256u * U : kOutOfRange, 0, 0);
-  W.s[U] = __builtin_amdgcn_raw_buffer_load_b32(
-      P.rsw, in ? P.ws + (uint32_t)s * 1024u + 128u * U : kOutOfRange, 0, 0);
+    W.b[U][f] = __builtin_amdgcn_raw_buffer_load_b128(rw, P.w[f] + 256u * U, 0, 0);
+  W.s[U] = __builtin_amdgcn_raw_buffer_load_b32(rsw, P.ws + 128u * U, 0, 0);
 }
 
 // quarter U's share of the copies of step s into stage memory cst
+// (in a last K tile of 128 elements, chunks 4-7 of a row copy the next row's
+// first codes: they meet W's zero padding, and E2M1 has no NaN or infinity,
+// so their products are exactly zero)
 template <int U>
 __device__ __forceinline__ void mxw_copies(uint8_t* cst, int s, const MxwPlan& P) {
+  const __amdgpu_buffer_rsrc_t ra = rsrc_from(P.a_base, P.a_n, (uint32_t)s * mxw::kRow);
 #pragma unroll
-  for (int i = 2 * U; i < 2 * U + 2; ++i) {
-    const int kb = s * mxw::kRow + P.a_kb[i];
-    dma16(P.ra, cst + P.a_lds[i], kb < P.row_bytes ? P.a_g[i] + (uint32_t)s * mxw::kRow
-                                                   : kOutOfRange);
-  }
+  for (int i = 2 * U; i < 2 * U + 2; ++i) dma16(ra, cst + P.a_lds[i], P.a_g[i]);
   if constexpr (U < 2) {
     const bool in = 8 * s + P.sa_kb < P.sc_cols;
     dma4(P.rsa, cst + mxw::kAStage + P.sa_lds[U], in ? P.sa_g[U] + 8u * s : kOutOfRange);
@@ -265,13 +278,15 @@ __global__ __launch_bounds__(256) void mxw_kernel(const uint8_t* __restrict__ a,
   const int cg0 = to.cg0;
 
   MxwPlan P;
-  P.ra = make_rsrc(a, g.a_bytes);
   P.rsa = make_rsrc(a_sc, g.asc_bytes);
-  P.rw = make_rsrc(wp, g.w_bytes);
-  P.rsw = make_rsrc(w_sc, g.wsc_bytes);
+  P.a_base = a;
+  P.w_base = wp;
+  P.wsc_base = w_sc;
+  P.a_n = g.a_bytes;
+  P.w_n = g.w_bytes;
+  P.wsc_n = g.wsc_bytes;
   P.row_bytes = g.K / 2;
   P.sc_cols = g.K / 32;
-  P.KT = g.KT;
   {
     const int cl = lane & 31, j = lane >> 5, par = (lane >> 4) & 1;
 #pragma unroll
@@ -289,7 +304,6 @@ __global__ __launch_bounds__(256) void mxw_kernel(const uint8_t* __restrict__ a,
       const int q = 8 * wave + i;
       const int r = 8 * q + (lane >> 3);
       const int ch = (lane & 7) ^ mxw::swz(r);
-      P.a_kb[i] = 16 * ch;
       P.a_g[i] = (uint32_t)(m0 + r) * (uint32_t)P.row_bytes + 16u * ch;
       P.a_lds[i] = q * 1024;
     }
@@ -430,14 +444,16 @@ constexpr int kCopyWait = 16 + 3 * kOps;
 }  // namespace f8w
 
 struct F8wPlan {
-  __amdgpu_buffer_rsrc_t ra, rb;
+  __amdgpu_buffer_rsrc_t ra;
+  const uint8_t* b_base;   // packed B and its size in bytes
+  uint32_t b_n;
   int rd_a;             // LDS: A chunk 4 (l >> 5) of the lane's row (XOR 16 (2u + h))
   uint32_t b[2];        // B fragment f of step 0 (step s: + 2048 s; instruction u: + 256 u,
                         // half h: + 1024 h)
   uint32_t a_g[2];      // A copies i = 0, 1 of step 0; copy i: + (i >> 1) * a_step
   int a_kb[2];          // their chunk's byte within a step
   uint32_t a_step;
-  int row_bytes, KT;
+  int row_bytes;
 };
 
 struct F8wB {
@@ -459,14 +475,15 @@ __device__ __forceinline__ void f8w_read_a(uintx4 (&x)[4][2], const uint8_t* st,
                                                  (4 * V + i) * 4096);
 }
 
-// B fragment f of instruction U of step s (two 16-byte loads)
+// B fragment f of instruction U of step s (two 16-byte loads; a step past
+// the last K tile reads the next column group's tiles, or zeros past the
+// end, into registers that are never used)
 template <int U, int F>
 __device__ __forceinline__ void f8w_load_b(F8wB& B, int s, const F8wPlan& P) {
-  const bool in = s < P.KT;
+  const __amdgpu_buffer_rsrc_t rb = rsrc_from(P.b_base, P.b_n, (uint32_t)s * 2048u);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    B.b[U][F][h] = __builtin_amdgcn_raw_buffer_load_b128(
-        P.rb, in ? P.b[F] + (uint32_t)s * 2048u + 256u * U + 1024u * h : kOutOfRange, 0, 0);
+    B.b[U][F][h] = __builtin_amdgcn_raw_buffer_load_b128(rb, P.b[F] + 256u * U + 1024u * h, 0, 0);
 }
 
 // copies 2 Q, 2 Q + 1 of this wave for step s (8 rows x 128 B each)
@@ -570,9 +587,9 @@ __global__ __launch_bounds__(256) void f8w_kernel(const uint8_t* __restrict__ a,
 
   F8wPlan P;
   P.ra = make_rsrc(a, g.a_bytes);
-  P.rb = make_rsrc(bp, g.w_bytes);
+  P.b_base = bp;
+  P.b_n = g.w_bytes;
   P.row_bytes = g.K;
-  P.KT = g.KT;
   {
     const int cl = lane & 31, j = lane >> 5, par = (lane >> 4) & 1;
     P.rd_a = cl * f8w::kRow + 16 * ((4 * j) ^ mxw::swz(cl));
