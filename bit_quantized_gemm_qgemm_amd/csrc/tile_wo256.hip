@@ -77,24 +77,19 @@ __device__ __forceinline__ int a16_lane_offset(int wm, int lane, int swz) {
 }
 
 // ---- epilogue: the 256 x 256 output tile goes through LDS -----------------
-// Each lane rounds its scaled accumulators (hardware RNE conversion) into a
-// row-major [256][512 B] tile in LDS; then the workgroup copies it out with
-// 16-byte row-contiguous stores.  16-byte chunk k of row r sits in slot
+// Each lane rounds its scaled accumulators to fp16 (round to nearest even)
+// into a row-major [256][512 B] tile in LDS; then the workgroup copies it out
+// with 16-byte row-contiguous stores.  16-byte chunk k of row r sits in slot
 // k ^ (((r >> 2) & 3) << 2): the rows that one 2-byte write instruction
-// touches (4 apart for 16 x 16 fragments, 4 apart for 32 x 32) land in
-// different banks.
+// touches (4 apart in a 16 x 16 fragment) land in different banks.
 __device__ __forceinline__ int c_tile_offset(int row, int col) {
   return row * (kBig * 2) + 16 * ((col >> 3) ^ (((row >> 2) & 3) << 2)) + 2 * (col & 7);
 }
 
-template <bool F16_OUT>
-__device__ __forceinline__ uint16_t round_out(float v) {
-  if constexpr (F16_OUT) return f32_to_f16_bits(v);
-  else return __builtin_bit_cast(uint16_t, (__bf16)v);
-}
-
 // 16 x 16 accumulators: lane holds rows 4 (lane >> 4) + i, column lane & 15.
-template <bool F16_OUT, bool COL_SCALE = F16_OUT>
+// COL_SCALE: multiply by the column's fp16 scale (per-column formats), else
+// by the per-tensor o.s.
+template <bool COL_SCALE>
 __device__ __forceinline__ void stage16(const floatx4 (&acc)[8][8], uint8_t* ct, const PipeOut& o,
                                         int n0, int wm, int wn, int lane) {
 #pragma unroll
@@ -111,7 +106,7 @@ __device__ __forceinline__ void stage16(const floatx4 (&acc)[8][8], uint8_t* ct,
       for (int i = 0; i < 4; ++i) {
         const int row = wm * 128 + fm * 16 + 4 * (lane >> 4) + i;
         *reinterpret_cast<uint16_t*>(ct + c_tile_offset(row, col)) =
-            round_out<F16_OUT>(acc[fm][fn][i] * s);
+            f32_to_f16_bits(acc[fm][fn][i] * s);
       }
   }
 }
@@ -285,7 +280,7 @@ struct F16Pipe {
   }
   __device__ __forceinline__ static void stage(const Acc& acc, uint8_t* ct, const PipeOut& o,
                                                int n0, int wm, int wn, int lane) {
-    stage16<true, NGT == 0 && WFMT != 7>(acc, ct, o, n0, wm, wn, lane);
+    stage16<NGT == 0 && WFMT != 7>(acc, ct, o, n0, wm, wn, lane);
   }
 };
 
