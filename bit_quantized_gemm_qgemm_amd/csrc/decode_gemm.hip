@@ -356,6 +356,32 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
   }
 }
 
+// Workgroup -> (column block, row block).  Workgroups are handed to the eight
+// XCDs round-robin by linear index, and each XCD has its own L2.  With one
+// row block the linear index is the column block.  With R > 1 row blocks,
+// the R row blocks of one column block take R consecutive slots of one XCD
+// (slot = index / 8, XCD = index % 8), so they start together and read the
+// same weight tiles through the same L2: the weight streams from HBM about
+// once instead of R times.  The column blocks are padded to a multiple of 8;
+// workgroups of the padding exit at once.
+struct DecodeBlock {
+  int cb, rb;
+  bool valid;
+};
+__device__ __forceinline__ DecodeBlock decode_block(int b, int CG, int G, int M, int rows) {
+  const int nrb = (M + rows - 1) / rows;
+  if (nrb <= 1) return DecodeBlock{b, 0, true};
+  const int slot = b >> 3;
+  const int cb = (slot / nrb) * 8 + (b & 7);
+  return DecodeBlock{cb, slot % nrb, cb * G < CG};
+}
+
+// Grid of the small-M kernel: see decode_block.
+inline unsigned decode_grid(int64_t CG, int G, int64_t M, int rows) {
+  const int64_t ncb = cdiv(CG, G), nrb = cdiv(M, rows);
+  return (unsigned)(nrb <= 1 ? ncb : cdiv(ncb, 8) * 8 * nrb);
+}
+
 // NGT > 0: grouped W4A16 / W8A16 (scales and zero points in the metadata
 // segment at wp + meta_offset; `scales` unused).
 // S: 16-row slabs per workgroup (rows m0 .. m0 + 16 S - 1).
@@ -384,8 +410,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int cg0 = blockIdx.x * G;
-  const int m0 = blockIdx.y * 16 * S;
+  const DecodeBlock blk = decode_block(blockIdx.x, CG, G, M, 16 * S);
+  if (!blk.valid) return;   // padding of the column blocks (whole workgroup)
+  const int cg0 = blk.cb * G;
+  const int m0 = blk.rb * 16 * S;
 
   DecodeAddr ad;
   ad.g = lane >> 4;
@@ -560,11 +588,17 @@ bool use_x_lds(int fmt, int64_t M, int nw, int s, int64_t KT) {
 // waves.  Above 16 rows a workgroup takes 2 (M <= 32) or 4 slabs, so each
 // weight tile is streamed and dequantized once for up to 64 rows instead of
 // once per 16; the activations of all slabs then share the register ring,
-// which caps G and the ring at two tiles.  INT4 keeps 2 slabs at every M:
-// with 4 slabs G could not exceed 3 and the grid of its wide weights grew to
-// 2.3 workgroups per CU (K = 8192, N = 28672, M = 64: 106 us against 68 us).
+// which caps G and the ring at two tiles.  The fp16-activation formats keep
+// 2 slabs at every M, staged through LDS (four would need 16 copy
+// instructions and 256 KB of slots, so they would load X directly): INT4
+// with 4 slabs could keep only 3 groups and its grid grew to 2.3 workgroups
+// per CU (K = 8192, N = 28672, M = 64: 106 us against 68 us); INT8 at
+// K = 4096, N = 11008 ran M = 64 / 96 / 128 in 24.2 / 43.8 / 44.0 us with
+// 4 direct slabs and 21.6 / 29.5 / 36.3 us with 2 staged ones.  The extra
+// row blocks cost little HBM traffic: decode_block puts the row blocks of
+// one column block on one XCD.
 DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
-  const int s = M <= 16 ? 1 : (M <= 32 || fmt == 1) ? 2 : 4;
+  const int s = M <= 16 ? 1 : (M <= 32 || fmt == 1 || fmt == 2) ? 2 : 4;
   // MXFP4 carries its scale words in the ring too: 2 groups with 4 slabs
   const int64_t gmax = s == 1 ? (fmt == 1 ? 8 : 4) : s == 2 ? (fmt == 1 ? 7 : 4) : fmt == 3 ? 2 : 3;
   int64_t g = cdiv(CG, 256);
@@ -581,7 +615,7 @@ template <int FMT, int G, int NW, int D, bool ELEMENTWISE, int S = 1, bool XL = 
 hipError_t launch_cfg(const void* x, const void* w, const void* s, const float* sa,
                       const float* sb, void* y, int64_t M, int64_t N, int64_t K, int64_t KT,
                       int64_t CG, hipStream_t stream, int64_t meta_offset = 0) {
-  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16 * S));
+  dim3 grid(decode_grid(CG, G, M, 16 * S));
   dim3 block(NW * kWave);
   hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, D, ELEMENTWISE, 0, S, XL>), grid, block, 0,
                      stream,
@@ -618,8 +652,10 @@ hipError_t launch_fmt_cfg(const DecodeConfig& c, const void* x, const void* w, c
   if constexpr (FMT == 1) {   // two INT4 slabs leave room for seven groups
     QG_GS(5, 2) QG_GS(6, 2) QG_GS(7, 2)
   }
-  QG_GS(1, 4) QG_GS(2, 4)
-  if constexpr (FMT != 3) {
+  if constexpr (FMT == 3 || FMT == 4) {   // four slabs: the e4m3 / E2M1 activations
+    QG_GS(1, 4) QG_GS(2, 4)
+  }
+  if constexpr (FMT == 4) {
     QG_GS(3, 4)
   }
 #undef QG_GS
@@ -659,7 +695,7 @@ template <int FMT, int NGT, int G, int NW, int S, bool XL>
 hipError_t launch_grouped_cfg(const void* x, const void* w, void* y, int64_t M, int64_t N,
                               int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
                               hipStream_t stream) {
-  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16 * S));
+  dim3 grid(decode_grid(CG, G, M, 16 * S));
   dim3 block(NW * kWave);
   hipLaunchKernelGGL((decode_gemm_kernel<FMT, G, NW, 2, false, NGT, S, XL>), grid, block, 0,
                      stream,
@@ -714,7 +750,7 @@ template <int G, int NW, int S, bool XL>
 hipError_t launch_nvfp4_cfg(const void* x, const void* w, const float* gs, void* y, int64_t M,
                             int64_t N, int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
                             hipStream_t stream) {
-  dim3 grid((unsigned)cdiv(CG, G), (unsigned)cdiv(M, 16 * S));
+  dim3 grid(decode_grid(CG, G, M, 16 * S));
   dim3 block(NW * kWave);
   hipLaunchKernelGGL((decode_gemm_kernel<7, G, NW, 2, false, 1, S, XL>), grid, block, 0, stream,
                      (const uint8_t*)x, (const uint8_t*)w, (const _Float16*)nullptr, gs,
