@@ -575,7 +575,23 @@ struct DecodeConfig {
 bool use_x_lds(int fmt, int64_t M, int nw, int s, int64_t KT) {
   const int rb = fmt == 3 || fmt == 4 ? 128 : 256;
   const int ni = rb == 256 ? 4 : 2;
-  return M > 8 && nw == 8 && s * ni <= 8 && M * KT * rb < ((int64_t)1 << 31);
+  return M > 8 && (nw == 8 || (nw == 4 && KT >= 16)) && s * ni <= 8 &&
+         M * KT * rb < ((int64_t)1 << 31);
+}
+
+// Waves per workgroup: eight, or four when K has fewer than 16 tiles.  A
+// launch with several row blocks (above 16 S rows) also takes four: its
+// staging slots then need 64 KB of LDS instead of 128, so two workgroups
+// share a CU and one's start (the first weight tiles arriving from HBM) and
+// end (the reduction and stores) overlap the other's K loop.  Measured on
+// MI355X at M = 64 / 96 / 128: W8A16 K = 4096, N = 11008 21.6 / 29.4 / 36.4
+// us with eight waves, 19.9 / 26.7 / 32.6 with four; at M = 128: grouped
+// W8A16 (group 128, same shape) 39.8 -> 34.0, grouped W4A16 (group 128,
+// K = 8192, N = 28672) 115 -> 109, MXFP4 K = N = 8192 29.8 -> 27.3, FP8
+// 30.5 -> 29.1, W4A16 K = 8192, N = 28672 89.5 -> 88.0.  Two waves (four
+// workgroups per CU) ran M = 64 slower (W4A16 71 us against 50).
+int decode_waves(int64_t M, int s, int64_t KT) {
+  return KT < 16 || (s > 1 && M > 16 * s) ? 4 : 8;
 }
 
 // Launch shape: about one workgroup per CU.  Measured on MI355X at the decode
@@ -603,8 +619,7 @@ DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
   const int64_t gmax = s == 1 ? (fmt == 1 ? 8 : 4) : s == 2 ? (fmt == 1 ? 7 : 4) : fmt == 3 ? 2 : 3;
   int64_t g = cdiv(CG, 256);
   g = g < 1 ? 1 : (g > gmax ? gmax : g);
-  DecodeConfig c{(int)g, 8, s == 1 && fmt == 2 ? 3 : 2, s, false};
-  if (KT < 16) c.nw = 4;
+  DecodeConfig c{(int)g, decode_waves(M, s, KT), s == 1 && fmt == 2 ? 3 : 2, s, false};
   c.xl = use_x_lds(fmt, M, c.nw, c.s, KT);
   return c;
 }
@@ -642,7 +657,9 @@ hipError_t launch_fmt_cfg(const DecodeConfig& c, const void* x, const void* w, c
 #define QG_G(GG) \
   QG_CASE(GG, 8, DEPTH, 1, false) QG_CASE(GG, 4, DEPTH, 1, false) QG_CASE(GG, 8, DEPTH, 1, true)
 #define QG_GS(GG, SS) QG_CASE(GG, 8, 2, SS, false) QG_CASE(GG, 4, 2, SS, false) \
-  if constexpr (SS * (FMT == 3 || FMT == 4 ? 2 : 4) <= 8) { QG_CASE(GG, 8, 2, SS, true) }
+  if constexpr (SS * (FMT == 3 || FMT == 4 ? 2 : 4) <= 8) {                                \
+    QG_CASE(GG, 8, 2, SS, true) QG_CASE(GG, 4, 2, SS, true)                               \
+  }
   constexpr int DEPTH = FMT == 2 ? 3 : 2;
   QG_G(1) QG_G(2) QG_G(3) QG_G(4)
   if constexpr (FMT == 1) {   // up to eight INT4 column groups fit in registers
@@ -709,11 +726,13 @@ template <int FMT, int NGT>
 hipError_t launch_grouped_ngt(const void* x, const void* w, void* y, int64_t M, int64_t N,
                               int64_t K, int64_t KT, int64_t CG, int64_t meta_offset,
                               hipStream_t stream) {
-  const int nw = KT < 16 ? 4 : 8;
-  const int s = slab_count(M, nw);
+  const int s = slab_count(M, KT < 16 ? 4 : 8);
   // two slabs with four metadata words per tile leave room for four INT4
   // groups (seven spill)
   const int g = slab_groups(CG, FMT == 1 && !(s == 2 && NGT == 4) ? 7 : 4, KT);
+  // seven groups with two metadata words keep eight waves: with four they
+  // would need more than 256 registers per lane (one wave per SIMD)
+  const int nw = g == 7 && NGT > 1 ? (KT < 16 ? 4 : 8) : decode_waves(M, s, KT);
   // seven groups with one slab load faster directly
   const bool xl = use_x_lds(FMT, M, nw, s, KT) && (s > 1 || g <= 4);
 #define QG_GCASE(GG, WW, SS, XX)                                                            \
@@ -721,15 +740,20 @@ hipError_t launch_grouped_ngt(const void* x, const void* w, void* y, int64_t M, 
     return launch_grouped_cfg<FMT, NGT, GG, WW, SS, XX>(x, w, y, M, N, K, KT, CG,           \
                                                         meta_offset, stream);
 #define QG_GCASE2(GG, SS) QG_GCASE(GG, 8, SS, false) QG_GCASE(GG, 8, SS, true)
+#define QG_GCASE4(GG) QG_GCASE2(GG, 2) QG_GCASE(GG, 4, 2, true)
   QG_GCASE(1, 4, 1, false) QG_GCASE(2, 4, 1, false)
   QG_GCASE2(1, 1) QG_GCASE2(2, 1) QG_GCASE2(3, 1) QG_GCASE2(4, 1)
-  QG_GCASE2(1, 2) QG_GCASE2(2, 2) QG_GCASE2(3, 2) QG_GCASE2(4, 2)
+  QG_GCASE4(1) QG_GCASE4(2) QG_GCASE4(3) QG_GCASE4(4)
   if constexpr (FMT == 1) {
     QG_GCASE(7, 8, 1, false)
   }
-  if constexpr (FMT == 1 && NGT < 4) {
+  if constexpr (FMT == 1 && NGT == 1) {
+    QG_GCASE4(7)
+  }
+  if constexpr (FMT == 1 && NGT == 2) {
     QG_GCASE2(7, 2)
   }
+#undef QG_GCASE4
 #undef QG_GCASE2
 #undef QG_GCASE
   return hipErrorInvalidValue;
@@ -765,17 +789,20 @@ hipError_t launch_decode_nvfp4(const void* x, const void* w_packed, const float*
                                void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const PackGeom pg = pack_geom(7, K, N);
   const int g = slab_groups(pg.cg, 7, pg.kt);
-  const int nw = pg.kt < 16 ? 4 : 8;
-  const int s = slab_count(M, nw);
+  const int s = slab_count(M, pg.kt < 16 ? 4 : 8);
+  // seven groups keep eight waves (with four: 264 registers per lane)
+  const int nw = g == 7 ? (pg.kt < 16 ? 4 : 8) : decode_waves(M, s, pg.kt);
   const bool xl = use_x_lds(7, M, nw, s, pg.kt) && (s > 1 || g <= 4);   // as for grouped
 #define QG_NCASE(GG, WW, SS, XX)                                                           \
   if (g == GG && nw == WW && s == SS && xl == XX)                                          \
     return launch_nvfp4_cfg<GG, WW, SS, XX>(x, w_packed, global_scale, y, M, N, K, pg.kt,  \
                                             pg.cg, pg.scales, stream);
 #define QG_NCASE2(GG, SS) QG_NCASE(GG, 8, SS, false) QG_NCASE(GG, 8, SS, true)
+#define QG_NCASE4(GG) QG_NCASE2(GG, 2) QG_NCASE(GG, 4, 2, true)
   QG_NCASE(1, 4, 1, false) QG_NCASE(2, 4, 1, false)
   QG_NCASE2(1, 1) QG_NCASE2(2, 1) QG_NCASE2(3, 1) QG_NCASE2(4, 1) QG_NCASE(7, 8, 1, false)
-  QG_NCASE2(1, 2) QG_NCASE2(2, 2) QG_NCASE2(3, 2) QG_NCASE2(4, 2) QG_NCASE2(7, 2)
+  QG_NCASE4(1) QG_NCASE4(2) QG_NCASE4(3) QG_NCASE4(4) QG_NCASE2(7, 2)
+#undef QG_NCASE4
 #undef QG_NCASE2
 #undef QG_NCASE
   return hipErrorInvalidValue;

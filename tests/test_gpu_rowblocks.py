@@ -7,9 +7,12 @@ XCD, and pads the column blocks to a multiple of eight (the padding
 workgroups exit at once).  These cases cross that mapping's edges against the
 CPU oracle for every format that uses the kernel: three to ten row blocks
 with a ragged last one, column-block counts below eight and not a multiple of
-eight, and the weight-only shapes from M = 256 up that take this kernel
-because their tile grid is small.  Bar: |Y - Y_ref| <= 1e-2 * (|X| @ |W_deq|)
-+ 1e-3 elementwise (the oracle's bound); two calls give identical bytes.
+eight, the weight-only shapes from M = 256 up that take this kernel because
+their tile grid is small, and seven column groups per workgroup.  Launches
+with several row blocks use four waves per workgroup (two workgroups per
+CU), except seven-group ones whose registers would not fit twice.
+Bar: |Y - Y_ref| <= 1e-2 * (|X| @ |W_deq|) + 1e-3 elementwise (the oracle's
+bound); two calls give identical bytes.
 """
 
 import numpy as np
@@ -94,7 +97,30 @@ def test_grouped_row_blocks(fmt, m, k, n, gk):
     check(lambda: fn(dev(x), wp, n, gk), y_ref, bound, f"{fmt} grouped {m}x{k}x{n}")
 
 
-@pytest.mark.parametrize("m,k,n", [(90, 2128, 150), (128, 2048, 64)])
+# N = 28672 gives 1792 column groups, seven per workgroup: the widest
+# register ring, with four waves per workgroup for INT4 (per-column scales
+# and group 128) and eight for NVFP4 and group 64
+def test_w4a16_seven_groups_row_blocks():
+    m, k, n = 40, 2048, 28672
+    case_id("w4a16 seven groups row blocks", m, k, n)
+    x, packed, s = wl.w4a16(m, k, n, seed=11)
+    y_ref, bound = oracle.gemm_w4a16(x, packed, s)
+    wp = qg.qgemm_prepack("w4a16", dev(packed), k, n)
+    check(lambda: qg.qgemm_w4a16(dev(x), wp, dev(s), n), y_ref, bound, f"w4a16 {m}x{k}x{n}")
+
+
+@pytest.mark.parametrize("gk", [128, 64])
+def test_grouped_w4a16_seven_groups_row_blocks(gk):
+    m, k, n = 40, 2048, 28672
+    case_id("w4a16 grouped seven groups row blocks", m, k, n, gk)
+    x, w, s, z = wl.w4a16_grouped(m, k, n, gk, 1, zeros=True, seed=12)
+    y_ref, bound = oracle.gemm_w4a16_grouped(x, w, s, z, gk, 1)
+    wp = qg.qgemm_prepack_grouped("w4a16_grouped", dev(w), k, n, dev(s), dev(z), gk, 1)
+    check(lambda: qg.qgemm_w4a16_grouped(dev(x), wp, n, gk), y_ref, bound,
+          f"w4a16 grouped {m}x{k}x{n} g{gk}")
+
+
+@pytest.mark.parametrize("m,k,n", [(90, 2128, 150), (128, 2048, 64), (40, 2048, 28672)])
 def test_nvfp4_row_blocks(m, k, n):
     case_id("nvfp4 row blocks", m, k, n)
     x, codes, scales, g = wl.nvfp4_weight(m, k, n, seed=3 * m + k + n)
