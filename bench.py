@@ -722,8 +722,9 @@ def kernel_name(setup, m):
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     # same rules as the library's dispatch
     if setup.fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped", "nvfp4"):
+        tiles = -(-m // 256) * -(-setup.n // 256)
         big = (m >= 256 and setup.n > 128 and setup.k % 8 == 0
-               and -(-m // 256) * -(-setup.n // 256) >= 64)
+               and (tiles >= 192 or (m >= 640 and tiles >= 48)))
         name = "pipe256_kernel" if big else "decode_gemm_kernel"
         return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     if m <= SMALL_M_MAX:

@@ -17,15 +17,26 @@ using qgemm::pack_geom;
 using qgemm::grouped_geom;
 
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;   // kernels index with 32-bit ints
-// The weight-only GEMMs take the 256 x 256 tiled kernel from M = 256 on, once
-// its grid has at least 64 workgroups; a smaller grid leaves most CUs idle,
-// and the small-M kernel (several 16-row slabs per workgroup, one pass over
-// the weight per 32 or 64 rows) is faster there.
+// The weight-only GEMMs take the 256 x 256 tiled kernel from M = 256 on once
+// its grid fills three quarters of the CUs (192 tiles), or from M = 640 with
+// at least 48 tiles; otherwise the small-M kernel.  A round of tiles costs
+// about the same whatever M is, while the small-M kernel's time grows with M.
+// Measured on MI355X (us, small-M kernel / tiled kernel):
+//   W8A16 K = 4096 N = 11008 (43 tile columns): M = 512 114 / 132, 768 189 / 134
+//   W4A16 K = 8192 N = 28672 (112): M = 256 177 / 219, 384 267 / 223
+//   W8A16 K = 4096 N = 4096 (16): M = 512 75 / 132, 768 165 / 132
+//   grouped W4A16 g128 K = 8192 N = 28672: M = 256 214 / 257, 384 318 / 258
+//   grouped W8A16 g128 K = 4096 N = 11008: M = 512 115 / 151, 768 186 / 153
+//   NVFP4 K = 8192 N = 28672: M = 256 198 / 247, 384 303 / 249
 constexpr int64_t kWeightOnlyTileMinM = 256;
-constexpr int64_t kWeightOnlyTileMinTiles = 64;
+constexpr int64_t kWeightOnlyTileFullGrid = 192;
+constexpr int64_t kWeightOnlyTileLongM = 640;
+constexpr int64_t kWeightOnlyTileLongMinTiles = 48;
 bool weight_only_tiled(int64_t M, int64_t N) {
-  return M >= kWeightOnlyTileMinM && N > 128 &&
-         qgemm::cdiv(M, 256) * qgemm::cdiv(N, 256) >= kWeightOnlyTileMinTiles;
+  if (M < kWeightOnlyTileMinM || N <= 128) return false;
+  const int64_t tiles = qgemm::cdiv(M, 256) * qgemm::cdiv(N, 256);
+  return tiles >= kWeightOnlyTileFullGrid ||
+         (M >= kWeightOnlyTileLongM && tiles >= kWeightOnlyTileLongMinTiles);
 }
 // FP8 and MXFP4 GEMMs with M up to this take the small-M kernel (16-row
 // slabs, up to four per workgroup); above it the tile kernels.  Measured on MI355X at

@@ -36,7 +36,7 @@ def _shapes(seed, count, m_range, n_range, k_values):
 
 # fp16 activations: K tiles of 128 (16 tiles from K = 2048 on); K % 8 != 0
 # takes the element-wise path.  Weight-only M up to 255 stays on this kernel
-# (the tiled kernel needs M >= 256).
+# (the tiled kernel needs M >= 256 and enough tiles).
 FP16_K = [24, 136, 1000, 1030, 2056, 2120, 3002, 4104]
 W4_SWEEP = _shapes(201, 10, (1, 129), (1, 700), FP16_K) + _shapes(202, 2, (129, 256), (1, 300), FP16_K)
 W8_SWEEP = _shapes(203, 10, (1, 129), (1, 700), FP16_K + [1001, 2051]) + \

@@ -118,7 +118,7 @@ def test_grouped_full_size_sampled(fmt, m):
     assert_within(y[:, cols], y_ref, bound, f"{fmt} grouped full M={m}")
 
 
-# M >= 256 with fewer than 64 tiles of 256 x 256: the small-M kernel with two
+# M >= 256 with too few 256 x 256 tiles for the tiled kernel: the small-M kernel with two
 # 16-row slabs per workgroup: every metadata density (NGT = 1, 2, 4 words per
 # column and tile), ragged M and N, K not a multiple of 128, short K.
 TILE_CASES = [
@@ -166,7 +166,7 @@ def test_grouped_tile_full_size_sampled(fmt):
     assert_within(y[:, cols], y_ref, bound, f"{fmt} grouped tile full")
 
 
-# At least 64 tiles of 256 x 256: the tiled kernel, on sampled outputs (every
+# From M = 640 with at least 48 tiles of 256 x 256: the tiled kernel, on sampled outputs (every
 # metadata density, K tail, K below one tile; each sampled column gets its own
 # group entries).
 TILED_CASES = [

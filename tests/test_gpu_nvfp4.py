@@ -90,7 +90,7 @@ def test_nvfp4_decode_full_size_sampled(m):
     assert ok.all(), f"{int((~ok).sum())} outside tolerance"
 
 
-# M >= 256 with fewer than 64 tiles of 256 x 256: the small-M kernel, two
+# M >= 256 with too few 256 x 256 tiles for the tiled kernel: the small-M kernel, two
 # 16-row slabs per workgroup.
 TILE_CASES = [
     (256, 256, 200),      # two K tiles, ragged N
@@ -128,7 +128,7 @@ def test_nvfp4_tile_one_hot_reads_back_every_weight():
 
 @pytest.mark.parametrize("m,k,n", [(2048, 1056, 2080), (2304, 48, 2048), (2048, 2048, 2048)])
 def test_nvfp4_tiled_sampled(m, k, n):
-    """At least 64 tiles of 256 x 256: the tiled kernel, on sampled outputs."""
+    """M >= 640 with at least 48 tiles of 256 x 256: the tiled kernel, on sampled outputs."""
     case_id("nvfp4 tiled", m, k, n)
     x, codes, scales, g = wl.nvfp4_weight(m, k, n, seed=m + k + n)
     y = run(x, codes, scales, g, k, n)

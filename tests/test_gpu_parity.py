@@ -220,7 +220,7 @@ def test_weight_only_one_hot_through_large_tiles(fmt):
     assert np.array_equal(y, wdeq)
 
 
-# At least 64 tiles of 256 x 256: the tiled kernel (K tail, short K, one K tile).
+# M >= 640 with at least 48 tiles of 256 x 256: the tiled kernel (K tail, short K, one K tile).
 TILED_CASES = [(2048, 1000, 2100), (2304, 136, 2048), (2050, 64, 2304)]
 
 

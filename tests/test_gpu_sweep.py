@@ -36,7 +36,7 @@ MX_SWEEP = _shapes(101, 10, (129, 700), (129, 700), [512, 640, 768, 896, 1152, 1
     _shapes(102, 4, (129, 520), (129, 520), [544, 608, 800])
 # FP8: M, N > 128 and at least two 128-element K tiles; K % 16 == 0
 FP8_SWEEP = _shapes(103, 12, (129, 700), (129, 700), [256, 272, 400, 528, 1024, 1040, 1296])
-# weight-only tile path: M >= 256 with at least 64 tiles of 256 x 256; K % 8 == 0
+# weight-only tile path: M >= 640 with 64 to 81 tiles of 256 x 256; K % 8 == 0
 WO_SWEEP = _shapes(104, 3, (1793, 2100), (1793, 2100), [136, 264, 392])
 
 
