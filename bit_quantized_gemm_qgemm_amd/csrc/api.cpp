@@ -38,11 +38,26 @@ bool weight_only_tiled(int64_t M, int64_t N) {
   return tiles >= kWeightOnlyTileFullGrid ||
          (M >= kWeightOnlyTileLongM && tiles >= kWeightOnlyTileLongMinTiles);
 }
-// FP8 and MXFP4 GEMMs with M up to this take the small-M kernel (16-row
-// slabs, up to four per workgroup); above it the tile kernels.  Measured on MI355X at
-// K = N = 8192: M = 32 / 64 / 128 in 15.7 / 24.0 / 43.5 us against 71-76 us
-// through the 128 x 128 tiles, and a tie at M = 256.
-constexpr int kDecodeMaxM = 128;
+// FP8 and MXFP4 GEMMs take the small-M kernel (16-row slabs, up to four per
+// workgroup) up to M = 128, and above that while the tiled kernels' grid
+// stays small: FP8 up to M = 512 while M * N <= 2.6e6 (5 * 2^19), MXFP4 up
+// to M = 256 while M * N <= 2^21.  Above, the tile kernels.  The small-M
+// kernel's time grows with M * N * K, while the tiled kernels take about one
+// 256 x 256 x K tile per CU whatever M is.  Measured on MI355X (us, small-M
+// kernel / tile kernels):
+//   FP8 K = N = 8192:   M = 144 47 / 69, 256 48 / 73, 384 71 / 70, 512 95 / 73
+//   FP8 K = N = 4096:   M = 512 37 / 40, 768 54 / 40
+//   FP8 K = 8192, N = 28672: M = 144 123 / 80
+//   MXFP4 K = N = 8192: M = 192 39 / 50, 256 49 / 56, 384 70 / 46
+//   MXFP4 K = N = 4096: M = 256 24 / 26, 384 34 / 25
+//   MXFP4 K = 8192, N = 28672: M = 144 117 / 52
+// Up to M = 128 the small-M kernel stays, also where 128 x 128 tiles would
+// win by a few percent for very wide N (FP8 N = 28672, M = 128: 86 / 80).
+bool scaled_small_m(int fmt, int64_t M, int64_t N) {
+  if (M <= 128) return true;
+  if (fmt == QGEMM_FP8) return M <= 512 && M * N <= 2621440;
+  return M <= 256 && M * N <= 2097152;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -181,7 +196,7 @@ int fp8_act_run(const float* a, const void* b_packed, const float* scale_b, void
   int st = launched(
       qgemm::launch_quantize_fp8_ws(a, M * K, codes, scale_a, partials, as_stream(stream)));
   if (st != QGEMM_OK || N == 0) return st;
-  if (M <= kDecodeMaxM)
+  if (scaled_small_m(QGEMM_FP8, M, N))
     return launched(qgemm::launch_decode_gemm(QGEMM_FP8, codes, b_packed, nullptr, scale_a,
                                               scale_b, c, M, N, K, as_stream(stream)));
   return launched(qgemm::launch_tile_gemm(QGEMM_FP8, codes, nullptr, b_packed, scale_a, scale_b,
@@ -356,7 +371,7 @@ int qgemm_mxfp4(const void* a_codes, const void* a_e8m0, const void* w_packed, v
   if (!aligned(a_codes, 16) || !aligned(w_packed, 16) || !aligned(c, 16)) return QGEMM_ERR_ALIGN;
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
-  if (M <= kDecodeMaxM)
+  if (scaled_small_m(QGEMM_MXFP4, M, N))
     return launched(qgemm::launch_decode_gemm(QGEMM_MXFP4, a_codes, w_packed, a_e8m0, nullptr,
                                               nullptr, c, M, N, K, as_stream(stream)));
   return launched(qgemm::launch_tile_gemm(QGEMM_MXFP4, a_codes, a_e8m0, w_packed, nullptr,
@@ -374,7 +389,7 @@ int qgemm_fp8(const void* a, const void* b_packed, const float* scale_a, const f
   if (!aligned(scale_a, 4) || !aligned(scale_b, 4)) return QGEMM_ERR_ALIGN;
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
-  if (M <= kDecodeMaxM)
+  if (scaled_small_m(QGEMM_FP8, M, N))
     return launched(qgemm::launch_decode_gemm(QGEMM_FP8, a, b_packed, nullptr, scale_a, scale_b,
                                               c, M, N, K, as_stream(stream)));
   return launched(qgemm::launch_tile_gemm(QGEMM_FP8, a, nullptr, b_packed, scale_a, scale_b, c, M,
@@ -409,7 +424,7 @@ int qgemm_mxfp4_act(const float* a, const void* w_packed, void* c, void* workspa
     if (st != QGEMM_OK) return st;
   }
   if (N == 0) return QGEMM_OK;
-  if (M <= kDecodeMaxM)
+  if (scaled_small_m(QGEMM_MXFP4, M, N))
     return launched(qgemm::launch_decode_gemm(QGEMM_MXFP4, codes, w_packed, e8m0, nullptr,
                                               nullptr, c, M, N, K, as_stream(stream)));
   return launched(qgemm::launch_tile_gemm(QGEMM_MXFP4, codes, e8m0, w_packed, nullptr, nullptr, c,

@@ -57,7 +57,8 @@ def test_mxfp4_act(m, n, k):
     assert oracle.within_tolerance(c.float().cpu().numpy(), c_ref, bound).all()
 
 
-@pytest.mark.parametrize("m,n,k", [(16, 300, 512), (1, 64, 128), (200, 272, 384), (17, 16, 16)])
+@pytest.mark.parametrize("m,n,k", [(16, 300, 512), (1, 64, 128), (200, 272, 384), (600, 272, 384),
+                                   (17, 16, 16)])
 def test_fp8_act(m, n, k):
     case_id("fp8 act", m, n, k)
     a, b = wl.fp8_operands(m, n, k, seed=m + n + k)

@@ -2,7 +2,8 @@
 
 The hand-picked decode cases cover each edge once.  Here a fixed, seeded
 draw of shapes crosses the small-M kernel's launch choices in combination
-for every format it serves: one to sixteen rows (one slab, activations
+for every format it serves (weight-only M up to 255, FP8 up to 512, MXFP4 up
+to 256): one to sixteen rows (one slab, activations
 loaded directly or staged above eight rows), two slabs, four (e4m3 / E2M1
 activations above 32 rows), one and several row blocks (several: four
 waves per workgroup and the XCD-aware workgroup mapping with padded column
@@ -42,8 +43,11 @@ W4_SWEEP = _shapes(201, 10, (1, 129), (1, 700), FP16_K) + _shapes(202, 2, (129, 
 W8_SWEEP = _shapes(203, 10, (1, 129), (1, 700), FP16_K + [1001, 2051]) + \
     _shapes(204, 2, (129, 256), (1, 300), FP16_K)
 # e4m3: K % 16 == 0, tiles of 128; E2M1: K % 32 == 0, tiles of 256
-FP8_SWEEP = _shapes(205, 10, (1, 129), (1, 700), [16, 272, 1040, 2064, 2128, 4112])
-MX_SWEEP = _shapes(206, 10, (1, 129), (1, 700), [32, 288, 1056, 4128, 4352])
+# (the small-M kernel takes FP8 up to M = 512 and MXFP4 up to M = 256 at these N)
+FP8_SWEEP = _shapes(205, 10, (1, 129), (1, 700), [16, 272, 1040, 2064, 2128, 4112]) + \
+    _shapes(210, 4, (129, 513), (1, 700), [16, 272, 2064, 2128])
+MX_SWEEP = _shapes(206, 10, (1, 129), (1, 700), [32, 288, 1056, 4128, 4352]) + \
+    _shapes(211, 3, (129, 257), (1, 700), [288, 4128, 4352])
 NV_SWEEP = _shapes(207, 8, (1, 129), (1, 700), [16, 272, 1040, 2064, 2128])
 # grouped: K and the group a multiple of 32
 GROUPED_SWEEP = [(m, n, k, int(g)) for (m, n, k), g in zip(

@@ -1,11 +1,14 @@
-"""GPU parity on both sides of the weight-only dispatch rule.
+"""GPU parity on both sides of the dispatch rules between the small-M kernel
+and the tiled kernels.
 
 The weight-only GEMMs (per-column INT4 / INT8, grouped, NVFP4 weights) take
 the 256 x 256 tiled kernel from M = 256 on once its grid of
 T = ceil(M / 256) * ceil(N / 256) tiles reaches 192, or from M = 640 once
-T >= 48; otherwise the small-M kernel.  Each pair of cases below sits on
-the two sides of one edge of that rule, so both kernels run at the shapes
-where the dispatch switches.  Every output is checked against the oracle
+T >= 48; otherwise the small-M kernel.  FP8 takes the small-M kernel up to
+M = 128, and up to M = 512 while M * N <= 2621440; MXFP4 up to M = 128, and
+up to M = 256 while M * N <= 2^21; otherwise the tiled kernels.  Each pair
+of cases below sits on the two sides of one edge of a rule, so both kernels
+run at the shapes where the dispatch switches.  Every output is checked against the oracle
 (bar: |Y - Y_ref| <= 1e-2 * (|X| @ |W_deq|) + 1e-3 elementwise) and each
 call is repeated for determinism.
 """
@@ -101,3 +104,49 @@ def test_nvfp4_dispatch_edges(m, k, n):
     wp = qg.qgemm_prepack("nvfp4", dev(codes), k, n, w_scales=dev(scales))
     gs = torch.tensor([g], dtype=torch.float32, device="cuda")
     check(lambda: qg.qgemm_nvfp4(dev(x), wp, gs, n), y_ref, bound, f"nvfp4 {m}x{k}x{n}")
+
+
+# FP8: (m, n, k), small-M kernel / tiles
+FP8_EDGES = [
+    (512, 5120, 256),     # M * N = 2621440: small-M kernel
+    (512, 5136, 256),     # M * N above: 256 x 256 tiles
+    (129, 20320, 256),    # small-M kernel
+    (129, 20336, 256),    # tiles
+    (512, 64, 272),       # small-M kernel
+    (513, 64, 272),       # M > 512: 128 x 128 tiles (N <= 128)
+]
+
+
+@pytest.mark.parametrize("m,n,k", FP8_EDGES)
+def test_fp8_dispatch_edges(m, n, k):
+    case_id("fp8 dispatch edge", m, n, k)
+    a, b = wl.fp8_operands(m, n, k, seed=m + n + k)
+    qa, sa = oracle.fp8_quantize(a)
+    qb, sb = oracle.fp8_quantize(b)
+    c_ref, bound = oracle.gemm_fp8(qa, qb, sa, sb)
+    bp = qg.qgemm_prepack("fp8", dev(qb), k, n)
+    sa_d = torch.tensor([sa], dtype=torch.float32, device="cuda")
+    sb_d = torch.tensor([sb], dtype=torch.float32, device="cuda")
+    check(lambda: qg.qgemm_fp8(dev(qa), bp, sa_d, sb_d, n), c_ref, bound, f"fp8 {m}x{n}x{k}")
+
+
+# MXFP4: (m, n, k), small-M kernel / tiles
+MX_EDGES = [
+    (256, 8192, 512),     # M * N = 2^21: small-M kernel
+    (256, 8208, 512),     # M * N above: 256 x 256 tiles
+    (256, 200, 640),      # small-M kernel
+    (257, 200, 640),      # M > 256: 256 x 256 tiles
+    (200, 10485, 288),    # small-M kernel (M * N = 2097000)
+    (200, 10500, 288),    # tiles: K = 288 is not a multiple of 128, the 128 x 128 kernel
+]
+
+
+@pytest.mark.parametrize("m,n,k", MX_EDGES)
+def test_mxfp4_dispatch_edges(m, n, k):
+    case_id("mxfp4 dispatch edge", m, n, k)
+    a, w = wl.mxfp4_operands(m, n, k, seed=m + n + k)
+    ac, ae = oracle.mxfp4_quantize(a)
+    wc, we = oracle.mxfp4_quantize(w)
+    c_ref, bound = oracle.gemm_mxfp4(ac, ae, wc, we)
+    wp = qg.qgemm_prepack("mxfp4", dev(wc), k, n, w_scales=dev(we))
+    check(lambda: qg.qgemm_mxfp4(dev(ac), dev(ae), wp, n), c_ref, bound, f"mxfp4 {m}x{n}x{k}")

@@ -334,19 +334,23 @@ def test_mxfp4_quantizer_ties_and_edges_bit_exact():
 
 MX_CASES = [
     (64, 64, 256),
-    (130, 70, 96),      # ragged M, N, K (K not a multiple of the 256-wide step)
+    (300, 70, 96),      # 128 x 128 tiles: ragged M, N, K (K not a multiple of the 256-wide step)
+    (130, 70, 96),      # the same ragged N and K through the small-M kernel above 128 rows
     (1, 16, 32),
     (257, 129, 544),
-    (256, 256, 1024),
+    (260, 256, 1024),
+    (256, 256, 1024),   # small-M kernel: M = 256 with M * N <= 2^21
     (16, 300, 2048),
     (300, 260, 640),    # 256 x 256 tiles: ragged M and N, K a multiple of 128
     (512, 512, 1024),
-    (129, 1000, 384),   # K = 384: a half 256-wide step at the end
+    (129, 16300, 384),  # M * N > 2^21: 256 x 256 tiles; K = 384, a half 256-wide step at the end
+    (129, 1000, 384),   # the same K through the small-M kernel
     (257, 384, 1280),   # 256 x 256 tiles, several pipeline iterations
-    (160, 136, 896),    # last 128-wide step all padding; 9 column tiles
+    (300, 136, 896),    # last 128-wide step all padding; 9 column tiles
     (100, 520, 800),    # small-M kernel: four slabs, two workgroup rows, K = 3.125 tiles
     (33, 136, 288),     # four slabs, one row of them ragged; K = 1.125 tiles
-    (128, 2100, 256),   # the largest M the small-M kernel takes
+    (128, 2100, 256),
+    (200, 600, 4128),   # small-M kernel above 128 rows: four row blocks of 64, eight waves' K
     (1024, 2048, 512),  # 4 x 8 tiles of 256 x 256: the tile count is a multiple of 8,
                         # so the XCD-remapped walk and its 4-row groups run
     (1280, 1792, 768),  # 5 x 7 = 35 tiles (plain walk), ragged group of tile rows
@@ -394,7 +398,7 @@ def test_mxfp4_one_hot_reads_back_dequantized_weights():
 
 @pytest.mark.parametrize("m,n,k", [(300, 272, 512), (512, 768, 2048)])
 def test_mxfp4_one_hot_through_large_tiles(m, n, k):
-    """One-hot read-back through the 256 x 256 kernel (M, N > 128): every
+    """One-hot read-back through the 256 x 256 kernel (M > 256, N > 128): every
     (row tile, column tile, K step, scale byte) mapping is hit, bit-exact."""
     case_id("mxfp4 one-hot large tiles", m, n, k)
     _, w = wl.mxfp4_operands(1, n, k, seed=9)
@@ -510,18 +514,22 @@ FP8_CASES = [
     (16, 64, 128),      # small-M path
     (1, 48, 256),
     (7, 130, 96),
-    (200, 72, 160),     # tile path, ragged
-    (256, 256, 512),
+    (600, 72, 160),     # 128 x 128 tiles, ragged
+    (200, 72, 160),     # the same through the small-M kernel above 128 rows
+    (768, 256, 512),
     (17, 16, 16),
-    (300, 260, 528),    # 256 x 256 tiles with a 16-wide K tail
-    (512, 512, 1024),
-    (129, 1000, 256),
-    (257, 300, 384),    # 256 x 256 tiles, six 64-wide steps
-    (136, 200, 2064),   # 256 x 256 tiles, K tail of 16 in the last step
+    (560, 260, 528),    # 256 x 256 tiles with a 16-wide K tail
+    (300, 260, 528),    # the same K tail through the small-M kernel
+    (512, 5200, 1024),  # M * N > 2.6e6: 256 x 256 tiles
+    (512, 5120, 1024),  # M * N = 2621440: the small-M kernel's largest grid, eight row blocks
+    (129, 20400, 256),  # M * N > 2.6e6 from M = 129: tiles
+    (640, 300, 384),    # 256 x 256 tiles, six 64-wide steps
+    (560, 200, 2064),   # 256 x 256 tiles, K tail of 16 in the last step
+    (136, 200, 2064),   # the same K tail through the small-M kernel
     (32, 256, 512),     # small-M kernel, two 16-row slabs per workgroup
     (64, 1024, 2048),   # four slabs
     (100, 512, 384),    # four slabs, two workgroup rows, ragged
-    (128, 2048, 256),   # the largest M the small-M kernel takes
+    (128, 2048, 256),
     (1024, 2048, 512),  # 4 x 8 tiles of 256 x 256: the XCD-remapped walk
     (2048, 1024, 1024), # 8 x 4 tiles: remapped walk, two 4-row groups
     (1200, 1800, 528),  # 5 x 8 = 40 tiles, remapped, ragged last tile row and column
@@ -562,9 +570,9 @@ def test_fp8_one_hot_reads_back_codes(m):
 
 
 def test_fp8_one_hot_through_large_tiles():
-    """One-hot read-back through the 256 x 256 path (M, N > 128), bit-exact:
+    """One-hot read-back through the 256 x 256 path (M > 512, N > 128), bit-exact:
     pins the 32 x 32 accumulator layout and the K order of both operands."""
-    m, n, k = 300, 272, 384
+    m, n, k = 600, 272, 384
     case_id("fp8 one-hot large tiles", m, n, k)
     b = np.random.default_rng(6).integers(0, 256, size=(k, n)).astype(np.uint8)
     b[(b & 0x7f) == 0x7f] = 0x3c                     # no NaN codes

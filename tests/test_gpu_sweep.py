@@ -30,12 +30,14 @@ def _shapes(seed, count, m_range, n_range, k_values):
     return out
 
 
-# MXFP4: M, N > 128 take the 256 x 256 kernel when K % 128 == 0 (K >= 512);
-# other multiples of 32 take the 128 x 128 kernel
-MX_SWEEP = _shapes(101, 10, (129, 700), (129, 700), [512, 640, 768, 896, 1152, 1408]) + \
-    _shapes(102, 4, (129, 520), (129, 520), [544, 608, 800])
-# FP8: M, N > 128 and at least two 128-element K tiles; K % 16 == 0
-FP8_SWEEP = _shapes(103, 12, (129, 700), (129, 700), [256, 272, 400, 528, 1024, 1040, 1296])
+# MXFP4: M > 256 (the small-M kernel's limit at these N) and N > 128 take the
+# 256 x 256 kernel when K % 128 == 0 (K >= 512); other multiples of 32 take
+# the 128 x 128 kernel
+MX_SWEEP = _shapes(101, 10, (257, 900), (129, 700), [512, 640, 768, 896, 1152, 1408]) + \
+    _shapes(102, 4, (257, 720), (129, 520), [544, 608, 800])
+# FP8: M > 512 (the small-M kernel's limit at these N), N > 128 and at least
+# two 128-element K tiles; K % 16 == 0
+FP8_SWEEP = _shapes(103, 12, (513, 1100), (129, 700), [256, 272, 400, 528, 1024, 1040, 1296])
 # weight-only tile path: M >= 640 with 64 to 81 tiles of 256 x 256; K % 8 == 0
 WO_SWEEP = _shapes(104, 3, (1793, 2100), (1793, 2100), [136, 264, 392])
 
