@@ -727,12 +727,18 @@ def kernel_name(setup, m):
                and (tiles >= 192 or (m >= 640 and tiles >= 48)))
         name = "pipe256_kernel" if big else "decode_gemm_kernel"
         return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
-    small = m <= 128 or ((m <= 512 and m * setup.n <= 2621440) if setup.fmt == "fp8"
-                         else (m <= 256 and m * setup.n <= 2097152))
+    if m <= 64:
+        small = True
+    elif m <= 128:
+        small = setup.n < (24576 if setup.fmt == "fp8" else 16384)
+    elif setup.fmt == "fp8":
+        small = m <= 512 and m * setup.n <= 2621440
+    else:
+        small = m <= 256 and m * setup.n <= 2097152
     if small:
         return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
     k_tiles = -(-setup.k // (256 if setup.fmt == "mxfp4" else 128))
-    big = m > 128 and setup.n > 128 and k_tiles >= 2 and (setup.fmt != "mxfp4" or setup.k % 128 == 0)
+    big = m > 64 and setup.n > 128 and k_tiles >= 2 and (setup.fmt != "mxfp4" or setup.k % 128 == 0)
     name = ("mxw_kernel" if setup.fmt == "mxfp4" else "f8w_kernel") if big \
         else "tile_gemm_kernel"
     return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"

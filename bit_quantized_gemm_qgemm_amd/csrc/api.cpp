@@ -39,22 +39,25 @@ bool weight_only_tiled(int64_t M, int64_t N) {
          (M >= kWeightOnlyTileLongM && tiles >= kWeightOnlyTileLongMinTiles);
 }
 // FP8 and MXFP4 GEMMs take the small-M kernel (16-row slabs, up to four per
-// workgroup) up to M = 128, and above that while the tiled kernels' grid
-// stays small: FP8 up to M = 512 while M * N <= 2.6e6 (5 * 2^19), MXFP4 up
-// to M = 256 while M * N <= 2^21.  Above, the tile kernels.  The small-M
-// kernel's time grows with M * N * K, while the tiled kernels take about one
-// 256 x 256 x K tile per CU whatever M is.  Measured on MI355X (us, small-M
-// kernel / tile kernels):
-//   FP8 K = N = 8192:   M = 144 47 / 69, 256 48 / 73, 384 71 / 70, 512 95 / 73
+// workgroup) up to M = 64; from 65 to 128 rows unless N is wide (FP8 N >=
+// 24576, MXFP4 N >= 16384), where one row of 256 x 256 tiles is faster; and
+// above that while the tiled kernels' grid stays small: FP8 up to M = 512
+// while M * N <= 2.6e6 (5 * 2^19), MXFP4 up to M = 256 while M * N <= 2^21.
+// Otherwise the tile kernels.  The small-M kernel's time grows with M * N * K,
+// while the tiled kernels take about one 256 x 256 x K tile per CU whatever M
+// is.  Measured on MI355X (us, small-M kernel / tile kernels):
+//   FP8 K = N = 8192:   M = 128 30 / 68, 144 47 / 69, 256 48 / 73, 384 71 / 70,
+//                       512 95 / 73
 //   FP8 K = N = 4096:   M = 512 37 / 40, 768 54 / 40
-//   FP8 K = 8192, N = 28672: M = 144 123 / 80
-//   MXFP4 K = N = 8192: M = 192 39 / 50, 256 49 / 56, 384 70 / 46
+//   FP8 K = 8192, N = 28672: M = 72 92 / 78, 128 86 / 72, 144 123 / 80
+//   FP8 K = 4096, N = 16384: M = 96 28 / 38
+//   MXFP4 K = N = 8192: M = 128 27 / 44, 192 39 / 50, 256 49 / 56, 384 70 / 46
 //   MXFP4 K = N = 4096: M = 256 24 / 26, 384 34 / 25
-//   MXFP4 K = 8192, N = 28672: M = 144 117 / 52
-// Up to M = 128 the small-M kernel stays, also where 128 x 128 tiles would
-// win by a few percent for very wide N (FP8 N = 28672, M = 128: 86 / 80).
+//   MXFP4 K = 8192, N = 28672: M = 72 87 / 48, 128 85 / 51, 144 117 / 52
+//   MXFP4 K = 4096, N = 16384: M = 72 27.6 / 24.7, 128 27.8 / 27.0
 bool scaled_small_m(int fmt, int64_t M, int64_t N) {
-  if (M <= 128) return true;
+  if (M <= 64) return true;
+  if (M <= 128) return N < (fmt == QGEMM_FP8 ? 24576 : 16384);
   if (fmt == QGEMM_FP8) return M <= 512 && M * N <= 2621440;
   return M <= 256 && M * N <= 2097152;
 }

@@ -301,11 +301,13 @@ bool pipe_fits(int fmt, int64_t M, int64_t N, int64_t K, int64_t group_k) {
 hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const void* w_packed,
                             const float* scale_a, const float* scale_b, void* c, int64_t M,
                             int64_t N, int64_t K, hipStream_t stream) {
-  // large tiles once both output dimensions fill them and K spans at least
-  // two 256-element tiles; the 128 x 128 kernel covers the rest (and MXFP4 K
-  // that is not a multiple of 128, whose scale rows the 4-byte copies of the
-  // large kernel cannot split)
-  const bool big = M > 128 && N > 128 && cdiv(K, kTileK8) >= 2 && pipe_fits(fmt, M, N, K, 0);
+  // large tiles once N exceeds 128, M exceeds 64 (the dispatch sends M <= 128
+  // here only for wide N, where one row of 256 x 256 tiles beats both the
+  // small-M kernel and 128 x 128 tiles) and K spans at least two 128-element
+  // tiles; the 128 x 128 kernel covers the rest (and MXFP4 K that is not a
+  // multiple of 128, whose scale rows the 4-byte copies of the large kernel
+  // cannot split)
+  const bool big = M > 64 && N > 128 && cdiv(K, kTileK8) >= 2 && pipe_fits(fmt, M, N, K, 0);
   if (fmt == 3) {
     if (big && K % 128 == 0 && cdiv(K, kTileK4) >= 2)
       return launch_mxfp4_256(a, a_e8m0, w_packed, c, M, N, K, stream);

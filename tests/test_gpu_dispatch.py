@@ -4,9 +4,11 @@ and the tiled kernels.
 The weight-only GEMMs (per-column INT4 / INT8, grouped, NVFP4 weights) take
 the 256 x 256 tiled kernel from M = 256 on once its grid of
 T = ceil(M / 256) * ceil(N / 256) tiles reaches 192, or from M = 640 once
-T >= 48; otherwise the small-M kernel.  FP8 takes the small-M kernel up to
-M = 128, and up to M = 512 while M * N <= 2621440; MXFP4 up to M = 128, and
-up to M = 256 while M * N <= 2^21; otherwise the tiled kernels.  Each pair
+T >= 48; otherwise the small-M kernel.  FP8 and MXFP4 take the small-M
+kernel up to M = 64, from 65 to 128 rows unless N is wide (FP8 N >= 24576,
+MXFP4 N >= 16384: one row of 256 x 256 tiles), and above that FP8 up to
+M = 512 while M * N <= 2621440, MXFP4 up to M = 256 while M * N <= 2^21;
+otherwise the tiled kernels.  Each pair
 of cases below sits on the two sides of one edge of a rule, so both kernels
 run at the shapes where the dispatch switches.  Every output is checked against the oracle
 (bar: |Y - Y_ref| <= 1e-2 * (|X| @ |W_deq|) + 1e-3 elementwise) and each
@@ -114,6 +116,11 @@ FP8_EDGES = [
     (129, 20336, 256),    # tiles
     (512, 64, 272),       # small-M kernel
     (513, 64, 272),       # M > 512: 128 x 128 tiles (N <= 128)
+    (128, 24560, 256),    # 65 .. 128 rows, N < 24576: small-M kernel
+    (128, 24576, 256),    # N >= 24576: one row of 256 x 256 tiles
+    (64, 25000, 272),     # M <= 64: small-M kernel
+    (65, 25000, 272),     # 256 x 256 tiles with 65 of their 256 rows, K tail of 16
+    (100, 24600, 128),    # one 128-element K tile: 128 x 128 tiles
 ]
 
 
@@ -138,6 +145,11 @@ MX_EDGES = [
     (257, 200, 640),      # M > 256: 256 x 256 tiles
     (200, 10485, 288),    # small-M kernel (M * N = 2097000)
     (200, 10500, 288),    # tiles: K = 288 is not a multiple of 128, the 128 x 128 kernel
+    (128, 16368, 512),    # 65 .. 128 rows, N < 16384: small-M kernel
+    (128, 16384, 512),    # N >= 16384: one row of 256 x 256 tiles
+    (64, 17000, 640),     # M <= 64: small-M kernel
+    (65, 17000, 640),     # 256 x 256 tiles with 65 of their 256 rows
+    (100, 16400, 288),    # K = 288: 128 x 128 tiles
 ]
 
 
