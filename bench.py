@@ -112,8 +112,9 @@ class Setup:
         self.name = name
         fmt, ms, n, k = WORKLOADS[name]
         self.fmt, self.ms, self.n, self.k = fmt, ms, n, k
-        # up to M = 128 the calls stream the weight through the small-M kernel
-        # (reported as weight GB/s against HBM); beyond, the tile kernels
+        # workloads with M up to 128 are reported as weight GB/s against HBM
+        # (their calls stream the weight through the small-M kernel); larger
+        # ones as TFLOP/s
         self.kind = "decode" if max(ms) <= SMALL_M_MAX else "tile"
         self.explicit = None   # W8A16 square: the explicit dequantize-then-matmul comparison
         dev = torch.device("cuda:0")

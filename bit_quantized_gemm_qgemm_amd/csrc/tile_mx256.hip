@@ -1,5 +1,5 @@
-// 256 x 256 matrix-core kernels for MXFP4 x MXFP4 and FP8 e4m3fn (M and N
-// above 128).
+// 256 x 256 matrix-core kernels for MXFP4 x MXFP4 and FP8 e4m3fn (M above 64,
+// N above 128).
 //
 // The MXFP4 page (section 2) tiles C into B_M x B_N blocks per workgroup and
 // sums, per 32-element micro-block, S_A * S_W * dot(A, W) (eq. 1) with the
