@@ -711,38 +711,18 @@ def config_summary(line):
 
 
 def kernel_name(setup, m):
-    """Label of the kernel that runs a call with M rows (rocprofv3 lists the
-    mangled template instance)."""
+    """Label of the kernel that runs a call with M rows, as the library's own
+    dispatch query names it (rocprofv3 lists the mangled template instance)."""
+    import bit_quantized_gemm_qgemm_amd as qg
+    fmt = {"fp8_act": "fp8", "mxfp4_act": "mxfp4"}.get(setup.fmt, setup.fmt)
+    group_k = GROUP_K if fmt in ("w4a16_grouped", "w8a16_grouped") else 0
+    name = qg.qgemm_dispatch_kernel(fmt, m, setup.n, setup.k, group_k)
+    label = f"{name}[{fmt}, M={m}, N={setup.n}, K={setup.k}]"
     if setup.fmt == "fp8_act":
-        return (f"qgemm_fp8_act call: quantize kernels + decode_gemm_kernel[fp8, M={m}, "
-                f"N={setup.n}, K={setup.k}]")
+        return "qgemm_fp8_act call: quantize kernels + " + label
     if setup.fmt == "mxfp4_act":
-        return (f"qgemm_mxfp4_act call: quantize_mxfp4_kernel + mxw_kernel[mxfp4, M={m}, "
-                f"N={setup.n}, K={setup.k}]")
-    if setup.kind == "decode":
-        return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
-    # same rules as the library's dispatch
-    if setup.fmt in ("w4a16", "w8a16", "w4a16_grouped", "w8a16_grouped", "nvfp4"):
-        tiles = -(-m // 256) * -(-setup.n // 256)
-        big = (m >= 256 and setup.n > 128 and setup.k % 8 == 0
-               and (tiles >= 192 or (m >= 640 and tiles >= 48)))
-        name = "pipe256_kernel" if big else "decode_gemm_kernel"
-        return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
-    if m <= 64:
-        small = True
-    elif m <= 128:
-        small = setup.n < (24576 if setup.fmt == "fp8" else 16384)
-    elif setup.fmt == "fp8":
-        small = m <= 512 and m * setup.n <= 2621440
-    else:
-        small = m <= 256 and m * setup.n <= 2097152
-    if small:
-        return f"decode_gemm_kernel[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
-    k_tiles = -(-setup.k // (256 if setup.fmt == "mxfp4" else 128))
-    big = m > 64 and setup.n > 128 and k_tiles >= 2 and (setup.fmt != "mxfp4" or setup.k % 128 == 0)
-    name = ("mxw_kernel" if setup.fmt == "mxfp4" else "f8w_kernel") if big \
-        else "tile_gemm_kernel"
-    return f"{name}[{setup.fmt}, M={m}, N={setup.n}, K={setup.k}]"
+        return "qgemm_mxfp4_act call: quantize_mxfp4_kernel + " + label
+    return label
 
 
 def main():

@@ -32,6 +32,7 @@ _I64 = ctypes.c_int64
 _SIGNATURES = [
     ("qgemm_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("qgemm_abi_version", ctypes.c_int, []),
+    ("qgemm_dispatch_kernel", ctypes.c_int, [ctypes.c_int, _I64, _I64, _I64, _I64]),
     ("qgemm_prepack_bytes", ctypes.c_int64, [ctypes.c_int, _I64, _I64]),
     ("qgemm_prepack", ctypes.c_int, [ctypes.c_int, _P, _P, _P, _I64, _I64, _P]),
     ("qgemm_quantize_mxfp4", ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
@@ -122,6 +123,23 @@ def _out(out, M, N, dtype, device):
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out must be [{M}, {N}], got {list(out.shape)}")
     return out
+
+
+# qgemm_dispatch_kernel results: the kernel each launches, by its name in
+# profiler traces
+KERNELS = {0: None, 1: "decode_gemm_kernel", 2: "pipe256_kernel", 3: "mxw_kernel",
+           4: "f8w_kernel", 5: "tile_gemm_kernel"}
+
+
+def qgemm_dispatch_kernel(fmt, M, N, K, group_k=0):
+    """Name of the kernel a GEMM call of this format and sizes launches (None
+    when M or N is 0); host-only.  The fused-quantization calls dispatch as
+    "mxfp4" / "fp8"."""
+    st = lib().qgemm_dispatch_kernel(int(FORMATS.get(fmt, fmt)), int(M), int(N), int(K),
+                                     int(group_k))
+    if st < 0:
+        raise QgemmError(int(st), "qgemm_dispatch_kernel")
+    return KERNELS[st]
 
 
 def qgemm_prepack_bytes(fmt, K, N):

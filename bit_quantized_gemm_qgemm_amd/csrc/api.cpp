@@ -125,6 +125,37 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 // A pointer may be NULL only when its array holds no elements.
 bool present(const void* p, int64_t elems) { return p != nullptr || elems == 0; }
 
+// The kernel a GEMM call of format fmt launches (M, N, K and group_k already
+// validated): the one dispatch every entry point and qgemm_dispatch_kernel
+// apply.  The fused-quantization calls dispatch as their GEMM format.
+int kernel_for(int fmt, int64_t M, int64_t N, int64_t K, int64_t group_k) {
+  if (M == 0 || N == 0) return QGEMM_KERNEL_NONE;
+  switch (fmt) {
+    case QGEMM_W4A16:
+    case QGEMM_W8A16:   // fp16 X rows of the tile kernel must be 16-byte aligned
+      return weight_only_tiled(M, N) && K > 0 && K % 8 == 0 &&
+                     qgemm::pipe_fits(fmt, M, N, K, 0)
+                 ? QGEMM_KERNEL_WEIGHT_ONLY_256
+                 : QGEMM_KERNEL_SMALL_M;
+    case QGEMM_NVFP4:   // K % 16 == 0
+      return weight_only_tiled(M, N) && K > 0 && qgemm::pipe_fits(fmt, M, N, K, 0)
+                 ? QGEMM_KERNEL_WEIGHT_ONLY_256
+                 : QGEMM_KERNEL_SMALL_M;
+    case QGEMM_W4A16_GROUPED:
+    case QGEMM_W8A16_GROUPED:   // K % 32 == 0
+      return weight_only_tiled(M, N) && K > 0 && qgemm::pipe_fits(fmt, M, N, K, group_k)
+                 ? QGEMM_KERNEL_WEIGHT_ONLY_256
+                 : QGEMM_KERNEL_SMALL_M;
+    case QGEMM_MXFP4:
+    case QGEMM_FP8:
+      if (scaled_small_m(fmt, M, N)) return QGEMM_KERNEL_SMALL_M;
+      if (!qgemm::tile_is_big(fmt, M, N, K)) return QGEMM_KERNEL_TILE_128;
+      return fmt == QGEMM_MXFP4 ? QGEMM_KERNEL_MXFP4_256 : QGEMM_KERNEL_FP8_256;
+    default:
+      return QGEMM_ERR_FORMAT;
+  }
+}
+
 int weight_only(int fmt, const void* x, const void* w_packed, const void* scales, void* y,
                 int64_t M, int64_t N, int64_t K, void* stream) {
   int st = check_sizes(fmt, M, N, K);
@@ -139,7 +170,7 @@ int weight_only(int fmt, const void* x, const void* w_packed, const void* scales
   // Large M: LDS-tiled matrix-core kernel (each weight byte is read once per
   // 256 rows).  Otherwise the register-dequant kernel in 16-row slabs, the
   // bandwidth path of decode.
-  if (weight_only_tiled(M, N) && K > 0 && K % 8 == 0 && qgemm::pipe_fits(fmt, M, N, K, 0))
+  if (kernel_for(fmt, M, N, K, 0) == QGEMM_KERNEL_WEIGHT_ONLY_256)
     return launched(qgemm::launch_weight_only_tile(fmt, x, w_packed, scales, y, M, N, K,
                                                    as_stream(stream)));
   return launched(qgemm::launch_decode_gemm(fmt, x, w_packed, scales, nullptr, nullptr, y, M, N,
@@ -165,7 +196,7 @@ int grouped_gemm(int fmt, const void* x, const void* w_packed, void* y, int64_t 
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
   // K % 32 == 0 here, so fp16 X rows are 16-byte aligned
-  if (weight_only_tiled(M, N) && K > 0 && qgemm::pipe_fits(fmt, M, N, K, group_k))
+  if (kernel_for(fmt, M, N, K, group_k) == QGEMM_KERNEL_WEIGHT_ONLY_256)
     return launched(qgemm::launch_weight_only_tile_grouped(fmt, x, w_packed, y, M, N, K, group_k,
                                                            as_stream(stream)));
   return launched(qgemm::launch_decode_grouped(fmt, x, w_packed, y, M, N, K, group_k,
@@ -199,7 +230,7 @@ int fp8_act_run(const float* a, const void* b_packed, const float* scale_b, void
   int st = launched(
       qgemm::launch_quantize_fp8_ws(a, M * K, codes, scale_a, partials, as_stream(stream)));
   if (st != QGEMM_OK || N == 0) return st;
-  if (scaled_small_m(QGEMM_FP8, M, N))
+  if (kernel_for(QGEMM_FP8, M, N, K, 0) == QGEMM_KERNEL_SMALL_M)
     return launched(qgemm::launch_decode_gemm(QGEMM_FP8, codes, b_packed, nullptr, scale_a,
                                               scale_b, c, M, N, K, as_stream(stream)));
   return launched(qgemm::launch_tile_gemm(QGEMM_FP8, codes, nullptr, b_packed, scale_a, scale_b,
@@ -255,7 +286,19 @@ const char* qgemm_status_string(int status) {
   }
 }
 
-int qgemm_abi_version(void) { return 102; }
+int qgemm_abi_version(void) { return 103; }
+
+int qgemm_dispatch_kernel(int fmt, int64_t M, int64_t N, int64_t K, int64_t group_k) {
+  int st;
+  if (fmt == QGEMM_W4A16_GROUPED || fmt == QGEMM_W8A16_GROUPED)
+    st = check_grouped(fmt, M, N, K, group_k);
+  else if (valid_format(fmt))
+    st = check_sizes(fmt, M, N, K);
+  else
+    return QGEMM_ERR_FORMAT;
+  if (st != QGEMM_OK) return st;
+  return kernel_for(fmt, M, N, K, group_k);
+}
 
 int64_t qgemm_prepack_bytes(int fmt, int64_t K, int64_t N) {
   if (!valid_format(fmt)) return QGEMM_ERR_FORMAT;
@@ -313,7 +356,7 @@ int qgemm_nvfp4(const void* x, const void* w_packed, const float* global_scale, 
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
   // K % 16 == 0 here, so fp16 X rows are 16-byte aligned
-  if (weight_only_tiled(M, N) && K > 0 && qgemm::pipe_fits(QGEMM_NVFP4, M, N, K, 0))
+  if (kernel_for(QGEMM_NVFP4, M, N, K, 0) == QGEMM_KERNEL_WEIGHT_ONLY_256)
     return launched(qgemm::launch_weight_only_tile_nvfp4(x, w_packed, global_scale, y, M, N, K,
                                                          as_stream(stream)));
   return launched(qgemm::launch_decode_nvfp4(x, w_packed, global_scale, y, M, N, K,
@@ -374,7 +417,7 @@ int qgemm_mxfp4(const void* a_codes, const void* a_e8m0, const void* w_packed, v
   if (!aligned(a_codes, 16) || !aligned(w_packed, 16) || !aligned(c, 16)) return QGEMM_ERR_ALIGN;
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
-  if (scaled_small_m(QGEMM_MXFP4, M, N))
+  if (kernel_for(QGEMM_MXFP4, M, N, K, 0) == QGEMM_KERNEL_SMALL_M)
     return launched(qgemm::launch_decode_gemm(QGEMM_MXFP4, a_codes, w_packed, a_e8m0, nullptr,
                                               nullptr, c, M, N, K, as_stream(stream)));
   return launched(qgemm::launch_tile_gemm(QGEMM_MXFP4, a_codes, a_e8m0, w_packed, nullptr,
@@ -392,7 +435,7 @@ int qgemm_fp8(const void* a, const void* b_packed, const float* scale_a, const f
   if (!aligned(scale_a, 4) || !aligned(scale_b, 4)) return QGEMM_ERR_ALIGN;
   if (M == 0 || N == 0) return QGEMM_OK;
   if ((st = check_device()) != QGEMM_OK) return st;
-  if (scaled_small_m(QGEMM_FP8, M, N))
+  if (kernel_for(QGEMM_FP8, M, N, K, 0) == QGEMM_KERNEL_SMALL_M)
     return launched(qgemm::launch_decode_gemm(QGEMM_FP8, a, b_packed, nullptr, scale_a, scale_b,
                                               c, M, N, K, as_stream(stream)));
   return launched(qgemm::launch_tile_gemm(QGEMM_FP8, a, nullptr, b_packed, scale_a, scale_b, c, M,
@@ -427,7 +470,7 @@ int qgemm_mxfp4_act(const float* a, const void* w_packed, void* c, void* workspa
     if (st != QGEMM_OK) return st;
   }
   if (N == 0) return QGEMM_OK;
-  if (scaled_small_m(QGEMM_MXFP4, M, N))
+  if (kernel_for(QGEMM_MXFP4, M, N, K, 0) == QGEMM_KERNEL_SMALL_M)
     return launched(qgemm::launch_decode_gemm(QGEMM_MXFP4, codes, w_packed, e8m0, nullptr,
                                               nullptr, c, M, N, K, as_stream(stream)));
   return launched(qgemm::launch_tile_gemm(QGEMM_MXFP4, codes, e8m0, w_packed, nullptr, nullptr, c,

@@ -172,6 +172,8 @@ hipError_t launch_decode_grouped(int fmt, const void* x, const void* w_packed, v
 // (every operand below 2^31 bytes).  Larger ones take the kernels that
 // address with 64 bits (the 128 x 128 tile kernel, the small-M kernel).
 bool pipe_fits(int fmt, int64_t M, int64_t N, int64_t K, int64_t group_k);
+// Whether launch_tile_gemm takes a 256 x 256 kernel (else 128 x 128 tiles).
+bool tile_is_big(int fmt, int64_t M, int64_t N, int64_t K);
 
 // LDS-tiled matrix-core path for W4A16 / W8A16 at large M (fp16 X with K a
 // positive multiple of 8; 256 x 256 output tiles).

@@ -298,19 +298,23 @@ bool pipe_fits(int fmt, int64_t M, int64_t N, int64_t K, int64_t group_k) {
   return g.total < lim;   // the code segment and any scale or metadata segment
 }
 
+// Large tiles once N exceeds 128, M exceeds 64 (the dispatch sends M <= 128
+// here only for wide N, where one row of 256 x 256 tiles beats both the
+// small-M kernel and 128 x 128 tiles) and K spans at least two 128-element
+// tiles; the 128 x 128 kernel covers the rest (and MXFP4 K that is not a
+// multiple of 128, whose scale rows the 4-byte copies of the large kernel
+// cannot split, or that spans a single 256-element step).
+bool tile_is_big(int fmt, int64_t M, int64_t N, int64_t K) {
+  const bool big = M > 64 && N > 128 && cdiv(K, kTileK8) >= 2 && pipe_fits(fmt, M, N, K, 0);
+  return fmt == 3 ? big && K % 128 == 0 && cdiv(K, kTileK4) >= 2 : big;
+}
+
 hipError_t launch_tile_gemm(int fmt, const void* a, const void* a_e8m0, const void* w_packed,
                             const float* scale_a, const float* scale_b, void* c, int64_t M,
                             int64_t N, int64_t K, hipStream_t stream) {
-  // large tiles once N exceeds 128, M exceeds 64 (the dispatch sends M <= 128
-  // here only for wide N, where one row of 256 x 256 tiles beats both the
-  // small-M kernel and 128 x 128 tiles) and K spans at least two 128-element
-  // tiles; the 128 x 128 kernel covers the rest (and MXFP4 K that is not a
-  // multiple of 128, whose scale rows the 4-byte copies of the large kernel
-  // cannot split)
-  const bool big = M > 64 && N > 128 && cdiv(K, kTileK8) >= 2 && pipe_fits(fmt, M, N, K, 0);
+  const bool big = tile_is_big(fmt, M, N, K);
   if (fmt == 3) {
-    if (big && K % 128 == 0 && cdiv(K, kTileK4) >= 2)
-      return launch_mxfp4_256(a, a_e8m0, w_packed, c, M, N, K, stream);
+    if (big) return launch_mxfp4_256(a, a_e8m0, w_packed, c, M, N, K, stream);
     return launch_tiles<true, 4, 4>(a, a_e8m0, w_packed, scale_a, scale_b, c, M, N, K, stream);
   }
   if (fmt == 4) {

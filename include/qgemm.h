@@ -89,6 +89,29 @@ const char* qgemm_status_string(int status);
 /* ABI version of this header (major * 100 + minor). */
 int qgemm_abi_version(void);
 
+/* The kernels a GEMM call can launch (qgemm_dispatch_kernel). */
+enum qgemm_kernel {
+  QGEMM_KERNEL_NONE = 0,            /* M = 0 or N = 0: nothing is launched          */
+  QGEMM_KERNEL_SMALL_M = 1,         /* register-dequant kernel in 16-row slabs      */
+  QGEMM_KERNEL_WEIGHT_ONLY_256 = 2, /* weight-only formats: 256 x 256 matrix tiles  */
+  QGEMM_KERNEL_MXFP4_256 = 3,       /* MXFP4: 256 x 256 matrix tiles                */
+  QGEMM_KERNEL_FP8_256 = 4,         /* FP8: 256 x 256 matrix tiles                  */
+  QGEMM_KERNEL_TILE_128 = 5         /* MXFP4 / FP8: 128 x 128 matrix tiles          */
+};
+
+/*
+ * qgemm_dispatch_kernel -- which kernel a GEMM call of format fmt with these
+ * sizes launches: the dispatch by M, N and K that every GEMM entry point
+ * applies (the W8A16 page's performance and autotune notes and the FP8
+ * page's parameter list choose a tile configuration per M, N, K; here a
+ * fixed rule fitted to measurements does).  qgemm_mxfp4_act and
+ * qgemm_fp8_act(_noalloc) dispatch as QGEMM_MXFP4 and QGEMM_FP8.  group_k is
+ * read for the grouped formats only.  Host-only: touches no device.  Returns
+ * a qgemm_kernel value, or a negative status for a format or sizes the entry
+ * point would reject (QGEMM_ERR_FORMAT, QGEMM_ERR_SHAPE).
+ */
+int qgemm_dispatch_kernel(int fmt, int64_t M, int64_t N, int64_t K, int64_t group_k);
+
 /*
  * qgemm_prepack_bytes -- size in bytes of the opaque packed weight buffer for
  * a K x N weight (N output columns; for MXFP4, N rows of W[N,K]).  Host-only,

@@ -90,6 +90,19 @@ int main() {
          QGEMM_ERR_ARCH);
   unsetenv("QGEMM_ARCH_OVERRIDE");
 
+  // the dispatch query (host-only)
+  expect("dispatch w8a16 decode", qgemm_dispatch_kernel(QGEMM_W8A16, 16, 11008, 4096, 0),
+         QGEMM_KERNEL_SMALL_M);
+  expect("dispatch w4a16 square", qgemm_dispatch_kernel(QGEMM_W4A16, 4096, 4096, 4096, 0),
+         QGEMM_KERNEL_WEIGHT_ONLY_256);
+  expect("dispatch mxfp4 square", qgemm_dispatch_kernel(QGEMM_MXFP4, 8192, 8192, 8192, 0),
+         QGEMM_KERNEL_MXFP4_256);
+  expect("dispatch empty", qgemm_dispatch_kernel(QGEMM_FP8, 0, 64, 64, 0), QGEMM_KERNEL_NONE);
+  expect("dispatch format", qgemm_dispatch_kernel(99, 4, 4, 32, 0), QGEMM_ERR_FORMAT);
+  expect("dispatch shape", qgemm_dispatch_kernel(QGEMM_MXFP4, 4, 4, 40, 0), QGEMM_ERR_SHAPE);
+  expect("dispatch group", qgemm_dispatch_kernel(QGEMM_W4A16_GROUPED, 4, 4, 64, 48),
+         QGEMM_ERR_SHAPE);
+
   std::printf("%s (%d failures)\n", failures ? "FAILED" : "ok", failures);
   return failures ? 1 : 0;
 }

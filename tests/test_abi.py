@@ -42,7 +42,7 @@ def test_header_declares_the_expected_entry_points():
                  "qgemm_status_string", "qgemm_abi_version", "qgemm_prepack_grouped",
                  "qgemm_prepack_grouped_bytes", "qgemm_w4a16_grouped", "qgemm_w8a16_grouped",
                  "qgemm_nvfp4", "qgemm_act_workspace_bytes", "qgemm_mxfp4_act",
-                 "qgemm_fp8_act", "qgemm_fp8_act_noalloc"):
+                 "qgemm_fp8_act", "qgemm_fp8_act_noalloc", "qgemm_dispatch_kernel"):
         assert want in names
 
 
@@ -60,7 +60,7 @@ def test_status_strings(lib):
         s = qg.status_string(st)
         assert s and s != "unknown status"
     assert qg.status_string(12345) == "unknown status"
-    assert lib.qgemm_abi_version() == 102
+    assert lib.qgemm_abi_version() == 103
 
 
 def test_prepack_bytes(lib):
