@@ -611,9 +611,12 @@ def run(name, steps, warmup, with_cpu, use_graph, with_ceiling=True):
     per_call = per_call_times(setup)
     per_call_warm = per_call_times(setup, warm=True)
     decode = setup.kind == "decode"
-    # the dominant kernel is the call with the longest average duration; each
-    # call's launches were timed with HIP events on the launch stream
-    dom = max(range(len(setup.calls)), key=lambda i: per_call[i])
+    # the dominant kernel is the call with the longest average duration (of
+    # calls within 2% of the longest, the one with the largest M, so that
+    # near-ties do not flip between runs); each call's launches were timed
+    # with HIP events on the launch stream
+    longest = max(per_call)
+    dom = max(i for i in range(len(setup.calls)) if per_call[i] >= 0.98 * longest)
     _, dom_alg, _, dom_flops = setup.calls[dom]
     if decode:
         value = wgt * steps / wall / 1e9
