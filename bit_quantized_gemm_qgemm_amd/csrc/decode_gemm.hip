@@ -563,8 +563,9 @@ struct DecodeConfig {
 };
 
 // Whether a launch stages its activation tiles through LDS: with more than
-// eight rows, eight waves, and at most 8 copy instructions per tile (fp16 X:
-// up to two slabs); X must span fewer than 2^31 bytes (32-bit buffer
+// eight rows, eight waves (or four with at least 16 K tiles: the launches
+// with several row blocks), and at most 8 copy instructions per tile (fp16
+// X: up to two slabs); X must span fewer than 2^31 bytes (32-bit buffer
 // offsets).  Measured on MI355X (K = 4096 / 8192, N = 8192 .. 28672, each
 // shape timed staged and direct in alternation, best of three): at M = 12
 // the two are within 1 %; at M = 16 staging saves 1 % (FP8) to 5 % (INT8),
@@ -594,11 +595,12 @@ int decode_waves(int64_t M, int s, int64_t KT) {
   return KT < 16 || (s > 1 && M > 16 * s) ? 4 : 8;
 }
 
-// Launch shape: about one workgroup per CU.  Measured on MI355X at the decode
-// workloads (W8A16 K=4096 N=11008, W4A16 K=8192 N=28672, FP8 K=N=8192, M = 1
-// .. 16): the weight streams fastest when the grid has close to 256
-// workgroups, each owning G = ceil(column groups / 256) column groups; more,
-// smaller workgroups leave the CUs unevenly loaded and fewer leave CUs idle.
+// Launch shape with one row block: about one workgroup per CU.  Measured on
+// MI355X at the decode workloads (W8A16 K=4096 N=11008, W4A16 K=8192
+// N=28672, FP8 K=N=8192, M = 1 .. 16): the weight streams fastest when the
+// grid has close to 256 workgroups, each owning G = ceil(column groups / 256)
+// column groups; more, smaller workgroups leave the CUs unevenly loaded and
+// fewer leave CUs idle.
 // G is capped by the register budget (8 for INT4, 4 for the byte formats);
 // INT8 keeps three K tiles in flight, the others two; short K uses four
 // waves.  Above 16 rows a workgroup takes 2 (M <= 32) or 4 slabs, so each
