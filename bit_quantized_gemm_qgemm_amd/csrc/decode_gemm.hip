@@ -76,32 +76,51 @@ struct Chunk {
 };
 
 // Per-lane and per-workgroup addressing of one launch.  Scalar (wave-uniform)
-// parts stay in SGPRs; each lane adds a 32-bit offset.
+// parts stay in SGPRs; each lane adds a 32-bit offset.  Activation and A
+// scale offsets count from row m0, the workgroup's first row.
 struct DecodeAddr {
-  const uint8_t* x;       // activations
+  const uint8_t* x;       // activations, row m0
+  uint32_t xrows;         // bytes of X from row m0 to its end
   uint32_t xlane[4];      // per slab: byte offset of this lane's row and first K piece
   const uint8_t* w;       // first weight tile of this workgroup
   int64_t cg_stride;      // bytes between column groups
+  uint32_t wspan;         // bytes of weights from any of its tiles on (at most 2^31 - 1)
   int cg_last;            // last valid group index relative to this workgroup
   uint32_t wlane;         // 16 * lane
   int K;
   int g;                  // lane group, lane >> 4
   const uint8_t* meta;    // grouped / NVFP4: first metadata tile of this workgroup;
-                          // MXFP4: the W scale segment
-  const uint8_t* asc;     // MXFP4: A scales, E8M0 [M, K/32]
+                          // MXFP4: the W scales of the 8-group band holding cg0
+  const uint8_t* asc;     // MXFP4: A scales, E8M0 [M, K/32], row m0
+  uint32_t arows;         // MXFP4: bytes of A scales from row m0 to their end
   uint32_t alane[4];      // MXFP4, per slab: this lane's row and block g in asc
   int cg0, KT;            // MXFP4: first column group, K tiles
   uint32_t wsh[8];        // MXFP4, per group: bit shift of its tile's scale byte
   int64_t meta_cg_stride; // bytes between column groups of metadata
   int meta_kt_stride;     // bytes of metadata per K tile
   uint32_t mlane;         // this lane's entries within a tile
-  // activations staged through LDS: the buffer over X, per (slab, copy
-  // instruction) the byte offset of this lane's 16 B in tile 0, and per
-  // operand piece this lane's byte offset within a staged slab
-  __amdgpu_buffer_rsrc_t xrsrc;
+  uint32_t mspan;         // bytes of metadata from any of its tiles on (at most 2^31 - 1)
+  // activations staged through LDS: per (slab, copy instruction) the byte
+  // offset of this lane's 16 B in tile 0, and per operand piece this lane's
+  // byte offset within a staged slab
   uint32_t xdma[8];
   uint32_t xrd[4];
 };
+
+// A raw buffer of `bytes` bytes at p.  Reads at or past `bytes` return zero
+// without touching memory; with bytes = 0 every read does.  A ring slot
+// whose K tile lies past the end issues the same loads as any other through
+// such an empty buffer: every slot then runs the same instructions on every
+// path, and the compiler's wait counts stay exact (a load under a branch
+// makes it wait for every load in flight at the merge, which empties the
+// ring once per tile).  `bytes` is wave-uniform and is chosen between
+// run-time values (a choice between constants such as ~0 and 0 is compiled
+// into a vector register, and each load then loops over its distinct values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dec_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+constexpr int kStreamLoad = 2;               // cache policy of the weight stream: nt
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr uint32_t kXOutOfRange = 0x80000000u;   // past every activation buffer
@@ -129,17 +148,24 @@ __device__ __forceinline__ int piece_k(int kt, int g, int p) {
 }
 
 // Load lane data of K tile `kt`: the lane's X (or A) pieces and each of the G
-// weight tiles.  X pieces past K read as zero.  Rows past M load row M-1
-// instead (their outputs are never stored); groups past the last column load
-// the last group (likewise discarded).
+// weight tiles; with live = false (a tile past the end) the same loads read
+// nothing.  X pieces past K read as zero when staged (and in the last rows
+// of X); loaded into registers they may hold the next row's values and are
+// zeroed at use (x_piece).  Rows past M load row M-1 instead (their outputs
+// are never stored); groups past the last column load the last group
+// (likewise discarded).
 template <int FMT, int G, bool X_ELEMENTWISE, int NGT = 0, int S = 1, bool XL = false>
 __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const DecodeAddr& ad,
-                                           int kt, uint8_t* xs = nullptr) {
-  constexpr int XV = DecodeTraits<FMT>::XV;
+                                           int kt, bool live, uint8_t* xs = nullptr) {
   constexpr int TB = DecodeTraits<FMT>::TB;
+  constexpr int RB = tile_x_bytes<FMT>();
   constexpr int PSTRIDE = (FMT == 4) ? 16 : 64;    // bytes between a lane's pieces
-  const uint8_t* xk = ad.x + (int64_t)kt * tile_x_bytes<FMT>();   // uniform
-  const bool full = (kt + 1) * tile_k<FMT>() <= ad.K;             // uniform
+  // the slots' loads are issued in ring order (the wait before a slot's
+  // compute then counts only the later slots' loads)
+  __builtin_amdgcn_sched_barrier(0);
+  // this tile's activations: from column kt * RB of row m0 to the end of X
+  const __amdgpu_buffer_rsrc_t xr =
+      dec_rsrc(ad.x + (int64_t)kt * RB, live ? ad.xrows - (uint32_t)kt * RB : 0u);
   if constexpr (XL) {
     // copy the S staged slabs of tile kt into this wave's LDS slot `xs`; in
     // a partial last tile, chunks past K take an offset past the buffer and
@@ -147,110 +173,102 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const Deco
     // chunk is wholly in or out).  Issued before the weight loads of the
     // chunk, with nothing scheduled across: the weight loads complete after
     // them.
-    constexpr int RB = tile_x_bytes<FMT>();
     constexpr int NI = x_copy_instrs<FMT>();
     constexpr int LPR = RB / 16;                  // lanes per row
     constexpr int KPC = tile_k<FMT>() / LPR;      // K elements per chunk
-    const uint32_t kb = (uint32_t)kt * RB;
+    const bool full = (kt + 1) * tile_k<FMT>() <= ad.K;   // uniform
     const int lane = __lane_id();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < S; ++q)
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        uint32_t off = ad.xdma[q * NI + i] + kb;
+        uint32_t off = ad.xdma[q * NI + i];
         if (!full) {
           const int r = i * (64 / LPR) + lane / LPR;
           const int c = (lane % LPR) ^ x_swz<FMT>(r);
           if (kt * tile_k<FMT>() + c * KPC >= ad.K) off = kXOutOfRange;
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ad.xrsrc, (lds_void_t*)(xs + q * 16 * RB + i * 1024),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(xs + q * 16 * RB + i * 1024),
                                                  16, off, 0, 0, 0);
       }
     __builtin_amdgcn_sched_barrier(0);
   } else if constexpr (!X_ELEMENTWISE) {
-    if (full) {
 #pragma unroll
-      for (int q = 0; q < S; ++q)
+    for (int q = 0; q < S; ++q)
 #pragma unroll
-        for (int p = 0; p < XV; ++p)
-          ch.x[q][p] = *reinterpret_cast<const uintx4*>(xk + ad.xlane[q] + PSTRIDE * p);
-    } else {
-      // K % 8 == 0 (fp16) or K % 16 == 0 (e4m3): a piece is wholly in or out
-#pragma unroll
-      for (int q = 0; q < S; ++q)
-#pragma unroll
-        for (int p = 0; p < XV; ++p) {
-          const int k = piece_k<FMT>(kt, ad.g, p);
-          ch.x[q][p] = (k < ad.K)
-                           ? *reinterpret_cast<const uintx4*>(xk + ad.xlane[q] + PSTRIDE * p)
-                           : uintx4{0, 0, 0, 0};
-        }
-    }
+      for (int p = 0; p < DecodeTraits<FMT>::XV; ++p)
+        ch.x[q][p] = __builtin_amdgcn_raw_buffer_load_b128(xr, ad.xlane[q] + PSTRIDE * p, 0, 0);
   } else {
     // K % 8 != 0 (fp16 only): rows are not 16-byte aligned; go element-wise
+    // (K and the tile decide each element; a tile past the end loads none)
     static_assert(S == 1 && FMT != 3 && FMT != 4, "the element-wise path: fp16 X, one slab");
-    constexpr int XB = 2;
-    const uint16_t* xr = reinterpret_cast<const uint16_t*>(xk + ad.xlane[0]);
+    const uint16_t* xr16 =
+        reinterpret_cast<const uint16_t*>(ad.x + (int64_t)kt * RB + ad.xlane[0]);
 #pragma unroll
-    for (int p = 0; p < XV; ++p) {
+    for (int p = 0; p < DecodeTraits<FMT>::XV; ++p) {
       uint32_t d[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = piece_k<FMT>(kt, ad.g, p) + 2 * j;
         const int e = (PSTRIDE / 2) * p + 2 * j;
-        const uint32_t lo = (k < ad.K) ? xr[e] : 0u;
-        const uint32_t hi = (k + 1 < ad.K) ? xr[e + 1] : 0u;
+        const uint32_t lo = (k < ad.K) ? xr16[e] : 0u;
+        const uint32_t hi = (k + 1 < ad.K) ? xr16[e + 1] : 0u;
         d[j] = lo | (hi << 16);
       }
       ch.x[0][p] = uintx4{d[0], d[1], d[2], d[3]};
     }
   }
   if constexpr (FMT == 3) {
-    // the E8M0 byte of block 8 kt + 4 h + g of each slab row; blocks past K
-    // take the unit scale (their codes read as zero)
-    const int nblk = ad.K / 32;
+    // the E8M0 byte of block 8 kt + 4 h + g of each slab row (blocks past K
+    // are replaced at use)
+    const __amdgpu_buffer_rsrc_t ar =
+        dec_rsrc(ad.asc + 8 * (int64_t)kt, live ? ad.arows - 8u * (uint32_t)kt : 0u);
 #pragma unroll
     for (int q = 0; q < S; ++q)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int blk = 8 * kt + 4 * h + ad.g;
-        ch.asc[q][h] = blk < nblk ? (uint32_t)ad.asc[ad.alane[q] + 8 * kt + 4 * h] : kE8M0One;
-      }
+      for (int h = 0; h < 2; ++h)
+        ch.asc[q][h] = __builtin_amdgcn_raw_buffer_load_b8(ar, ad.alane[q] + 4 * h, 0, 0);
   }
+  const __amdgpu_buffer_rsrc_t wr = dec_rsrc(ad.w + (int64_t)kt * TB, live ? ad.wspan : 0u);
+  // grouped / NVFP4: this tile's metadata; MXFP4: the W scales of blocks
+  // 8 kt .. 8 kt + 7 (512 B per 8 column groups and 128-element block,
+  // [lane][group], 2 KT blocks per band of 8 groups)
+  const __amdgpu_buffer_rsrc_t mr =
+      dec_rsrc(ad.meta + (int64_t)kt * (FMT == 3 ? 1024 : ad.meta_kt_stride),
+               live ? ad.mspan : 0u);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int gg = g < ad.cg_last ? g : ad.cg_last;                      // uniform
-    const uint8_t* t = ad.w + gg * ad.cg_stride + (int64_t)kt * TB;     // uniform
-    ch.w[g][0] = __builtin_nontemporal_load(reinterpret_cast<const uintx4*>(t + ad.wlane));
+    const int gg = g < ad.cg_last ? g : ad.cg_last;                // uniform
+    const uint32_t wo = (uint32_t)(gg * ad.cg_stride);             // uniform
+    ch.w[g][0] = __builtin_amdgcn_raw_buffer_load_b128(wr, ad.wlane, wo, kStreamLoad);
     if constexpr (DecodeTraits<FMT>::WV == 2)
-      ch.w[g][1] =
-          __builtin_nontemporal_load(reinterpret_cast<const uintx4*>(t + 1024 + ad.wlane));
+      ch.w[g][1] = __builtin_amdgcn_raw_buffer_load_b128(wr, ad.wlane + 1024, wo, kStreamLoad);
     if constexpr (FMT == 3) {
-      // the scale entries of this group's column for blocks 8 kt + 4 h + g:
-      // 512 B per (8 column tiles, 128-element block), [lane][tile]
       const int cg = ad.cg0 + gg;
+      const int band = (cg >> 3) - (ad.cg0 >> 3);                  // 0 or 1
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint8_t* e = ad.meta + ((int64_t)(cg >> 3) * (2 * ad.KT) + 2 * kt + h) * 512;
-        ch.meta[g][h] = *reinterpret_cast<const uint32_t*>(e + ad.wlane / 2 + 4 * ((cg >> 2) & 1));
+        const uint32_t mo = (uint32_t)(band * 1024 * ad.KT + 512 * h + 4 * ((cg >> 2) & 1));
+        ch.meta[g][h] = __builtin_amdgcn_raw_buffer_load_b32(mr, ad.wlane / 2, mo, 0);
       }
     }
     if constexpr (NGT > 0) {
-      const uint8_t* mt = ad.meta + gg * ad.meta_cg_stride + (int64_t)kt * ad.meta_kt_stride;
+      const uint32_t mo = (uint32_t)(gg * ad.meta_cg_stride);
       if constexpr (FMT == 7) {
-        ch.meta[g][0] = *reinterpret_cast<const uint32_t*>(mt + ad.mlane);   // 4 block scales
+        ch.meta[g][0] = __builtin_amdgcn_raw_buffer_load_b32(mr, ad.mlane, mo, 0);   // 4 block scales
       } else if constexpr (NGT == 4) {
-        const uintx4 v = *reinterpret_cast<const uintx4*>(mt + ad.mlane);
+        const uintx4 v = __builtin_amdgcn_raw_buffer_load_b128(mr, ad.mlane, mo, 0);
         ch.meta[g][0] = v[0]; ch.meta[g][1] = v[1]; ch.meta[g][2] = v[2]; ch.meta[g][3] = v[3];
       } else if constexpr (NGT == 2) {
-        const uintx2 v = *reinterpret_cast<const uintx2*>(mt + ad.mlane);
+        const uintx2 v = __builtin_amdgcn_raw_buffer_load_b64(mr, ad.mlane, mo, 0);
         ch.meta[g][0] = v[0]; ch.meta[g][1] = v[1];
       } else {
-        ch.meta[g][0] = *reinterpret_cast<const uint32_t*>(mt + ad.mlane);
+        ch.meta[g][0] = __builtin_amdgcn_raw_buffer_load_b32(mr, ad.mlane, mo, 0);
       }
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Operand piece p of slab q: from the chunk's registers or, staged, from the
@@ -262,6 +280,30 @@ __device__ __forceinline__ uintx4 x_piece(const Chunk<FMT, G, NGT, S>& ch, const
     return *reinterpret_cast<const uintx4*>(xs + q * 16 * tile_x_bytes<FMT>() + ad.xrd[p]);
   else
     return ch.x[q][p];
+}
+
+// Tile kt reaches past K (the last tile, when K is not a multiple of the
+// tile): clear the X pieces past K that were loaded into registers (they
+// hold the next row's values) and give MXFP4 blocks past K the unit A scale
+// (their codes are zero; the bytes after a row's last block belong to the
+// next row).  Staged pieces past K arrived as zeros.
+template <int FMT, int G, int NGT, int S, bool XL>
+__device__ __forceinline__ void cut_chunk(Chunk<FMT, G, NGT, S>& ch, const DecodeAddr& ad,
+                                          int kt) {
+  if constexpr (!XL) {
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+#pragma unroll
+      for (int p = 0; p < DecodeTraits<FMT>::XV; ++p)
+        if (piece_k<FMT>(kt, ad.g, p) >= ad.K) ch.x[q][p] = uintx4{0, 0, 0, 0};
+  }
+  if constexpr (FMT == 3) {
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (8 * kt + 4 * h + ad.g >= ad.K / 32) ch.asc[q][h] = kE8M0One;
+  }
 }
 
 template <int FMT, int G, int NGT = 0, int S = 1, bool XL = false>
@@ -417,22 +459,25 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
 
   DecodeAddr ad;
   ad.g = lane >> 4;
-  ad.x = x;
-  // rows past M load row M - 1 (their outputs are never stored)
+  // X from row m0 (rows past M load row M - 1: their outputs are never stored)
+  const int64_t rowbytes = FMT == 3 ? K / 2 : FMT == 4 ? (int64_t)K : 2 * (int64_t)K;
+  ad.x = x + (int64_t)m0 * rowbytes;
+  ad.xrows = (uint32_t)((int64_t)(M - m0) * rowbytes);
 #pragma unroll
   for (int q = 0; q < S; ++q) {
-    const int row = min(m0 + 16 * q + (lane & 15), M - 1);
+    const int r = min(m0 + 16 * q + (lane & 15), M - 1) - m0;
     if constexpr (FMT == 3) {   // 16 B of codes at k = 32 g of a block
-      ad.xlane[q] = (uint32_t)((int64_t)row * (K / 2) + 16 * ad.g);
-      ad.alane[q] = (uint32_t)((int64_t)row * (K / 32) + ad.g);
+      ad.xlane[q] = (uint32_t)((int64_t)r * rowbytes + 16 * ad.g);
+      ad.alane[q] = (uint32_t)((int64_t)r * (K / 32) + ad.g);
     } else {
       const int xb = FMT == 4 ? 1 : 2;
-      ad.xlane[q] = (uint32_t)(((int64_t)row * K + (FMT == 4 ? 32 : 8) * ad.g) * xb);
+      ad.xlane[q] = (uint32_t)((int64_t)r * rowbytes + (FMT == 4 ? 32 : 8) * ad.g * xb);
     }
   }
   if constexpr (FMT == 3) {
     // `scales` carries the A E8M0 bytes; meta_offset locates the W scales
-    ad.asc = reinterpret_cast<const uint8_t*>(scales);
+    ad.asc = reinterpret_cast<const uint8_t*>(scales) + (int64_t)m0 * (K / 32);
+    ad.arows = (uint32_t)((int64_t)(M - m0) * (K / 32));
     ad.cg0 = cg0;
     ad.KT = KT;
 #pragma unroll
@@ -447,18 +492,21 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
   ad.wlane = 16u * lane;
   ad.K = K;
   // grouped: NGT words per column and tile; NVFP4: 8 scale bytes per column
-  // and tile, the lanes of group g reading the dword of blocks 2s + (g >> 1)
+  // and tile, the lanes of group g reading the dword of blocks 2s + (g >> 1);
+  // MXFP4: the band of 8 column groups holding cg0 (2 KT blocks of 512 B)
   ad.meta_kt_stride = FMT == 7 ? kScaleTileBytes : 16 * (NGT > 0 ? NGT : 1) * 4;
   ad.meta_cg_stride = (int64_t)KT * ad.meta_kt_stride;
-  ad.meta = FMT == 3 ? wp + meta_offset : wp + meta_offset + (int64_t)cg0 * ad.meta_cg_stride;
+  ad.meta = FMT == 3 ? wp + meta_offset + (int64_t)(cg0 >> 3) * 1024 * KT
+                     : wp + meta_offset + (int64_t)cg0 * ad.meta_cg_stride;
   ad.mlane = FMT == 7 ? (uint32_t)((lane & 15) * 8 + 4 * (ad.g >> 1))
                       : (uint32_t)((lane & 15) * (NGT > 0 ? NGT : 1) * 4);
+  constexpr int64_t kSpanCap = 0x7fffffff;
+  ad.wspan = (uint32_t)min((int64_t)G * ad.cg_stride, kSpanCap);
+  ad.mspan = (uint32_t)min(FMT == 3 ? 2048 * (int64_t)KT : (int64_t)G * ad.meta_cg_stride,
+                           kSpanCap);
   if constexpr (XL) {
     constexpr int NI = x_copy_instrs<FMT>();
     constexpr int LPR = RB / 16;
-    const int64_t rowbytes = FMT == 3 ? K / 2 : FMT == 4 ? (int64_t)K : 2 * (int64_t)K;
-    ad.xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(x), (short)0,
-                                                 (int)(M * rowbytes), 0x00020000);
     // copy instruction i of slab q: row i * (64 / LPR) + lane / LPR of the
     // slab, chunk (lane % LPR) ^ swz(row); rows past M copy row M - 1
 #pragma unroll
@@ -466,7 +514,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int r = i * (64 / LPR) + lane / LPR;
-        const int row = min(m0 + 16 * q + r, M - 1);
+        const int row = min(m0 + 16 * q + r, M - 1) - m0;
         const int c = (lane % LPR) ^ x_swz<FMT>(r);
         ad.xdma[q * NI + i] = (uint32_t)(row * rowbytes + 16 * c);
       }
@@ -490,27 +538,48 @@ __global__ __launch_bounds__(NW * kWave) void decode_gemm_kernel(
     for (int g = 0; g < G; ++g) acc[q][g] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // K tiles wave, wave + NW, ...; a ring of D register buffers keeps D tiles
-  // of loads in flight per wave
+  // of loads in flight per wave.  The prologue fills every slot (a slot past
+  // the end through an empty buffer); the steady loop runs while every
+  // compute and every reload of its round is a real tile, with no branch
+  // around a load, so each compute waits only for its own slot; the last
+  // 2 D - 1 tiles at most take the guarded loop (which holds the last tile,
+  // the only one K can cut: X pieces loaded into registers and MXFP4 scales
+  // past K are replaced there).
+  constexpr bool CUTS = (!XL && !X_ELEMENTWISE) || FMT == 3;
   Chunk<FMT, G, NGT, S> ring[D];
   uint8_t* const xw = smem + wave * XWAVE;   // this wave's staging slots (XL)
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (wave + d * NW < KT)
-      load_chunk<FMT, G, X_ELEMENTWISE, NGT, S, XL>(ring[d], ad, wave + d * NW, xw + d * XSLOT);
-  for (int base = wave; base < KT; base += D * NW) {
+    load_chunk<FMT, G, X_ELEMENTWISE, NGT, S, XL>(ring[d], ad, wave + d * NW, wave + d * NW < KT,
+                                                  xw + d * XSLOT);
+  int base = wave;
+  for (; base + (2 * D - 1) * NW < KT; base += D * NW) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute_chunk<FMT, G, NGT, S, XL>(ring[d], acc, mk, ad, xw + d * XSLOT);
+      load_chunk<FMT, G, X_ELEMENTWISE, NGT, S, XL>(ring[d], ad, base + (d + D) * NW, true,
+                                                    xw + d * XSLOT);
+    }
+  }
+  for (; base < KT; base += D * NW) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int kt = base + d * NW;
       if (kt < KT) {
+        if (CUTS && (kt + 1) * tile_k<FMT>() > K) cut_chunk<FMT, G, NGT, S, XL>(ring[d], ad, kt);
         compute_chunk<FMT, G, NGT, S, XL>(ring[d], acc, mk, ad, xw + d * XSLOT);
         if (kt + D * NW < KT)
-          load_chunk<FMT, G, X_ELEMENTWISE, NGT, S, XL>(ring[d], ad, kt + D * NW,
+          load_chunk<FMT, G, X_ELEMENTWISE, NGT, S, XL>(ring[d], ad, kt + D * NW, true,
                                                         xw + d * XSLOT);
       }
     }
   }
-  // the partial-sum buffer reuses the staging slots of every wave
-  if constexpr (XL) __syncthreads();
+  // the partial-sum buffer reuses the staging slots of every wave: the
+  // empty copies of the slots past the end must have landed as well
+  if constexpr (XL) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
 
   // ---- reduce the NW partial tiles in a fixed order, one slab at a time
   const float fp8_scale = (FMT == 4) ? (*scale_a) * (*scale_b) : (FMT == 7) ? *scale_a : 1.0f;
@@ -602,8 +671,9 @@ int decode_waves(int64_t M, int s, int64_t KT) {
 // column groups; more, smaller workgroups leave the CUs unevenly loaded and
 // fewer leave CUs idle.
 // G is capped by the register budget (8 for INT4, 4 for the byte formats);
-// INT8 keeps three K tiles in flight, the others two; short K uses four
-// waves.  Above 16 rows a workgroup takes 2 (M <= 32) or 4 slabs, so each
+// every format keeps two K tiles in flight per wave (INT8 at M <= 16 with
+// three: 9.7 / 9.8 / 10.9 us at M = 1 / 4 / 16, K = 4096, N = 11008, against
+// 9.4 / 9.5 / 10.6 with two); short K uses four waves.  Above 16 rows a workgroup takes 2 (M <= 32) or 4 slabs, so each
 // weight tile is streamed and dequantized once for up to 64 rows instead of
 // once per 16; the activations of all slabs then share the register ring,
 // which caps G and the ring at two tiles.  The fp16-activation formats keep
@@ -621,7 +691,7 @@ DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
   const int64_t gmax = s == 1 ? (fmt == 1 ? 8 : 4) : s == 2 ? (fmt == 1 ? 7 : 4) : fmt == 3 ? 2 : 3;
   int64_t g = cdiv(CG, 256);
   g = g < 1 ? 1 : (g > gmax ? gmax : g);
-  DecodeConfig c{(int)g, decode_waves(M, s, KT), s == 1 && fmt == 2 ? 3 : 2, s, false};
+  DecodeConfig c{(int)g, decode_waves(M, s, KT), 2, s, false};
   c.xl = use_x_lds(fmt, M, c.nw, c.s, KT);
   return c;
 }
@@ -662,7 +732,7 @@ hipError_t launch_fmt_cfg(const DecodeConfig& c, const void* x, const void* w, c
   if constexpr (SS * (FMT == 3 || FMT == 4 ? 2 : 4) <= 8) {                                \
     QG_CASE(GG, 8, 2, SS, true) QG_CASE(GG, 4, 2, SS, true)                               \
   }
-  constexpr int DEPTH = FMT == 2 ? 3 : 2;
+  constexpr int DEPTH = 2;
   QG_G(1) QG_G(2) QG_G(3) QG_G(4)
   if constexpr (FMT == 1) {   // up to eight INT4 column groups fit in registers
     QG_G(5) QG_G(6) QG_G(7) QG_G(8)
