@@ -84,7 +84,8 @@ struct DecodeAddr {
   uint32_t xlane[4];      // per slab: byte offset of this lane's row and first K piece
   const uint8_t* w;       // first weight tile of this workgroup
   int64_t cg_stride;      // bytes between column groups
-  uint32_t wspan;         // bytes of weights from any of its tiles on (at most 2^31 - 1)
+  uint32_t wspan;         // record count of a tile's weight buffer: G groups' bytes, capped
+                          // at 2^31 - 1 (above every offset a tile reads)
   int cg_last;            // last valid group index relative to this workgroup
   uint32_t wlane;         // 16 * lane
   int K;
@@ -99,23 +100,22 @@ struct DecodeAddr {
   int64_t meta_cg_stride; // bytes between column groups of metadata
   int meta_kt_stride;     // bytes of metadata per K tile
   uint32_t mlane;         // this lane's entries within a tile
-  uint32_t mspan;         // bytes of metadata from any of its tiles on (at most 2^31 - 1)
+  uint32_t mspan;         // the same for a tile's metadata buffer
   // activations staged through LDS: per (slab, copy instruction) the byte
-  // offset of this lane's 16 B in tile 0, and per operand piece this lane's
-  // byte offset within a staged slab
+  // offset of this lane's 16 B from a tile's first byte in row m0, and per
+  // operand piece this lane's byte offset within a staged slab
   uint32_t xdma[8];
   uint32_t xrd[4];
 };
 
 // A raw buffer of `bytes` bytes at p.  Reads at or past `bytes` return zero
-// without touching memory; with bytes = 0 every read does.  A ring slot
-// whose K tile lies past the end issues the same loads as any other through
-// such an empty buffer: every slot then runs the same instructions on every
-// path, and the compiler's wait counts stay exact (a load under a branch
-// makes it wait for every load in flight at the merge, which empties the
-// ring once per tile).  `bytes` is wave-uniform and is chosen between
-// run-time values (a choice between constants such as ~0 and 0 is compiled
-// into a vector register, and each load then loops over its distinct values).
+// without touching memory; with bytes = 0 every read does.  The prologue
+// fills a ring slot whose K tile lies past the end through such an empty
+// buffer instead of skipping its loads under a branch: where the paths of a
+// branch around loads merge, the compiler waits for every load in flight.
+// `bytes` is wave-uniform and is chosen between run-time values (a choice
+// between constants such as ~0 and 0 is compiled into a vector register, and
+// each load then loops over its distinct values).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dec_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
                                            0x00020000);
@@ -123,7 +123,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dec_rsrc(const void* p, uint32
 constexpr int kStreamLoad = 2;               // cache policy of the weight stream: nt
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-constexpr uint32_t kXOutOfRange = 0x80000000u;   // past every activation buffer
+constexpr uint32_t kXOutOfRange = 0x80000000u;   // past any staged tile's activation buffer
 
 // Activation tiles staged through LDS.  A staged slab is the 16 rows x RB
 // bytes (RB = tile_x_bytes: 256 for fp16 X, 128 for e4m3 / E2M1 codes) of
@@ -151,9 +151,9 @@ __device__ __forceinline__ int piece_k(int kt, int g, int p) {
 // weight tiles; with live = false (a tile past the end) the same loads read
 // nothing.  X pieces past K read as zero when staged (and in the last rows
 // of X); loaded into registers they may hold the next row's values and are
-// zeroed at use (x_piece).  Rows past M load row M-1 instead (their outputs
-// are never stored); groups past the last column load the last group
-// (likewise discarded).
+// cleared before that tile's compute (cut_chunk).  Rows past M load row M-1
+// instead (their outputs are never stored); groups past the last column load
+// the last group (likewise discarded).
 template <int FMT, int G, bool X_ELEMENTWISE, int NGT = 0, int S = 1, bool XL = false>
 __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const DecodeAddr& ad,
                                            int kt, bool live, uint8_t* xs = nullptr) {
