@@ -12,13 +12,15 @@
 // Work split: a workgroup owns G column groups (16 columns each) and S
 // 16-row slabs of X; its NW waves split the K tiles round-robin, so at any
 // time the waves of a workgroup read neighbouring tiles.  Each wave keeps D K
-// tiles of loads in flight in a register ring (above eight rows the
-// activation part of a tile goes to a wave-private LDS slot instead, copied
-// with whole-row DMA reads) and its fp32 partial sums in registers; the workgroup reduces them through LDS in a fixed order
-// (deterministic, no atomics, no workspace) and the epilogue applies the
-// per-column scale (or the per-tensor FP8 / NVFP4 scales) once to the fp32
-// sum before rounding to the output type; the grouped formats apply their
-// scales in the dequant, before the matrix instruction.
+// tiles of loads in flight in a register ring (above eight rows, unless one
+// slab meets more than four column groups, the activation part of a tile
+// goes to a wave-private LDS slot instead, copied with whole-row DMA reads)
+// and its fp32 partial sums in registers; the workgroup reduces them through
+// LDS in a fixed order (deterministic, no atomics, no workspace) and the
+// epilogue applies the per-column scale (or the per-tensor FP8 / NVFP4
+// scales) once to the fp32 sum before rounding to the output type; the
+// grouped formats apply their scales in the dequant, before the matrix
+// instruction.
 //
 // K order inside a 128-wide tile (fp16 formats): matrix step s (0..3) of lane
 // group g = lane >> 4 covers k = 32 s + 8 g + [0, 8).  Both operands use the
@@ -631,17 +633,24 @@ struct DecodeConfig {
   bool xl; // activation tiles staged through LDS
 };
 
-// Whether a launch stages its activation tiles through LDS: with more than
-// eight rows, eight waves (or four with at least 16 K tiles: the launches
-// with several row blocks), and at most 8 copy instructions per tile (fp16
-// X: up to two slabs); X must span fewer than 2^31 bytes (32-bit buffer
-// offsets).  Measured on MI355X (K = 4096 / 8192, N = 8192 .. 28672, each
-// shape timed staged and direct in alternation, best of three): at M = 12
-// the two are within 1 %; at M = 16 staging saves 1 % (FP8) to 5 % (INT8),
-// at M = 32 8 % (INT4) to 11 % (grouped INT8), at M = 64 .. 128 up to 21 %
-// (FP8).  The grouped INT4 and NVFP4 launches with seven column groups and
-// one slab are the exception (NVFP4 at M = 16: 25.4 us direct, 26.4
-// staged); they stage from two slabs on.
+// Whether a launch may stage its activation tiles through LDS: with more
+// than eight rows, eight waves (or four with at least 16 K tiles: the
+// launches with several row blocks), and at most 8 copy instructions per
+// tile (fp16 X: up to two slabs); X must span fewer than 2^31 bytes (32-bit
+// buffer offsets).  With one slab the callers stage only up to four column
+// groups.  Measured on MI355X, each shape timed staged and direct in
+// alternation: one slab, one or two groups, staging wins (W4A16 K = N = 4096,
+// M = 12 / 16: 5.0 / 5.3 us against 5.9 / 6.4 direct; W4A16, NVFP4 and
+// grouped W4A16 with two groups, K = N = 8192, M = 16: 10.0 / 10.8 / 11.3
+// against 11.5 / 12.5 / 12.8); FP8 and INT8 with two to four groups run
+// within 3 % either way; with more than four groups the weight loads
+// outnumber the activation loads and direct loads win (W4A16 N = 28672,
+// seven groups: K = 8192, M = 9 / 12 / 16 21.3 / 21.2 / 22.0 against
+// 22.1 / 22.5 / 22.5; K = 4096, M = 12 / 16 13.0 / 13.3 against 14.3 / 14.3;
+// eight groups, N = 32768, M = 12 / 16 28.0 / 28.0 against 29.3 / 28.4).
+// From two slabs on staging saved 8 % (INT4) to 11 % (grouped INT8) at
+// M = 32 and up to 21 % at M = 64 .. 128 (FP8) with an earlier form of the
+// main loop.
 bool use_x_lds(int fmt, int64_t M, int nw, int s, int64_t KT) {
   const int rb = fmt == 3 || fmt == 4 ? 128 : 256;
   const int ni = rb == 256 ? 4 : 2;
@@ -692,7 +701,7 @@ DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
   int64_t g = cdiv(CG, 256);
   g = g < 1 ? 1 : (g > gmax ? gmax : g);
   DecodeConfig c{(int)g, decode_waves(M, s, KT), 2, s, false};
-  c.xl = use_x_lds(fmt, M, c.nw, c.s, KT);
+  c.xl = use_x_lds(fmt, M, c.nw, c.s, KT) && (c.s > 1 || c.g <= 4);
   return c;
 }
 
@@ -805,7 +814,7 @@ hipError_t launch_grouped_ngt(const void* x, const void* w, void* y, int64_t M, 
   // seven groups with two metadata words keep eight waves: with four they
   // would need more than 256 registers per lane (one wave per SIMD)
   const int nw = g == 7 && NGT > 1 ? (KT < 16 ? 4 : 8) : decode_waves(M, s, KT);
-  // seven groups with one slab load faster directly
+  // one slab with more than four groups loads X directly (see use_x_lds)
   const bool xl = use_x_lds(FMT, M, nw, s, KT) && (s > 1 || g <= 4);
 #define QG_GCASE(GG, WW, SS, XX)                                                            \
   if (g == GG && nw == WW && s == SS && xl == XX)                                           \
@@ -864,7 +873,7 @@ hipError_t launch_decode_nvfp4(const void* x, const void* w_packed, const float*
   const int s = slab_count(M, pg.kt < 16 ? 4 : 8);
   // seven groups keep eight waves (with four: 264 registers per lane)
   const int nw = g == 7 ? (pg.kt < 16 ? 4 : 8) : decode_waves(M, s, pg.kt);
-  const bool xl = use_x_lds(7, M, nw, s, pg.kt) && (s > 1 || g <= 4);   // as for grouped
+  const bool xl = use_x_lds(7, M, nw, s, pg.kt) && (s > 1 || g <= 4);   // see use_x_lds
 #define QG_NCASE(GG, WW, SS, XX)                                                           \
   if (g == GG && nw == WW && s == SS && xl == XX)                                          \
     return launch_nvfp4_cfg<GG, WW, SS, XX>(x, w_packed, global_scale, y, M, N, K, pg.kt,  \
