@@ -3,13 +3,13 @@
 The hand-picked decode cases cover each edge once.  Here a fixed, seeded
 draw of shapes crosses the small-M kernel's launch choices in combination
 for every format it serves (weight-only M up to 255, FP8 up to 512, MXFP4 up
-to 256): one to sixteen rows (one slab, activations
-loaded directly or staged above eight rows), two slabs, four (e4m3 / E2M1
-activations above 32 rows), one and several row blocks (several: four
-waves per workgroup and the XCD-aware workgroup mapping with padded column
-blocks), short K (four waves) against long K (eight), K tails inside the
-last tile, fp16 rows that are not 16-byte aligned (K % 8 != 0, the
-element-wise path), and ragged N.  Every output is checked against the
+to 256): one to sixteen rows (one slab, activations loaded directly, or
+staged above eight rows with up to four column groups), two slabs, four
+(e4m3 / E2M1 activations above 32 rows), one and several row blocks
+(several: four waves per workgroup and the XCD-aware workgroup mapping with
+padded column blocks), short K (four waves) against long K (eight), K tails
+inside the last tile, fp16 rows that are not 16-byte aligned (K % 8 != 0,
+the element-wise path), and ragged N.  Every output is checked against the
 oracle with its bound, and each call is repeated for determinism.
 """
 

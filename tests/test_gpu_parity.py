@@ -135,7 +135,7 @@ W8_CASES = [
     (16, 1000, 129),    # K % 128 != 0
     (33, 256, 64),      # M > 16
     (2, 64, 1),
-    (9, 200, 9000),     # four groups, three tiles in flight, short K, ragged N
+    (9, 200, 9000),     # four groups, short K, ragged N
     (16, 520, 2100),
     (256, 2048, 300),   # M >= 256 with few 256 x 256 tiles: the small-M kernel, slabs
     (300, 1000, 520),   # ragged M, N and K
