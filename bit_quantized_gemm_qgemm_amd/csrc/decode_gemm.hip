@@ -34,6 +34,8 @@
 #include "qgemm_common.h"
 #include "qgemm_dequant.h"
 
+#include <algorithm>
+
 namespace qgemm {
 namespace {
 
@@ -165,9 +167,10 @@ __device__ __forceinline__ void load_chunk(Chunk<FMT, G, NGT, S>& ch, const Deco
   // the slots' loads are issued in ring order (the wait before a slot's
   // compute then counts only the later slots' loads)
   __builtin_amdgcn_sched_barrier(0);
-  // this tile's activations: from column kt * RB of row m0 to the end of X
-  const __amdgpu_buffer_rsrc_t xr =
-      dec_rsrc(ad.x + (int64_t)kt * RB, live ? ad.xrows - (uint32_t)kt * RB : 0u);
+  // this tile's activations: from column kt * RB of row m0 to the end of X,
+  // at most 2^31 - 1 bytes (the host keeps every offset below that)
+  const __amdgpu_buffer_rsrc_t xr = dec_rsrc(
+      ad.x + (int64_t)kt * RB, live ? min(ad.xrows - (uint32_t)kt * RB, 0x7fffffffu) : 0u);
   if constexpr (XL) {
     // copy the S staged slabs of tile kt into this wave's LDS slot `xs`; in
     // a partial last tile, chunks past K take an offset past the buffer and
@@ -864,10 +867,40 @@ hipError_t launch_nvfp4_cfg(const void* x, const void* w, const float* gs, void*
   return hipGetLastError();
 }
 
+// A lane's activation offset inside the kernel is 32-bit and counts from its
+// workgroup's first row (row * row bytes + a few hundred bytes), so it stays
+// below 2^31 while (rows per workgroup - 1) * row bytes does.  A call whose
+// activation rows are longer than that allows runs as consecutive launches
+// over row chunks short enough (each launch streams the whole weight; it
+// takes rows of over 2^31 / 63 bytes, K in the tens of millions).
+constexpr int64_t kRowOffsetLimit = ((int64_t)1 << 31) - 4096;
+
+template <class Launch>
+hipError_t in_row_chunks(int64_t M, int64_t row_bytes, Launch launch) {
+  int64_t r = M;
+  if ((std::min<int64_t>(M, 64) - 1) * row_bytes >= kRowOffsetLimit)
+    r = (kRowOffsetLimit - 1) / row_bytes + 1;   // (r - 1) * row_bytes < limit
+  for (int64_t m = 0; m < M; m += r) {
+    const hipError_t e = launch(m, std::min(r, M - m));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <class T>
+const T* rows_at(const void* p, int64_t m, int64_t row_bytes) {
+  return reinterpret_cast<const T*>(static_cast<const uint8_t*>(p) + m * row_bytes);
+}
+
 }  // namespace
 
 hipError_t launch_decode_nvfp4(const void* x, const void* w_packed, const float* global_scale,
                                void* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if ((std::min<int64_t>(M, 64) - 1) * 2 * K >= kRowOffsetLimit)
+    return in_row_chunks(M, 2 * K, [&](int64_t m, int64_t rows) {
+      return launch_decode_nvfp4(rows_at<uint8_t>(x, m, 2 * K), w_packed, global_scale,
+                                 static_cast<uint8_t*>(y) + m * 2 * N, rows, N, K, stream);
+    });
   const PackGeom pg = pack_geom(7, K, N);
   const int g = slab_groups(pg.cg, 7, pg.kt);
   const int s = slab_count(M, pg.kt < 16 ? 4 : 8);
@@ -892,6 +925,12 @@ hipError_t launch_decode_nvfp4(const void* x, const void* w_packed, const float*
 hipError_t launch_decode_grouped(int fmt, const void* x, const void* w_packed, void* y,
                                  int64_t M, int64_t N, int64_t K, int64_t group_k,
                                  hipStream_t stream) {
+  if ((std::min<int64_t>(M, 64) - 1) * 2 * K >= kRowOffsetLimit)
+    return in_row_chunks(M, 2 * K, [&](int64_t m, int64_t rows) {
+      return launch_decode_grouped(fmt, rows_at<uint8_t>(x, m, 2 * K), w_packed,
+                                   static_cast<uint8_t*>(y) + m * 2 * N, rows, N, K, group_k,
+                                   stream);
+    });
   if (fmt == 5) return launch_grouped_fmt<1>(x, w_packed, y, M, N, K, group_k, stream);
   if (fmt == 6) return launch_grouped_fmt<2>(x, w_packed, y, M, N, K, group_k, stream);
   return hipErrorInvalidValue;
@@ -900,6 +939,15 @@ hipError_t launch_decode_grouped(int fmt, const void* x, const void* w_packed, v
 hipError_t launch_decode_gemm(int fmt, const void* x, const void* w_packed, const void* scales,
                               const float* scale_a, const float* scale_b, void* y, int64_t M,
                               int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t row_bytes = fmt == 3 ? K / 2 : fmt == 4 ? K : 2 * K;
+  if ((std::min<int64_t>(M, 64) - 1) * row_bytes >= kRowOffsetLimit)
+    return in_row_chunks(M, row_bytes, [&](int64_t m, int64_t rows) {
+      // MXFP4: `scales` are A's E8M0 bytes, K / 32 per row
+      const void* s = fmt == 3 ? rows_at<uint8_t>(scales, m, K / 32) : scales;
+      return launch_decode_gemm(fmt, rows_at<uint8_t>(x, m, row_bytes), w_packed, s, scale_a,
+                                scale_b, static_cast<uint8_t*>(y) + m * 2 * N, rows, N, K,
+                                stream);
+    });
   switch (fmt) {
     case 1: return launch_fmt<1>(x, w_packed, scales, scale_a, scale_b, y, M, N, K, stream);
     case 2: return launch_fmt<2>(x, w_packed, scales, scale_a, scale_b, y, M, N, K, stream);

@@ -171,3 +171,46 @@ def test_mxfp4_packed_weight_over_2gib():
     torch.cuda.empty_cache()
     c_ref, bound = oracle.gemm_mxfp4(a_c, a_e, w_c, w_e)
     assert np.all(oracle.within_tolerance(got, c_ref, bound))
+
+
+def _w8a16_reference_in_k_chunks(x, w, s, step=1 << 22):
+    """The oracle's product and bound, summed over K chunks (both are sums
+    over k, so the chunks add exactly in fp64 up to rounding)."""
+    import oracle
+    s_np = s.cpu().numpy()
+    y = np.zeros((x.shape[0], w.shape[1]))
+    bound = np.zeros_like(y)
+    for k0 in range(0, x.shape[1], step):
+        k1 = min(x.shape[1], k0 + step)
+        yc, bc = oracle.gemm_w8a16(x[:, k0:k1].cpu().numpy(), w[k0:k1].cpu().numpy(), s_np)
+        y += yc
+        bound += bc
+    return y, bound
+
+
+def test_decode_rows_and_weight_stream_over_2gib():
+    """W8A16 with M = 16, K = 2^27 - 64 and N = 16 through the small-M kernel:
+    4 GiB of activations (256 MB per row) and one column group of 2 GiB
+    packed weights.  A lane's activation offset counts from its workgroup's
+    first row in 32 bits, so the call runs as two launches of eight rows;
+    each weight tile's buffer starts at the tile, so the 2 GiB stream needs
+    no offset past 2^31.  M = 1 on the same operands takes a single launch.
+    Every output is checked against the oracle, accumulated over K."""
+    import oracle
+    m, k, n = 16, (1 << 27) - 64, 16
+    case_id("w8a16 decode rows and weight stream over 2 GiB", m, k, n)
+    assert qg.qgemm_dispatch_kernel("w8a16", m, n, k) == "decode_gemm_kernel"
+    assert qg.qgemm_prepack_bytes(2, k, n) >= 1 << 31
+    g = torch.Generator(device="cuda").manual_seed(41)
+    x = torch.randn((m, k), generator=g, device="cuda", dtype=torch.float32).half()
+    w = torch.randint(-127, 128, (k, n), generator=g, device="cuda", dtype=torch.int8)
+    s = (torch.rand((n,), generator=g, device="cuda") * 0.008 + 0.002).half()
+    wp = qg.qgemm_prepack("w8a16", w, k, n)
+    y = qg.qgemm_w8a16(x, wp, s, n).float().cpu().numpy().astype(np.float64)
+    y1 = qg.qgemm_w8a16(x[:1], wp, s, n).float().cpu().numpy().astype(np.float64)
+    del wp
+    y_ref, bound = _w8a16_reference_in_k_chunks(x, w, s)
+    del x, w
+    torch.cuda.empty_cache()
+    assert np.all(oracle.within_tolerance(y, y_ref, bound))
+    assert np.all(oracle.within_tolerance(y1, y_ref[:1], bound[:1]))
