@@ -131,3 +131,20 @@ def test_mxfp4_nan_scale_after_last_block(k):
     wp = qg.qgemm_prepack("mxfp4", dev(wc), k, N, w_scales=dev(we))
     c = qg.qgemm_mxfp4(dev(ac), dev(ae), wp, N)
     check(c[:1], c_ref, bound, f"mxfp4 {m}x{N}x{k} row 0")
+
+
+@pytest.mark.parametrize("m", [1, 16])
+@pytest.mark.parametrize("n", [4112, 10000, 12304, 16400])
+def test_mxfp4_column_groups_per_workgroup(m, n):
+    """The W scale bytes of four consecutive column groups share a word, and
+    the words of eight groups form a band.  N gives 2 (4112), 3 (10000) and 4
+    (12304, 16400) groups per workgroup (three straddle quads and bands),
+    each with a last workgroup of fewer groups; K = 1056 cuts the last tile."""
+    k = 1056
+    case_id("mxfp4 scale words per quad", m, n, k)
+    a, w = wl.mxfp4_operands(m, n, k, seed=n + m)
+    ac, ae = oracle.mxfp4_quantize(a)
+    wc, we = oracle.mxfp4_quantize(w)
+    c_ref, bound = oracle.gemm_mxfp4(ac, ae, wc, we)
+    wp = qg.qgemm_prepack("mxfp4", dev(wc), k, n, w_scales=dev(we))
+    check(qg.qgemm_mxfp4(dev(ac), dev(ae), wp, n), c_ref, bound, f"mxfp4 {m}x{n}x{k}")
