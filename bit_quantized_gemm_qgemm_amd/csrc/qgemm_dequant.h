@@ -80,6 +80,19 @@ __device__ __forceinline__ half8_t dequant_w4_group(uint32_t q, uint32_t e) {
   return half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
+// The same without the scale: (1024 + code) - (1024 + z) = w - z, exact in
+// fp16 (the caller applies s to the fp32 sum of a whole group).
+__device__ __forceinline__ half8_t dequant_w4_group_unscaled(uint32_t q, uint32_t e) {
+  const half2_t me = __builtin_bit_cast(half2_t, e);
+  const half2_t zc = {me.x, me.x};
+  const uint32_t magic = 0x64006400u;
+  const half2_t h0 = __builtin_bit_cast(half2_t, (q & 0x000f000fu) | magic) - zc;
+  const half2_t h1 = __builtin_bit_cast(half2_t, ((q >> 4) & 0x000f000fu) | magic) - zc;
+  const half2_t h2 = __builtin_bit_cast(half2_t, ((q >> 8) & 0x000f000fu) | magic) - zc;
+  const half2_t h3 = __builtin_bit_cast(half2_t, ((q >> 12) & 0x000f000fu) | magic) - zc;
+  return half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+
 __device__ __forceinline__ half8_t dequant_w8_group(uint32_t lo, uint32_t hi, uint32_t e) {
   const half2_t me = __builtin_bit_cast(half2_t, e);
   const half2_t zc = {me.x, me.x};
