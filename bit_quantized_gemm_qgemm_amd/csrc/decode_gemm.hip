@@ -390,7 +390,7 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
         if constexpr (FMT == 7) {
           b = dequant_nvfp4(ch.w[g][0][s], ch.meta[g][0] >> (8 * s));
         } else if constexpr (TILE_SCALE) {
-          b = dequant_w4_group_unscaled(ch.w[g][0][s], ch.meta[g][0]);
+          b = dequant_w4_group_unscaled(ch.w[g][0][s], ch.meta[g][0], mk);
         } else if constexpr (NGT > 0) {
           // (w - z) * s rounded once to fp16, z and s of this step's group
           const uint32_t e = ch.meta[g][(s * NGT) >> 2];

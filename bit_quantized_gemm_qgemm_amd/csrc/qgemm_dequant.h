@@ -80,16 +80,25 @@ __device__ __forceinline__ half8_t dequant_w4_group(uint32_t q, uint32_t e) {
   return half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
-// The same without the scale: (1024 + code) - (1024 + z) = w - z, exact in
-// fp16 (the caller applies s to the fp32 sum of a whole group).
-__device__ __forceinline__ half8_t dequant_w4_group_unscaled(uint32_t q, uint32_t e) {
+// The same without the scale, w - z exact in fp16 (the caller applies s to
+// the fp32 sum of a whole group), in dequant_w4's form: the low nibble of a
+// byte gives (1024 + code) - (1024 + z), the high one 16 code + 1024 times
+// 1/16 minus (64 + z); 1024 + z - 960 = 64 + z is exact.
+__device__ __forceinline__ half8_t dequant_w4_group_unscaled(uint32_t q, uint32_t e,
+                                                             W4Masks mk) {
   const half2_t me = __builtin_bit_cast(half2_t, e);
   const half2_t zc = {me.x, me.x};
+  const half2_t d960 = {(_Float16)960.0f, (_Float16)960.0f};
+  const half2_t zc16 = zc - d960;
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const uint32_t magic = 0x64006400u;
-  const half2_t h0 = __builtin_bit_cast(half2_t, (q & 0x000f000fu) | magic) - zc;
-  const half2_t h1 = __builtin_bit_cast(half2_t, ((q >> 4) & 0x000f000fu) | magic) - zc;
-  const half2_t h2 = __builtin_bit_cast(half2_t, ((q >> 8) & 0x000f000fu) | magic) - zc;
-  const half2_t h3 = __builtin_bit_cast(half2_t, ((q >> 12) & 0x000f000fu) | magic) - zc;
+  const uint32_t q2 = q >> 8;
+  const half2_t h0 = __builtin_bit_cast(half2_t, (q & mk.lo) | magic) - zc;
+  const half2_t h1 =
+      __builtin_elementwise_fma(__builtin_bit_cast(half2_t, (q & mk.hi) | magic), sixteenth, -zc16);
+  const half2_t h2 = __builtin_bit_cast(half2_t, (q2 & mk.lo) | magic) - zc;
+  const half2_t h3 =
+      __builtin_elementwise_fma(__builtin_bit_cast(half2_t, (q2 & mk.hi) | magic), sixteenth, -zc16);
   return half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
