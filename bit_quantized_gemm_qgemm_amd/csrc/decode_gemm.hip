@@ -369,14 +369,14 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
       }
     }
   } else {
-    // grouped INT4 with one group per column and tile (group 128): the tile's
-    // four steps accumulate (w - z) unscaled (exact in fp16) into a tile sum,
-    // and one fp32 fma per accumulator applies the group's scale; each
-    // dequantized weight then costs no multiply.  (w - z) * s is exact in
-    // fp32, so a single weight still reaches the output as (w - z) * s
+    // grouped INT4 / INT8 with one group per column and tile (group 128): the
+    // tile's four steps accumulate (w - z) unscaled (exact in fp16) into a
+    // tile sum, and one fp32 fma per accumulator applies the group's scale;
+    // each dequantized weight then costs no multiply.  (w - z) * s is exact
+    // in fp32, so a single weight still reaches the output as (w - z) * s
     // rounded once.  (Not with two slabs held in registers: their tile sums
     // would not fit beside them.)
-    constexpr bool TILE_SCALE = FMT == 1 && NGT == 1 && (S == 1 || XL);
+    constexpr bool TILE_SCALE = (FMT == 1 || FMT == 2) && NGT == 1 && (S == 1 || XL);
     floatx4 tile[TILE_SCALE ? S : 1][TILE_SCALE ? G : 1];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -390,7 +390,12 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
         if constexpr (FMT == 7) {
           b = dequant_nvfp4(ch.w[g][0][s], ch.meta[g][0] >> (8 * s));
         } else if constexpr (TILE_SCALE) {
-          b = dequant_w4_group_unscaled(ch.w[g][0][s], ch.meta[g][0], mk);
+          if constexpr (FMT == 1) {
+            b = dequant_w4_group_unscaled(ch.w[g][0][s], ch.meta[g][0], mk);
+          } else {
+            const uintx4& h = ch.w[g][s >> 1];
+            b = dequant_w8_group_unscaled(h[2 * (s & 1)], h[2 * (s & 1) + 1], ch.meta[g][0]);
+          }
         } else if constexpr (NGT > 0) {
           // (w - z) * s rounded once to fp16, z and s of this step's group
           const uint32_t e = ch.meta[g][(s * NGT) >> 2];

@@ -129,6 +129,19 @@ __device__ __forceinline__ half8_t dequant_nvfp4(uint32_t q, uint32_t sc8) {
   return half8_t{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
+// Grouped INT8 without the scale: (1024 + w + 128) - (1152 + z) = w - z,
+// exact in fp16 (the caller applies s to the fp32 sum of a whole group).
+__device__ __forceinline__ half8_t dequant_w8_group_unscaled(uint32_t lo, uint32_t hi,
+                                                             uint32_t e) {
+  const half2_t me = __builtin_bit_cast(half2_t, e);
+  const half2_t zc = {me.x, me.x};
+  const half2_t a = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) - zc;
+  const half2_t b = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) - zc;
+  const half2_t c = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) - zc;
+  const half2_t d = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) - zc;
+  return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
 // Two biased INT8 bytes (w + 128) of a word, selected by `sel`, -> w as fp16.
 __device__ __forceinline__ half2_t dequant_w8_pair(uint32_t d, uint32_t sel) {
   // byte permute of {0x64646464 : d}: selector 0..3 picks bytes of d, 4 picks 0x64
