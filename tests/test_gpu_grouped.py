@@ -101,6 +101,28 @@ def test_grouped_one_hot_reads_back_dequantized_weights(fmt, gk, gn):
     assert np.array_equal(run(fmt, x, w, s, z, k, n, gk, gn), wdeq)
 
 
+@pytest.mark.parametrize("fmt", ["w4a16", "w8a16"])
+@pytest.mark.parametrize("k", [256, 2048])
+def test_grouped_g128_one_hot_through_tile_sums(fmt, k):
+    """Group 128 at up to 16 rows: the small-M kernel accumulates w - z over a
+    K tile and applies s to the fp32 tile sum.  Sixteen one-hot rows at a
+    time read the weights back as fp16((w - z) * s), bit-exact, negative
+    scales included (K = 256: activations loaded directly; K = 2048: staged
+    through LDS, one row block of eight waves)."""
+    n, gk = 136, 128
+    case_id(f"{fmt} grouped g128 one-hot, tile sums", k, n)
+    gen = wl.w4a16_grouped if fmt == "w4a16" else wl.w8a16_grouped
+    _, w, s, z = gen(1, k, n, gk, 1, seed=k + 7)
+    s = (s.astype(np.float32) * np.where(np.arange(s.shape[1]) % 2 == 0, -1, 1)).astype(np.float16)
+    deq = oracle.dequant_w4_grouped if fmt == "w4a16" else oracle.dequant_w8_grouped
+    wdeq = oracle.round_fp16(deq(w, s, z, gk, 1))
+    starts = range(0, k, 16) if k <= 256 else [0, 112, 128, 1024, 2032]
+    for k0 in starts:
+        x = np.zeros((16, k), np.float16)
+        x[np.arange(16), k0 + np.arange(16)] = 1
+        assert np.array_equal(run(fmt, x, w, s, z, k, n, gk, 1), wdeq[k0:k0 + 16]), f"rows {k0}.."
+
+
 @pytest.mark.parametrize("fmt,m", [("w4a16", 1), ("w4a16", 16), ("w8a16", 4)])
 def test_grouped_full_size_sampled(fmt, m):
     """GPTQ-style group_k = 128 with zero points at the decode shapes (W4A16
