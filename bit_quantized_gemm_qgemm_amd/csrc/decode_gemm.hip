@@ -369,14 +369,17 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
       }
     }
   } else {
-    // grouped INT4 / INT8 with one group per column and tile (group 128): the
-    // tile's four steps accumulate (w - z) unscaled (exact in fp16) into a
-    // tile sum, and one fp32 fma per accumulator applies the group's scale;
-    // each dequantized weight then costs no multiply.  (w - z) * s is exact
-    // in fp32, so a single weight still reaches the output as (w - z) * s
-    // rounded once.  (Not with two slabs held in registers: their tile sums
-    // would not fit beside them.)
-    constexpr bool TILE_SCALE = (FMT == 1 || FMT == 2) && NGT == 1 && (S == 1 || XL);
+    // grouped INT4 / INT8 with group 128 or 64 (one or two groups per column
+    // and tile): the matrix steps of a group accumulate (w - z) unscaled
+    // (exact in fp16) into a group sum, and one fp32 fma per accumulator
+    // applies the group's scale; each dequantized weight then costs no
+    // multiply.  (w - z) * s is exact in fp32, so a single weight still
+    // reaches the output as (w - z) * s rounded once.  (Group 128 with one
+    // slab or staged activations, group 64 with one slab: otherwise the
+    // group sums would not fit beside the ring.)
+    constexpr bool TILE_SCALE =
+        (FMT == 1 || FMT == 2) && ((NGT == 1 && (S == 1 || XL)) || (NGT == 2 && S == 1));
+    constexpr int SPG = NGT == 2 ? 2 : 4;   // matrix steps per scale group
     floatx4 tile[TILE_SCALE ? S : 1][TILE_SCALE ? G : 1];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -390,11 +393,12 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
         if constexpr (FMT == 7) {
           b = dequant_nvfp4(ch.w[g][0][s], ch.meta[g][0] >> (8 * s));
         } else if constexpr (TILE_SCALE) {
+          const uint32_t e = ch.meta[g][(s * NGT) >> 2];
           if constexpr (FMT == 1) {
-            b = dequant_w4_group_unscaled(ch.w[g][0][s], ch.meta[g][0], mk);
+            b = dequant_w4_group_unscaled(ch.w[g][0][s], e, mk);
           } else {
             const uintx4& h = ch.w[g][s >> 1];
-            b = dequant_w8_group_unscaled(h[2 * (s & 1)], h[2 * (s & 1) + 1], ch.meta[g][0]);
+            b = dequant_w8_group_unscaled(h[2 * (s & 1)], h[2 * (s & 1) + 1], e);
           }
         } else if constexpr (NGT > 0) {
           // (w - z) * s rounded once to fp16, z and s of this step's group
@@ -415,21 +419,25 @@ __device__ __forceinline__ void compute_chunk(const Chunk<FMT, G, NGT, S>& ch,
         for (int q = 0; q < S; ++q) {
           if constexpr (TILE_SCALE)
             tile[q][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                xv[q], b, s == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : tile[q][g], 0, 0, 0);
+                xv[q], b, s % SPG == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : tile[q][g], 0, 0, 0);
           else
             acc[q][g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xv[q], b, acc[q][g], 0, 0, 0);
         }
       }
-    }
-    if constexpr (TILE_SCALE) {
-      // the lane's accumulator column is its B-operand column (lane & 15),
-      // whose word holds the group's scale in its high half
+      if constexpr (TILE_SCALE) {
+        if (s % SPG == SPG - 1) {
+          // the lane's accumulator column is its B-operand column (lane & 15),
+          // whose word holds the group's scale in its high half
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(ch.meta[g][0] >> 16));
-        const floatx4 sv = {sc, sc, sc, sc};
+          for (int g = 0; g < G; ++g) {
+            const uint32_t e = ch.meta[g][(s * NGT) >> 2];
+            const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
+            const floatx4 sv = {sc, sc, sc, sc};
 #pragma unroll
-        for (int q = 0; q < S; ++q) acc[q][g] = __builtin_elementwise_fma(tile[q][g], sv, acc[q][g]);
+            for (int q = 0; q < S; ++q)
+              acc[q][g] = __builtin_elementwise_fma(tile[q][g], sv, acc[q][g]);
+          }
+        }
       }
     }
   }
