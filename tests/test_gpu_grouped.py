@@ -102,17 +102,17 @@ def test_grouped_one_hot_reads_back_dequantized_weights(fmt, gk, gn):
 
 
 @pytest.mark.parametrize("fmt", ["w4a16", "w8a16"])
-@pytest.mark.parametrize("k", [256, 2048])
-def test_grouped_g128_one_hot_through_tile_sums(fmt, k):
-    """Group 128 at up to 16 rows: the small-M kernel accumulates w - z over a
-    K tile and applies s to the fp32 tile sum.  Sixteen one-hot rows at a
-    time read the weights back as fp16((w - z) * s), bit-exact, negative
-    scales included (K = 256: activations loaded directly; K = 2048: staged
-    through LDS, one row block of eight waves)."""
-    n, gk = 136, 128
-    case_id(f"{fmt} grouped g128 one-hot, tile sums", k, n)
+@pytest.mark.parametrize("k,gk", [(256, 128), (2048, 128), (256, 64)])
+def test_grouped_one_hot_through_group_sums(fmt, k, gk):
+    """Group 128 or 64 at up to 16 rows: the small-M kernel accumulates w - z
+    over the matrix steps of a group and applies s to the fp32 group sum.
+    Sixteen one-hot rows at a time read the weights back as fp16((w - z) * s),
+    bit-exact, negative scales included (K = 256: activations loaded
+    directly; K = 2048: staged through LDS, one row block of eight waves)."""
+    n = 136
+    case_id(f"{fmt} grouped one-hot through group sums", k, n, gk)
     gen = wl.w4a16_grouped if fmt == "w4a16" else wl.w8a16_grouped
-    _, w, s, z = gen(1, k, n, gk, 1, seed=k + 7)
+    _, w, s, z = gen(1, k, n, gk, 1, seed=k + gk)
     s = (s.astype(np.float32) * np.where(np.arange(s.shape[1]) % 2 == 0, -1, 1)).astype(np.float16)
     deq = oracle.dequant_w4_grouped if fmt == "w4a16" else oracle.dequant_w8_grouped
     wdeq = oracle.round_fp16(deq(w, s, z, gk, 1))
