@@ -745,6 +745,17 @@ DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
   g = g < 1 ? 1 : (g > gmax ? gmax : g);
   DecodeConfig c{(int)g, decode_waves(M, s, KT), 2, s, false};
   c.xl = use_x_lds(fmt, M, c.nw, c.s, KT) && (c.s > 1 || c.g <= 4);
+  // e4m3 activations, one slab, at least 16 K tiles and two column groups:
+  // four waves loading A directly, each with twice the tiles (most of them
+  // in the steady loop).  Measured on MI355X against eight staged waves,
+  // K = 8192: N = 8192 M = 1 / 8 / 16 11.9 / 12.1 / 12.2 us against 12.1 /
+  // 12.5 / 12.6; N = 16384 M = 1 / 16 23.5 / 23.8 against 25.4 / 25.4; with
+  // one group (K = N = 4096, M = 16) 5.35 against 5.15, and the other
+  // formats ran as fast or faster with eight.
+  if (fmt == 4 && s == 1 && KT >= 16 && g >= 2) {
+    c.nw = 4;
+    c.xl = false;
+  }
   return c;
 }
 

@@ -148,3 +148,20 @@ def test_mxfp4_column_groups_per_workgroup(m, n):
     c_ref, bound = oracle.gemm_mxfp4(ac, ae, wc, we)
     wp = qg.qgemm_prepack("mxfp4", dev(wc), k, n, w_scales=dev(we))
     check(qg.qgemm_mxfp4(dev(ac), dev(ae), wp, n), c_ref, bound, f"mxfp4 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m", [1, 9, 16])
+@pytest.mark.parametrize("n,k", [(4112, 2064), (8216, 4096)])
+def test_fp8_four_waves(m, n, k):
+    """FP8 with one slab, at least 16 K tiles and two or more column groups
+    runs four waves loading A directly (17 or 32 K tiles: the steady loop
+    and a cut last tile; N leaves a last workgroup of one group)."""
+    case_id("fp8 four waves", m, n, k)
+    a, b = wl.fp8_operands(m, n, k, seed=k + n + m)
+    qa, sa = oracle.fp8_quantize(a)
+    qb, sb = oracle.fp8_quantize(b)
+    c_ref, bound = oracle.gemm_fp8(qa, qb, sa, sb)
+    sa_d = torch.tensor([sa], dtype=torch.float32, device="cuda")
+    sb_d = torch.tensor([sb], dtype=torch.float32, device="cuda")
+    c = qg.qgemm_fp8(dev(qa), qg.qgemm_prepack("fp8", dev(qb), k, n), sa_d, sb_d, n)
+    check(c, c_ref, bound, f"fp8 {m}x{n}x{k}")
