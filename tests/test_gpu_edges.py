@@ -214,3 +214,69 @@ def test_decode_rows_and_weight_stream_over_2gib():
     torch.cuda.empty_cache()
     assert np.all(oracle.within_tolerance(y, y_ref, bound))
     assert np.all(oracle.within_tolerance(y1, y_ref[:1], bound[:1]))
+
+
+LONG_ROWS_K = 72 << 20   # 151 MB fp16 rows: 15 rows span 2.26 GB, past 2^31
+
+
+def _long_rows_x(m, k, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return torch.randn((m, k), generator=g, device="cuda", dtype=torch.float32).half()
+
+
+def test_grouped_decode_rows_over_2gib():
+    """The grouped entry point runs activation rows longer than the small-M
+    kernel's 32-bit offsets allow as row chunks too: M = 16, K = 72 Mi
+    (2.4 GB of fp16 X, chunks of 15 rows and 1), N = 16, grouped INT4 with
+    group 128; every output against the oracle summed over K."""
+    import oracle
+    m, k, n, gk = 16, LONG_ROWS_K, 16, 128
+    case_id("grouped decode rows over 2 GiB", m, k, n)
+    x = _long_rows_x(m, k, 43)
+    w = random_bytes((k // 2, n), 44)
+    g = torch.Generator(device="cuda").manual_seed(48)
+    s = (torch.rand((k // gk, n), generator=g, device="cuda") * 0.015 + 0.005).half()
+    z = random_bytes((k // gk, n), 45, 0, 16)
+    wp = qg.qgemm_prepack_grouped("w4a16_grouped", w, k, n, s, z, gk, 1)
+    y = qg.qgemm_w4a16_grouped(x, wp, n, gk).float().cpu().numpy().astype(np.float64)
+    del wp
+    y_ref = np.zeros((m, n))
+    bound = np.zeros((m, n))
+    step = 1 << 23
+    for k0 in range(0, k, step):
+        k1 = min(k, k0 + step)
+        yc, bc = oracle.gemm_w4a16_grouped(
+            x[:, k0:k1].cpu().numpy(), w[k0 // 2:k1 // 2].cpu().numpy(),
+            s[k0 // gk:k1 // gk].cpu().numpy(), z[k0 // gk:k1 // gk].cpu().numpy(), gk, 1)
+        y_ref += yc
+        bound += bc
+    del x, w, s, z
+    torch.cuda.empty_cache()
+    assert np.all(oracle.within_tolerance(y, y_ref, bound))
+
+
+def test_nvfp4_decode_rows_over_2gib():
+    """As above for NVFP4 weights (codes [N, K/2], e4m3 block scales with
+    exponent field 4..10)."""
+    import oracle
+    m, k, n = 16, LONG_ROWS_K, 16
+    case_id("nvfp4 decode rows over 2 GiB", m, k, n)
+    x = _long_rows_x(m, k, 49)
+    codes = random_bytes((n, k // 2), 46)
+    scales = random_bytes((n, k // 16), 47, 32, 88)
+    gs = torch.tensor([0.01], dtype=torch.float32, device="cuda")
+    wp = qg.qgemm_prepack("nvfp4", codes, k, n, w_scales=scales)
+    y = qg.qgemm_nvfp4(x, wp, gs, n).float().cpu().numpy().astype(np.float64)
+    del wp
+    y_ref = np.zeros((m, n))
+    bound = np.zeros((m, n))
+    step = 1 << 23
+    for k0 in range(0, k, step):
+        k1 = min(k, k0 + step)
+        yc, bc = oracle.gemm_nvfp4(x[:, k0:k1].cpu().numpy(), codes[:, k0 // 2:k1 // 2].cpu().numpy(),
+                                   scales[:, k0 // 16:k1 // 16].cpu().numpy(), np.float32(0.01))
+        y_ref += yc
+        bound += bc
+    del x, codes, scales
+    torch.cuda.empty_cache()
+    assert np.all(oracle.within_tolerance(y, y_ref, bound))
