@@ -756,6 +756,18 @@ DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
     c.nw = 4;
     c.xl = false;
   }
+  // e4m3 activations with up to eight rows: one column group per workgroup
+  // (two to seven workgroups per CU; the activation bytes each re-reads are
+  // few).  Measured on MI355X against the rule above, M = 1 / 8: K = 8192,
+  // N = 8192 11.6 / 11.6 us against 12.0 / 12.1, N = 16384 21.0 / 21.1
+  // against 23.4 / 23.6, N = 28672 36.7 / 38.1 against 39.2 / 38.3; K = 4096,
+  // N = 8192 6.8 / 7.1 against 7.2 / 7.4.  At 16 rows it lost (N = 8192:
+  // 13.4 against 12.2).
+  if (fmt == 4 && M <= 8) {
+    c.g = 1;
+    c.nw = decode_waves(M, s, KT);
+    c.xl = false;
+  }
   return c;
 }
 

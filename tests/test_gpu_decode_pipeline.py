@@ -152,11 +152,12 @@ def test_mxfp4_column_groups_per_workgroup(m, n):
 
 @pytest.mark.parametrize("m", [1, 9, 16])
 @pytest.mark.parametrize("n,k", [(4112, 2064), (8216, 4096)])
-def test_fp8_four_waves(m, n, k):
-    """FP8 with one slab, at least 16 K tiles and two or more column groups
-    runs four waves loading A directly (17 or 32 K tiles: the steady loop
-    and a cut last tile; N leaves a last workgroup of one group)."""
-    case_id("fp8 four waves", m, n, k)
+def test_fp8_launch_shapes(m, n, k):
+    """FP8 launch shapes at one slab with many column groups: up to eight
+    rows one group per workgroup (eight waves), 9 .. 16 rows four waves
+    loading A directly (17 or 32 K tiles: the steady loop and a cut last
+    tile; N leaves a last workgroup of one group)."""
+    case_id("fp8 launch shapes", m, n, k)
     a, b = wl.fp8_operands(m, n, k, seed=k + n + m)
     qa, sa = oracle.fp8_quantize(a)
     qb, sb = oracle.fp8_quantize(b)
