@@ -2,7 +2,7 @@
 
 Builds tests/asan_abi_check.cpp against libqgemm's host code (api.cpp built
 with the sanitizer on its host pass only; the kernel objects are the normal
-build) and runs it.  Every call in the driver is answered on the host before
+build) and runs it.  Every call in that program is answered on the host before
 anything is launched, so no GPU is needed; the run fails on any sanitizer
 report or unexpected status.
 """
