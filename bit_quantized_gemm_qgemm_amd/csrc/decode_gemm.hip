@@ -768,6 +768,18 @@ DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
     c.nw = decode_waves(M, s, KT);
     c.xl = false;
   }
+  // E2M1 activations, one slab, at least 16 K tiles, and more than 256
+  // workgroups of the largest G: four waves loading A directly, so that two
+  // workgroups share a CU and one's start and end overlap the other's K loop.
+  // Measured on MI355X against eight staged waves, M = 1 / 16: K = 8192,
+  // N = 20480 19.9 / 22.3 us against 20.6 / 23.0, N = 28672 22.2 / 23.4
+  // against 23.2 / 24.8; K = 4096, N = 28672 13.0 / 13.5 against 13.8 / 15.5.
+  // With at most 256 workgroups it ran as fast (N = 12288, 16384) or slower
+  // (N = 8192: 9.1 / 9.6 against 8.6 / 9.2).
+  if (fmt == 3 && s == 1 && KT >= 16 && cdiv(CG, c.g) > 256) {
+    c.nw = 4;
+    c.xl = false;
+  }
   return c;
 }
 

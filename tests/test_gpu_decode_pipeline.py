@@ -166,3 +166,20 @@ def test_fp8_launch_shapes(m, n, k):
     sb_d = torch.tensor([sb], dtype=torch.float32, device="cuda")
     c = qg.qgemm_fp8(dev(qa), qg.qgemm_prepack("fp8", dev(qb), k, n), sa_d, sb_d, n)
     check(c, c_ref, bound, f"fp8 {m}x{n}x{k}")
+
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16400, 4160), (16, 16400, 4160), (9, 20496, 4096),
+                                   (16, 20496, 4096)])
+def test_mxfp4_four_wave_launch(m, n, k):
+    """MXFP4 with at least 16 K tiles and more than 256 workgroups of four
+    column groups runs four waves loading A directly: N = 16400 gives 257
+    workgroups, N = 20496 321 (each with a last workgroup of one group);
+    K = 4160 cuts the last of 17 tiles, K = 4096 fills 16."""
+    case_id("mxfp4 four-wave launch", m, n, k)
+    a, w = wl.mxfp4_operands(m, n, k, seed=k + n + m)
+    ac, ae = oracle.mxfp4_quantize(a)
+    wc, we = oracle.mxfp4_quantize(w)
+    c_ref, bound = oracle.gemm_mxfp4(ac, ae, wc, we)
+    wp = qg.qgemm_prepack("mxfp4", dev(wc), k, n, w_scales=dev(we))
+    check(qg.qgemm_mxfp4(dev(ac), dev(ae), wp, n), c_ref, bound, f"mxfp4 {m}x{n}x{k}")
