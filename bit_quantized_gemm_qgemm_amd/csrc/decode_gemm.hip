@@ -780,6 +780,12 @@ DecodeConfig pick_decode_config(int fmt, int64_t M, int64_t CG, int64_t KT) {
     c.nw = 4;
     c.xl = false;
   }
+  // INT8 weights on the same wide grids take four waves only up to eight
+  // rows (activations loaded directly either way): M = 1, K = 4096, N = 20480
+  // 18.1 / 18.2 us against 18.8, N = 28672 20.6 / 20.8 against 21.5; K = 8192,
+  // N = 28672 39.2 against 43.1.  At 16 rows, direct loads cost more than
+  // the overlap gains (N = 20480: 21.0 against 20.2 staged).
+  if (fmt == 2 && s == 1 && M <= 8 && KT >= 16 && cdiv(CG, c.g) > 256) c.nw = 4;
   return c;
 }
 

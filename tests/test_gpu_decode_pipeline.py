@@ -183,3 +183,16 @@ def test_mxfp4_four_wave_launch(m, n, k):
     c_ref, bound = oracle.gemm_mxfp4(ac, ae, wc, we)
     wp = qg.qgemm_prepack("mxfp4", dev(wc), k, n, w_scales=dev(we))
     check(qg.qgemm_mxfp4(dev(ac), dev(ae), wp, n), c_ref, bound, f"mxfp4 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,k", [(1, 4160), (8, 4160), (8, 4096), (16, 4160)])
+def test_w8a16_four_wave_launch(m, k):
+    """INT8 weights with more than 256 workgroups of four column groups
+    (N = 20496: 321, the last of one group) run four waves up to eight rows
+    and eight staged waves at 16; K = 4160 cuts the last of 33 tiles."""
+    n = 20496
+    case_id("w8a16 four-wave launch", m, k, n)
+    x, w, s = wl.w8a16(m, k, n, seed=k + n + m)
+    y_ref, bound = oracle.gemm_w8a16(x, w, s)
+    y = qg.qgemm_w8a16(dev(x), qg.qgemm_prepack("w8a16", dev(w), k, n), dev(s), n)
+    check(y, y_ref, bound, f"w8a16 {m}x{k}x{n}")
