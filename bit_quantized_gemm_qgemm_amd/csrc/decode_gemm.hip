@@ -897,7 +897,12 @@ hipError_t launch_grouped_ngt(const void* x, const void* w, void* y, int64_t M, 
   const int g = slab_groups(CG, FMT == 1 && !(s == 2 && NGT == 4) ? 7 : 4, KT);
   // seven groups with two metadata words keep eight waves: with four they
   // would need more than 256 registers per lane (one wave per SIMD)
-  const int nw = g == 7 && NGT > 1 ? (KT < 16 ? 4 : 8) : decode_waves(M, s, KT);
+  int nw = g == 7 && NGT > 1 ? (KT < 16 ? 4 : 8) : decode_waves(M, s, KT);
+  // grouped INT8 up to eight rows with more than 256 workgroups: four waves,
+  // as for per-column INT8 (K = 4096, N = 28672, group 128, M = 1 / 8: 21.1 /
+  // 21.3-21.4 us against 21.6-22.1 / 22.3-22.5; K = 8192: M = 1 40.2 against
+  // 43.5)
+  if (FMT == 2 && s == 1 && M <= 8 && KT >= 16 && cdiv(CG, g) > 256) nw = 4;
   // one slab with more than four groups loads X directly (see use_x_lds)
   const bool xl = use_x_lds(FMT, M, nw, s, KT) && (s > 1 || g <= 4);
 #define QG_GCASE(GG, WW, SS, XX)                                                            \
@@ -907,6 +912,9 @@ hipError_t launch_grouped_ngt(const void* x, const void* w, void* y, int64_t M, 
 #define QG_GCASE2(GG, SS) QG_GCASE(GG, 8, SS, false) QG_GCASE(GG, 8, SS, true)
 #define QG_GCASE4(GG) QG_GCASE2(GG, 2) QG_GCASE(GG, 4, 2, true)
   QG_GCASE(1, 4, 1, false) QG_GCASE(2, 4, 1, false)
+  if constexpr (FMT == 2) {
+    QG_GCASE(3, 4, 1, false) QG_GCASE(4, 4, 1, false)
+  }
   QG_GCASE2(1, 1) QG_GCASE2(2, 1) QG_GCASE2(3, 1) QG_GCASE2(4, 1)
   QG_GCASE4(1) QG_GCASE4(2) QG_GCASE4(3) QG_GCASE4(4)
   if constexpr (FMT == 1) {

@@ -214,3 +214,16 @@ def test_grouped_tiled_sampled(fmt, m, k, n, gk, gn, zp):
     zc = None if z is None else z[:, cols // gn]
     y_ref, bound = gemm(x[rows], w[:, cols], s[:, cols // gn], zc, gk, 1)
     assert_within(y[np.ix_(rows, cols)], y_ref, bound, f"{fmt} grouped tiled sampled")
+
+
+@pytest.mark.parametrize("m,k,gk", [(1, 4224, 128), (8, 4096, 64), (8, 4224, 128),
+                                    (16, 4096, 128)])
+def test_w8a16_grouped_four_wave_launch(m, k, gk):
+    """Grouped INT8 with more than 256 workgroups of four column groups
+    (N = 20496: 321, the last of one group) runs four waves up to eight rows
+    and eight at 16 (K = 4224: 33 tiles)."""
+    n = 20496
+    case_id("w8a16 grouped four-wave launch", m, k, n, gk)
+    x, w, s, z = wl.w8a16_grouped(m, k, n, gk, 1, zeros=True, seed=m + k + n + gk)
+    y_ref, bound = oracle.gemm_w8a16_grouped(x, w, s, z, gk, 1)
+    assert_within(run("w8a16", x, w, s, z, k, n, gk, 1), y_ref, bound, f"w8a16 grouped {m}x{k}x{n}")
